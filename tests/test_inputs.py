@@ -1,0 +1,94 @@
+"""The seeded input generator: published test vector, moments, bf16
+rounding, per-workload routing skew."""
+import numpy as np
+import pytest
+import torch
+
+from moe_inputs import CONFIGS, rng
+import oracle
+
+
+def test_splitmix64_published_vector():
+    # SplitMix64 seeded with 1234567: the first five outputs as published
+    # with the reference implementation (Vigna's xoshiro/splitmix64 page).
+    got = rng.splitmix64_at(1234567, np.arange(5))
+    want = [6457827717110365317, 3203168211198807973, 9817491932198370423,
+            4593380528125082431, 16408922859458223821]
+    assert [int(v) for v in got] == want
+
+
+def test_normal_moments_and_support():
+    z = rng.normal_f32(rng.stream_key(0, 1, 0), 0, 1 << 20, 1.0)
+    assert abs(float(z.mean())) < 5e-3
+    assert abs(float(z.std()) - 1.0) < 5e-3
+    # Irwin-Hall(4) support is +-2*sqrt(3)
+    assert float(np.abs(z).max()) <= 2 * np.sqrt(3) + 1e-6
+    # kurtosis of a 4-term uniform sum: 3 - 6/(5*4) = 2.7
+    k = float(((z.astype(np.float64)) ** 4).mean())
+    assert abs(k - 2.7) < 0.05
+
+
+def test_counter_based_blocks_agree():
+    key = rng.stream_key(3, 4, 5)
+    whole = rng.normal_f32(key, 0, 1000, 0.5)
+    part = rng.normal_f32(key, 317, 100, 0.5)
+    assert np.array_equal(whole[317:417], part)
+    # chunking inside the generator does not change values
+    assert np.array_equal(rng.normal_f32(key, 0, 1000, 0.5, chunk=7), whole)
+
+
+def test_streams_distinct_and_deterministic():
+    c = CONFIGS["tiny_fp32"]
+    a = rng.gen(c, "x")
+    b = rng.gen(c, "x")
+    assert np.array_equal(a, b)
+    assert not np.array_equal(rng.gen(c, "W1", 0), rng.gen(c, "W1", 1))
+    rows = rng.gen_rows(c, "x", np.array([5, 0, 255]))
+    assert np.array_equal(rows, a[[5, 0, 255]])
+
+
+def test_weight_std_is_inverse_sqrt_fan_in():
+    c = CONFIGS["moe_s_like"]
+    W1 = rng.gen(c, "W1", 0)     # fan_in d = 1024
+    W2 = rng.gen(c, "W2", 3)     # fan_in f = 4096
+    assert abs(W1.std() * np.sqrt(c.d) - 1) < 0.01
+    assert abs(W2.std() * np.sqrt(c.f) - 1) < 0.01
+
+
+def test_bf16_rounding_matches_torch():
+    a = rng.normal_f32(rng.stream_key(1, 1, 1), 0, 100000, 3.0)
+    # include exact ties (bit 15 set, lower bits zero) both ways
+    ties = np.array([0x3F808000, 0x3F818000, 0xBF808000, 0x3F80FFFF],
+                    dtype=np.uint32).view(np.float32)
+    a = np.concatenate([a, ties])
+    mine = rng.bf16_round_bits(a)
+    ref = torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy()
+    assert np.array_equal(mine, ref.view(np.uint16))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["skewed_zipf1.2", "many_expert_zipf1.0"])
+def test_routing_skew_lands_in_band(name):
+    c = CONFIGS[name]
+    x = rng.gen(c, "x")
+    Wg = rng.gen(c, "Wg")
+    l = oracle.gate_logits(x, Wg, rng.logit_bias(c))
+    cnt = np.bincount(oracle.topk_select(l, c.k).ravel(), minlength=c.E)
+    if name.startswith("skewed"):
+        # heaviest expert about 4x the mean load
+        assert 3.5 <= cnt.max() / cnt.mean() <= 4.5
+    else:
+        # some experts get no token, a few get more than 1000
+        assert (cnt == 0).sum() >= 1
+        assert (cnt > 1000).sum() >= 1
+
+
+def test_moe_s_like_is_near_uniform():
+    c = CONFIGS["moe_s_like"]
+    assert rng.logit_bias(c) is None
+    x = rng.gen(c, "x")
+    Wg = rng.gen(c, "Wg")
+    cnt = np.bincount(oracle.topk_select(oracle.gate_logits(x, Wg), c.k).ravel(),
+                      minlength=c.E)
+    assert cnt.max() / cnt.mean() < 1.5
+    assert cnt.sum() == c.R
