@@ -1,0 +1,221 @@
+/*
+ * libmoe -- MoE layer forward and backward on one AMD Instinct MI355X (gfx950).
+ *
+ * The layer: a gate scores each token against every expert, each token goes
+ * to its k best experts, the (token, slot) pairs are counting-sorted into one
+ * contiguous, unpadded segment per expert, every expert runs its FFN on its
+ * segment as one grouped GEMM, and the outputs are gathered back to token
+ * order weighted by the gate.  Backward runs the same steps in reverse.
+ *
+ * Sources (page title, section):
+ *  - "ES-MoE: Scaling Beyond the GPU Memory Limit for Large Mixture-of-Experts
+ *    Model Training" (xllm-io paper review), 三 技术架构 / 专家级卸载与处理 and
+ *    四 核心创新: expert placement follows the gate; tokens are assigned to
+ *    their experts in sequence instead of a batched matmul over a dense
+ *    dispatch mask; zero padding is removed (自适应卸载, GPU-only mode).
+ *  - "FastMoE: A Fast Mixture-of-Expert Training System" (nubint.ai review),
+ *    제안 방법: a scatter/gather layout batches each expert's inputs; the
+ *    expert FFN runs the experts' linear layers in parallel.
+ *  - "Flattening Every Memory Peak in Long-Context Mixture-of-Experts
+ *    Training", abstract: the dispatch buffer grows with the routing matrix;
+ *    reordering work leaves loss and gradients exact.
+ *
+ * Conventions shared by every entry point
+ *  - All tensors are device pointers to dense row-major arrays.  Element type
+ *    of x, weights, activations and their gradients is `dt` (MOE_F32 or
+ *    MOE_BF16); logits, gate weights and their gradients are always float;
+ *    indices are int32.
+ *  - The caller owns every buffer, including workspaces; the library never
+ *    allocates or frees device memory and never copies device -> host.
+ *  - Every call is asynchronous on `stream`.  Arguments are validated on the
+ *    host before anything is launched; on error nothing is launched and the
+ *    status says why.  No C++ exception crosses this interface.
+ *  - Outputs are overwritten unless an argument says "accumulated".
+ *  - Bit-reproducible: no float atomics; every reduction has a fixed order.
+ *  - Limits: 1 <= k <= E <= 1024; T*k < 2^31; d and f multiples of 64 for
+ *    the FFN and for combine/unpermute (any d >= 1 for the gate).  T = 0 is
+ *    accepted and launches nothing.
+ *  - Threads: entry points are reentrant; concurrent calls on different
+ *    streams must not share output or workspace buffers.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1,  /* bad size, null pointer, misaligned pointer */
+    MOE_ERR_UNSUPPORTED = -2,  /* device is not gfx950, or dtype/act not built */
+    MOE_ERR_WORKSPACE = -3,    /* workspace too small (see *_workspace_bytes) */
+    MOE_ERR_HIP = -4           /* a HIP runtime call or launch failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+typedef enum { MOE_ACT_GELU = 0, MOE_ACT_SWIGLU = 1 } moe_act;
+
+/* Human-readable text of a status code (static storage). */
+const char *moe_status_string(moe_status s);
+
+/* Interface version; bumped on any signature change. */
+int moe_abi_version(void);
+
+/*
+ * moe_init -- check that `device` is a gfx950 GPU and cache its properties.
+ * Optional: every entry point checks the current device itself on first use.
+ * Returns MOE_ERR_UNSUPPORTED for another architecture.
+ */
+moe_status moe_init(int device);
+
+/*
+ * moe_gate_topk -- gate scores, top-k choice and gate weights.
+ *   logits[t,e] = sum_{i=0..d-1} x[t,i]*Wg[i,e] (+ logit_bias[e]), fp32,
+ *                 summed in increasing i with every product and sum rounded
+ *                 (bf16 products are exact in fp32, so a fused chain gives the
+ *                 same bits); this fixed order makes the routing reproducible.
+ *   topk_idx[t,j] = index of the j-th largest logit (ties: lower index first).
+ *   topk_w[t,j]   = renorm ? softmax over the k selected logits
+ *                          : softmax over all E logits, at the selected expert.
+ * Source: ES-MoE review, 三 技术架构 (placement known after the gating network);
+ * the gate formula is not printed -- linear gate + softmax top-k is the reading.
+ *   x [T,d] dt, Wg [d,E] dt, logit_bias [E] float or NULL (a workload input,
+ *   not a trained parameter), logits [T,E] float, topk_idx [T,k] int32,
+ *   topk_w [T,k] float.
+ */
+moe_status moe_gate_topk(const void *x, const void *Wg, const float *logit_bias,
+                         int T, int d, int E, int k, int renorm, moe_dtype dt,
+                         float *logits, int32_t *topk_idx, float *topk_w,
+                         hipStream_t stream);
+
+/*
+ * moe_permute -- stable counting sort of the (token, slot) pairs by expert
+ * and the row copy into expert-segment order.  No dispatch mask, no padding.
+ *   counts[e]   = number of pairs routed to e
+ *   offsets[e]  = sum_{e'<e} counts[e'], offsets[E] = T*k
+ *   dest[t,j]   = offsets[e] + #{t' < t : e in topk_idx[t']}, e = topk_idx[t,j]
+ *   src[r]      = token of permuted row r (src[dest[t,j]] = t)
+ *   x_perm[r,:] = x[src[r],:]
+ * Integer outputs are exact and independent of scheduling (no atomic-order
+ * dependence).  Sources: ES-MoE review, 三 技术架构 / 专家级卸载与处理 (tokens
+ * assigned to experts in sequence); FastMoE review, 제안 방법 (scatter/gather
+ * layout by expert).
+ *   topk_idx [T,k] int32 (each row: k distinct experts in [0,E)), x [T,d] dt,
+ *   counts [E], offsets [E+1], dest [T,k], src [T*k] int32, x_perm [T*k,d] dt.
+ *   ws: device workspace of at least moe_permute_workspace_bytes(T,E,k).
+ * Entries of topk_idx outside [0,E) give MOE_ERR_INVALID_ARG only if detected
+ * on the host; the kernels skip them (their dest entries are then undefined).
+ */
+size_t moe_permute_workspace_bytes(int T, int E, int k);
+moe_status moe_permute(const int32_t *topk_idx, const void *x, int T, int d,
+                       int E, int k, moe_dtype dt, int32_t *counts,
+                       int32_t *offsets, int32_t *dest, int32_t *src,
+                       void *x_perm, void *ws, size_t ws_bytes,
+                       hipStream_t stream);
+
+/*
+ * moe_expert_ffn_fwd -- every expert's FFN on its segment, one grouped GEMM
+ * per product over the ragged segments (rows offsets[e]..offsets[e+1]).
+ *   GeLU:   H = X_e W1[e], A = GeLU(H) (exact erf form), O = A W2[e]
+ *   SwiGLU: H1 = X_e W1[e], H3 = X_e W3[e], A = SiLU(H1)*H3, O = A W2[e]
+ * Source: FastMoE review, 제안 방법 (dedicated expert FFN, parallel expert
+ * linear layers); ES-MoE review, 三 技术架构 (experts take their tokens in
+ * sequence, no padding).
+ *   x_perm [R,d] dt, offsets [E+1] int32 (device; R = offsets[E]),
+ *   W1 [E,d,f], W3 [E,d,f] (SwiGLU only, else NULL), W2 [E,f,d] dt,
+ *   h_save [R,f] (GeLU: H) or [R,2f] (SwiGLU: row r = H1[r,:] then H3[r,:]),
+ *   a_save [R,f] (A), out_perm [R,d] dt.  Accumulation is fp32.
+ *   ws: at least moe_ffn_workspace_bytes(R,E,d,f,act,dt,0).
+ */
+size_t moe_ffn_workspace_bytes(int R, int E, int d, int f, moe_act act,
+                               moe_dtype dt, int backward);
+moe_status moe_expert_ffn_fwd(const void *x_perm, const int32_t *offsets,
+                              int R, int E, int d, int f, moe_act act,
+                              moe_dtype dt, const void *W1, const void *W3,
+                              const void *W2, void *h_save, void *a_save,
+                              void *out_perm, void *ws, size_t ws_bytes,
+                              hipStream_t stream);
+
+/*
+ * moe_expert_ffn_bwd -- gradients of moe_expert_ffn_fwd.
+ *   dA = dO W2[e]^T;  GeLU: dH = dA * GeLU'(H)
+ *                     SwiGLU: dH1 = dA*H3*SiLU'(H1), dH3 = dA*SiLU(H1)
+ *   dW2[e] = A_e^T dO_e;  dW1[e] = X_e^T dH(1)_e;  dW3[e] = X_e^T dH3_e
+ *   dx_perm = dH W1[e]^T (+ dH3 W3[e]^T)
+ * An expert with no rows gets dW = 0.  The dW products sum over the ragged
+ * segment length; each output tile is summed by one workgroup in order.
+ *   d_out_perm [R,d], x_perm [R,d], h_save, a_save as written by the forward,
+ *   dx_perm [R,d], dW1 [E,d,f], dW3 [E,d,f] (SwiGLU only), dW2 [E,f,d], dt.
+ *   ws: at least moe_ffn_workspace_bytes(R,E,d,f,act,dt,1) (holds dH).
+ */
+moe_status moe_expert_ffn_bwd(const void *d_out_perm, const void *x_perm,
+                              const void *h_save, const void *a_save,
+                              const int32_t *offsets, int R, int E, int d,
+                              int f, moe_act act, moe_dtype dt, const void *W1,
+                              const void *W3, const void *W2, void *dx_perm,
+                              void *dW1, void *dW3, void *dW2, void *ws,
+                              size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_combine -- y[t,:] = sum_{j=0..k-1} topk_w[t,j] * out_perm[dest[t,j],:],
+ * fp32 sum in slot order, rounded once to dt.  The gather back to token
+ * order (FastMoE review, 제안 방법).
+ *   out_perm [T*k,d] dt, dest [T,k] int32, topk_w [T,k] float, y [T,d] dt.
+ */
+moe_status moe_combine(const void *out_perm, const int32_t *dest,
+                       const float *topk_w, int T, int k, int d, moe_dtype dt,
+                       void *y, hipStream_t stream);
+
+/*
+ * moe_combine_bwd -- derivative of moe_combine:
+ *   d_out_perm[dest[t,j],:] = topk_w[t,j] * dy[t,:]
+ *   d_topk_w[t,j]           = sum_i dy[t,i] * out_perm[dest[t,j],i]  (fp32)
+ *   dy [T,d] dt, out_perm [T*k,d] dt, dest [T,k], topk_w [T,k] float,
+ *   d_out_perm [T*k,d] dt, d_topk_w [T,k] float.
+ */
+moe_status moe_combine_bwd(const void *dy, const void *out_perm,
+                           const int32_t *dest, const float *topk_w, int T,
+                           int k, int d, moe_dtype dt, void *d_out_perm,
+                           float *d_topk_w, hipStream_t stream);
+
+/*
+ * moe_unpermute_grad -- backward of moe_permute's row copy, the sum back to
+ * token order: dx[t,:] (+)= sum_j dx_perm[dest[t,j],:], gathered per token in
+ * slot order (deterministic, no atomics).
+ *   dx_perm [T*k,d] dt, dest [T,k] int32, dx [T,d] dt;
+ *   accumulate != 0 adds to dx instead of overwriting it.
+ */
+moe_status moe_unpermute_grad(const void *dx_perm, const int32_t *dest, int T,
+                              int k, int d, moe_dtype dt, void *dx,
+                              int accumulate, hipStream_t stream);
+
+/*
+ * moe_gate_topk_bwd -- backward of moe_gate_topk through the gate weights
+ * (the selection itself is piecewise constant):
+ *   renorm=1: dl[t,idx_j] = w_j (dw_j - sum_j' w_j' dw_j'), 0 elsewhere
+ *   renorm=0: dl[t,e] = p_e (g_e - sum_j w_j dw_j), p = softmax(logits[t,:]),
+ *             g_e = dw_j where e = idx_j else 0
+ *   dWg = x^T dl (overwritten; the sum over tokens runs in fixed chunks
+ *         reduced in order), dx += dl Wg^T (accumulated: call after
+ *         moe_unpermute_grad has written dx).
+ *   x [T,d] dt, Wg [d,E] dt, logits [T,E], topk_idx [T,k], topk_w [T,k],
+ *   d_topk_w [T,k] float, dx [T,d] dt, dWg [d,E] dt.
+ *   ws: at least moe_gate_bwd_workspace_bytes(T,d,E).
+ */
+size_t moe_gate_bwd_workspace_bytes(int T, int d, int E);
+moe_status moe_gate_topk_bwd(const void *x, const void *Wg, const float *logits,
+                             const int32_t *topk_idx, const float *topk_w,
+                             const float *d_topk_w, int T, int d, int E, int k,
+                             int renorm, moe_dtype dt, void *dx, void *dWg,
+                             void *ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

@@ -1,0 +1,114 @@
+// Shared helpers of the HIP kernels: element types, 16-byte vector access,
+// host-side validation and launch-status plumbing.  gfx950 only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// ----------------------------------------------------------------- types
+
+typedef uint16_t bf16_t;                       // raw bf16 bits in memory
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+    return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// Round to nearest even; NaN stays NaN (quiet).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// Element load/store in fp32 for the two storage types.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    static __device__ __forceinline__ float ld(const float* p) { return *p; }
+    static __device__ __forceinline__ void st(float* p, float v) { *p = v; }
+    static constexpr int kVec = 4;             // elements per 16 bytes
+};
+template <> struct Elem<bf16_t> {
+    static __device__ __forceinline__ float ld(const bf16_t* p) {
+        return bf16_to_f32(*p);
+    }
+    static __device__ __forceinline__ void st(bf16_t* p, float v) {
+        *p = f32_to_bf16(v);
+    }
+    static constexpr int kVec = 8;
+};
+
+// 16-byte vector <-> fp32 registers.
+template <typename T> struct Vec16;
+template <> struct Vec16<float> {
+    static constexpr int N = 4;
+    static __device__ __forceinline__ void ld(const float* p, float* o) {
+        float4 v = *reinterpret_cast<const float4*>(p);
+        o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+    }
+    static __device__ __forceinline__ void st(float* p, const float* o) {
+        *reinterpret_cast<float4*>(p) = make_float4(o[0], o[1], o[2], o[3]);
+    }
+};
+template <> struct Vec16<bf16_t> {
+    static constexpr int N = 8;
+    static __device__ __forceinline__ void ld(const bf16_t* p, float* o) {
+        uint4 v = *reinterpret_cast<const uint4*>(p);
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            o[2 * i] = __uint_as_float(w[i] << 16);
+            o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+    static __device__ __forceinline__ void st(bf16_t* p, const float* o) {
+        uint4 v;
+        v.x = pack_bf16x2(o[0], o[1]);
+        v.y = pack_bf16x2(o[2], o[3]);
+        v.z = pack_bf16x2(o[4], o[5]);
+        v.w = pack_bf16x2(o[6], o[7]);
+        *reinterpret_cast<uint4*>(p) = v;
+    }
+};
+
+// ------------------------------------------------------------ host side
+
+// Checks (once per device) that the current device is gfx950 and returns
+// its compute-unit count, or a negative moe_status.
+int device_cus();
+
+inline bool aligned16(const void* p) {
+    return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+inline int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+inline moe_status launch_status() {
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+}  // namespace moe
+
+#define MOE_CHECK_ARG(cond) \
+    do { if (!(cond)) return MOE_ERR_INVALID_ARG; } while (0)
+
+#define MOE_CHECK_DEVICE()                              \
+    do {                                                \
+        int cus_ = moe::device_cus();                   \
+        if (cus_ < 0) return (moe_status)cus_;          \
+    } while (0)

@@ -1,0 +1,492 @@
+// Gate: logits, top-k choice and gate weights (forward); gradient through
+// the gate weights into the logits, the gate matrix and the tokens (backward).
+//
+// Source: ES-MoE review (xllm-io), 三 技术架构 / 专家级卸载与处理 -- the
+// expert choice comes out of the gating network before any expert runs.
+// The page prints no gate formula; the reading here is a linear gate with a
+// softmax over the k selected logits (or over all E when renorm = 0).
+//
+// The logits decide integer routing, so they are summed in one fixed fp32
+// order: increasing feature index i, each product and each sum rounded.
+// This file is compiled with -ffp-contract=off so no multiply-add is fused
+// for fp32 inputs; for bf16 inputs the fp32 product is exact and an explicit
+// fused multiply-add gives the same bits.
+#include <float.h>
+
+#include "common.h"
+
+namespace moe {
+namespace {
+
+// ------------------------------------------------------------ logits
+// Block: 256 threads.  TE experts per block column (4 per thread), the rest
+// of the threads span tokens (4 per thread).  Feature chunks of KC are
+// staged in LDS; every thread keeps 4x4 independent fp32 chains.
+constexpr int KC = 16;
+
+template <typename T, int TE>
+__global__ __launch_bounds__(256) void gate_logits_kernel(
+    const T* __restrict__ x, const T* __restrict__ Wg,
+    const float* __restrict__ bias, int Tn, int d, int E,
+    float* __restrict__ logits) {
+#pragma clang fp contract(off)
+    constexpr int TX = TE / 4;            // threads across experts
+    constexpr int TY = 256 / TX;          // threads across tokens
+    constexpr int TT = 4 * TY;            // tokens per block
+    __shared__ float xs[KC][TT];
+    __shared__ float ws[KC][TE];
+    const int tid = threadIdx.x;
+    const int tx = tid % TX, ty = tid / TX;
+    const long t0 = (long)blockIdx.x * TT;
+    const int e0 = blockIdx.y * TE;
+    float acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = 0.0f;
+
+    for (int k0 = 0; k0 < d; k0 += KC) {
+        const int kmax = min(KC, d - k0);
+        for (int q = tid; q < TT * KC; q += 256) {
+            const int tok = q / KC, kk = q % KC;
+            const long t = t0 + tok;
+            float v = 0.0f;
+            if (t < Tn && kk < kmax) v = Elem<T>::ld(x + t * d + k0 + kk);
+            xs[kk][tok] = v;
+        }
+        for (int q = tid; q < KC * TE; q += 256) {
+            const int kk = q / TE, ee = q % TE;
+            float v = 0.0f;
+            if (kk < kmax && e0 + ee < E)
+                v = Elem<T>::ld(Wg + (long)(k0 + kk) * E + e0 + ee);
+            ws[kk][ee] = v;
+        }
+        __syncthreads();
+        for (int kk = 0; kk < kmax; ++kk) {
+            float xv[4], wv[4];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) xv[a] = xs[kk][ty * 4 + a];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) wv[b] = ws[kk][tx * 4 + b];
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    if constexpr (sizeof(T) == 2) {
+                        // exact product: one rounding either way
+                        acc[a][b] = __builtin_fmaf(xv[a], wv[b], acc[a][b]);
+                    } else {
+                        float p = xv[a] * wv[b];
+                        acc[a][b] = acc[a][b] + p;
+                    }
+                }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const long t = t0 + ty * 4 + a;
+        if (t >= Tn) continue;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int e = e0 + tx * 4 + b;
+            if (e >= E) continue;
+            float v = acc[a][b];
+            if (bias) v = v + bias[e];
+            logits[t * E + e] = v;
+        }
+    }
+}
+
+// ------------------------------------------------------------- top-k
+// One wave per token.  Lane l holds experts l, l+64, ...  Each of the k
+// rounds is a wave arg-max on (value desc, index asc); the winner is taken
+// out of its lane.  Selected logits wait in LDS for the weight pass.
+__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
+    return va > vb || (va == vb && ia < ib);
+}
+
+template <int NV>
+__global__ __launch_bounds__(256) void topk_kernel(
+    const float* __restrict__ logits, int Tn, int E, int k, int renorm,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+    extern __shared__ float sel_val[];       // [4][k]
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const long t = (long)blockIdx.x * 4 + wv;
+    if (t >= Tn) return;                      // whole wave leaves together
+    float* sv = sel_val + wv * k;
+    float v[NV];
+    uint32_t live = 0;
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+        const int e = lane + 64 * q;
+        v[q] = e < E ? logits[t * E + e] : -FLT_MAX;
+        if (e < E) live |= 1u << q;
+    }
+    float best0 = 0.0f;
+    for (int j = 0; j < k; ++j) {
+        float bv = -FLT_MAX;
+        int bi = 0x7fffffff;
+#pragma unroll
+        for (int q = 0; q < NV; ++q) {
+            const int e = lane + 64 * q;
+            if ((live >> q) & 1u) {
+                if (bi == 0x7fffffff || better(v[q], e, bv, bi)) {
+                    bv = v[q];
+                    bi = e;
+                }
+            }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const float ov = __shfl_xor(bv, off);
+            const int oi = __shfl_xor(bi, off);
+            if (oi != 0x7fffffff && (bi == 0x7fffffff || better(ov, oi, bv, bi))) {
+                bv = ov;
+                bi = oi;
+            }
+        }
+        if ((bi & 63) == lane) live &= ~(1u << (bi >> 6));
+        if (j == 0) best0 = bv;
+        if (lane == 0) {
+            topk_idx[t * k + j] = bi;
+            sv[j] = bv;
+        }
+    }
+    // normaliser
+    float den = 0.0f;
+    if (renorm) {
+        for (int j = lane; j < k; j += 64) den += expf(sv[j] - best0);
+    } else {
+#pragma unroll
+        for (int q = 0; q < NV; ++q)
+            if (lane + 64 * q < E) den += expf(v[q] - best0);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off);
+    const float inv = 1.0f / den;
+    for (int j = lane; j < k; j += 64)
+        topk_w[t * k + j] = expf(sv[j] - best0) * inv;
+}
+
+// ---------------------------------------------------------- backward
+// dl[t,:]: one wave per token (4 tokens per block).  slot[e] maps an expert
+// to its slot in the token's top-k, or -1.
+__global__ __launch_bounds__(256) void gate_dlogits_kernel(
+    const float* __restrict__ logits, const int32_t* __restrict__ topk_idx,
+    const float* __restrict__ topk_w, const float* __restrict__ dw, int Tn,
+    int E, int k, int renorm, float* __restrict__ dl) {
+    extern __shared__ int slot_mem[];         // [4][E]
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const long t = (long)blockIdx.x * 4 + wv;
+    const bool active = t < Tn;
+    int* slot = slot_mem + wv * E;
+    for (int e = lane; e < E; e += 64) slot[e] = -1;
+    __syncthreads();
+    float s = 0.0f;
+    if (active) {
+        for (int j = lane; j < k; j += 64) {
+            const int e = topk_idx[t * k + j];
+            if (e >= 0 && e < E) slot[e] = j;
+            s += topk_w[t * k + j] * dw[t * k + j];
+        }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    __syncthreads();
+    if (!active) return;
+    if (renorm) {
+        for (int e = lane; e < E; e += 64) {
+            const int j = slot[e];
+            dl[t * E + e] = j >= 0 ? topk_w[t * k + j] * (dw[t * k + j] - s) : 0.0f;
+        }
+        return;
+    }
+    float m = -FLT_MAX;
+    for (int e = lane; e < E; e += 64) m = fmaxf(m, logits[t * E + e]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    float z = 0.0f;
+    for (int e = lane; e < E; e += 64) z += expf(logits[t * E + e] - m);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off);
+    const float inv = 1.0f / z;
+    for (int e = lane; e < E; e += 64) {
+        const int j = slot[e];
+        const float g = j >= 0 ? dw[t * k + j] : 0.0f;
+        dl[t * E + e] = expf(logits[t * E + e] - m) * inv * (g - s);
+    }
+}
+
+// partial[c][i][e] = sum over tokens of chunk c (in order) of x[t,i]*dl[t,e].
+// Thread: one feature i and up to 8 experts; TPI threads share one i.
+constexpr int GB_TC = 1024;     // tokens per chunk
+constexpr int GB_TS = 8;        // tokens staged per LDS round
+
+template <typename T>
+__global__ __launch_bounds__(256) void gate_dwg_partial_kernel(
+    const T* __restrict__ x, const float* __restrict__ dl, int Tn, int d,
+    int E, int tpi, float* __restrict__ partial) {
+    extern __shared__ float sm[];
+    const int iw = 256 / tpi;
+    float* xs = sm;                           // [GB_TS][iw]
+    float* ds = sm + GB_TS * iw;              // [GB_TS][E]
+    const int tid = threadIdx.x;
+    const int il = tid % iw, eg = tid / iw;
+    const int i0 = blockIdx.y * iw;
+    const long c = blockIdx.x;
+    const long tbeg = c * GB_TC;
+    const long tend = min((long)Tn, tbeg + GB_TC);
+    float acc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+    for (long ts0 = tbeg; ts0 < tend; ts0 += GB_TS) {
+        const int nts = (int)min((long)GB_TS, tend - ts0);
+        for (int q = tid; q < GB_TS * iw; q += 256) {
+            const int tt = q / iw, ii = q % iw;
+            float v = 0.0f;
+            if (tt < nts && i0 + ii < d) v = Elem<T>::ld(x + (ts0 + tt) * d + i0 + ii);
+            xs[q] = v;
+        }
+        for (int q = tid; q < GB_TS * E; q += 256) {
+            const int tt = q / E, e = q % E;
+            ds[q] = tt < nts ? dl[(ts0 + tt) * E + e] : 0.0f;
+        }
+        __syncthreads();
+        for (int tt = 0; tt < nts; ++tt) {
+            const float xv = xs[tt * iw + il];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int e = eg * 8 + q;
+                if (e < E) acc[q] = fmaf(xv, ds[tt * E + e], acc[q]);
+            }
+        }
+        __syncthreads();
+    }
+    const int i = i0 + il;
+    if (i >= d) return;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int e = eg * 8 + q;
+        if (e < E) partial[(c * d + i) * E + e] = acc[q];
+    }
+}
+
+template <typename T>
+__global__ void gate_dwg_reduce_kernel(const float* __restrict__ partial,
+                                       int nchunk, long n, T* __restrict__ dWg) {
+    const long q = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (q >= n) return;
+    float s = 0.0f;
+    for (int c = 0; c < nchunk; ++c) s += partial[(long)c * n + q];
+    Elem<T>::st(dWg + q, s);
+}
+
+// WgT[e][i] = Wg[i][e] in fp32, so a gate column is contiguous.
+template <typename T>
+__global__ void gate_transpose_kernel(const T* __restrict__ Wg, int d, int E,
+                                      float* __restrict__ WgT) {
+    const long q = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (q >= (long)d * E) return;
+    const int i = (int)(q / E), e = (int)(q % E);
+    WgT[(long)e * d + i] = Elem<T>::ld(Wg + q);
+}
+
+// dx[t,:] += sum_e dl[t,e] WgT[e,:].  renorm=1 uses the k nonzero entries
+// only (coefficients recomputed from w and dw); renorm=0 reads dl.
+// One block of 256 threads per token, 16 bytes of dx per thread step.
+template <typename T>
+__global__ __launch_bounds__(256) void gate_dx_kernel(
+    const float* __restrict__ WgT, const float* __restrict__ dl,
+    const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_w,
+    const float* __restrict__ dw, int d, int E, int k, int renorm,
+    T* __restrict__ dx) {
+    extern __shared__ float coef_mem[];       // [E] coefficients (renorm=0) or [2k]
+    const long t = blockIdx.x;
+    const int tid = threadIdx.x;
+    int n;
+    if (renorm) {
+        // s = sum_j w_j dw_j, computed by one wave in a fixed tree order
+        float* c = coef_mem;
+        int* ci = reinterpret_cast<int*>(coef_mem + k);
+        if (tid < 64) {
+            float s = 0.0f;
+            for (int j = tid; j < k; j += 64) s += topk_w[t * k + j] * dw[t * k + j];
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+            for (int j = tid; j < k; j += 64) {
+                const int e = topk_idx[t * k + j];
+                const bool ok = e >= 0 && e < E;
+                c[j] = ok ? topk_w[t * k + j] * (dw[t * k + j] - s) : 0.0f;
+                ci[j] = ok ? e : 0;
+            }
+        }
+        n = k;
+    } else {
+        for (int e = tid; e < E; e += 256) coef_mem[e] = dl[t * E + e];
+        n = E;
+    }
+    __syncthreads();
+    constexpr int V = Vec16<T>::N;
+    const int* ci = reinterpret_cast<const int*>(coef_mem + k);
+    for (int i0 = tid * V; i0 < d; i0 += 256 * V) {
+        float acc[V];
+#pragma unroll
+        for (int q = 0; q < V; ++q) acc[q] = 0.0f;
+        for (int j = 0; j < n; ++j) {
+            const int e = renorm ? ci[j] : j;
+            const float cf = coef_mem[j];
+            const float* w = WgT + (long)e * d + i0;
+#pragma unroll
+            for (int q = 0; q < V; ++q) acc[q] = fmaf(cf, w[q], acc[q]);
+        }
+        float cur[V];
+        Vec16<T>::ld(dx + t * d + i0, cur);
+#pragma unroll
+        for (int q = 0; q < V; ++q) cur[q] = cur[q] + acc[q];
+        Vec16<T>::st(dx + t * d + i0, cur);
+    }
+}
+
+template <typename T>
+moe_status launch_logits(const void* x, const void* Wg, const float* bias,
+                         int Tn, int d, int E, float* logits, hipStream_t s) {
+    const T* xp = static_cast<const T*>(x);
+    const T* wp = static_cast<const T*>(Wg);
+    if (E <= 8) {
+        dim3 g(cdiv(Tn, 4 * (256 / 2)), cdiv(E, 8));
+        gate_logits_kernel<T, 8><<<g, 256, 0, s>>>(xp, wp, bias, Tn, d, E, logits);
+    } else if (E <= 16) {
+        dim3 g(cdiv(Tn, 4 * (256 / 4)), cdiv(E, 16));
+        gate_logits_kernel<T, 16><<<g, 256, 0, s>>>(xp, wp, bias, Tn, d, E, logits);
+    } else if (E <= 32) {
+        dim3 g(cdiv(Tn, 4 * (256 / 8)), cdiv(E, 32));
+        gate_logits_kernel<T, 32><<<g, 256, 0, s>>>(xp, wp, bias, Tn, d, E, logits);
+    } else {
+        dim3 g(cdiv(Tn, 4 * (256 / 16)), cdiv(E, 64));
+        gate_logits_kernel<T, 64><<<g, 256, 0, s>>>(xp, wp, bias, Tn, d, E, logits);
+    }
+    return launch_status();
+}
+
+moe_status launch_topk(const float* logits, int Tn, int E, int k, int renorm,
+                       int32_t* idx, float* w, hipStream_t s) {
+    const int blocks = cdiv(Tn, 4);
+    const size_t lds = sizeof(float) * 4 * (size_t)k;
+    const int nv = cdiv(E, 64);
+    if (nv <= 1)
+        topk_kernel<1><<<blocks, 256, lds, s>>>(logits, Tn, E, k, renorm, idx, w);
+    else if (nv <= 2)
+        topk_kernel<2><<<blocks, 256, lds, s>>>(logits, Tn, E, k, renorm, idx, w);
+    else if (nv <= 4)
+        topk_kernel<4><<<blocks, 256, lds, s>>>(logits, Tn, E, k, renorm, idx, w);
+    else if (nv <= 8)
+        topk_kernel<8><<<blocks, 256, lds, s>>>(logits, Tn, E, k, renorm, idx, w);
+    else
+        topk_kernel<16><<<blocks, 256, lds, s>>>(logits, Tn, E, k, renorm, idx, w);
+    return launch_status();
+}
+
+int threads_per_feature(int E) {
+    int need = (E + 7) / 8, tpi = 1;
+    while (tpi < need) tpi *= 2;
+    return tpi;
+}
+
+struct GateBwdWs {
+    size_t dl, wgt, partial, total;
+};
+
+GateBwdWs gate_bwd_layout(int Tn, int d, int E) {
+    GateBwdWs w;
+    const size_t nchunk = (size_t)cdiv(Tn, GB_TC);
+    w.dl = 0;
+    w.wgt = align_up(w.dl + sizeof(float) * (size_t)Tn * E, 256);
+    w.partial = align_up(w.wgt + sizeof(float) * (size_t)E * d, 256);
+    w.total = align_up(w.partial + sizeof(float) * nchunk * d * E, 256);
+    return w;
+}
+
+template <typename T>
+moe_status launch_gate_bwd(const void* x, const void* Wg, const float* logits,
+                           const int32_t* idx, const float* w, const float* dw,
+                           int Tn, int d, int E, int k, int renorm, void* dx,
+                           void* dWg, void* ws, hipStream_t s) {
+    const GateBwdWs L = gate_bwd_layout(Tn, d, E);
+    char* base = static_cast<char*>(ws);
+    float* dl = reinterpret_cast<float*>(base + L.dl);
+    float* wgt = reinterpret_cast<float*>(base + L.wgt);
+    float* partial = reinterpret_cast<float*>(base + L.partial);
+    const T* xp = static_cast<const T*>(x);
+
+    gate_transpose_kernel<T><<<cdiv((long)d * E, 256), 256, 0, s>>>(
+        static_cast<const T*>(Wg), d, E, wgt);
+    gate_dlogits_kernel<<<cdiv(Tn, 4), 256, sizeof(int) * 4 * (size_t)E, s>>>(
+        logits, idx, w, dw, Tn, E, k, renorm, dl);
+    const int tpi = threads_per_feature(E);
+    const int iw = 256 / tpi;
+    const int nchunk = cdiv(Tn, GB_TC);
+    dim3 g(nchunk, cdiv(d, iw));
+    const size_t lds = sizeof(float) * (size_t)GB_TS * (iw + E);
+    gate_dwg_partial_kernel<T><<<g, 256, lds, s>>>(xp, dl, Tn, d, E, tpi, partial);
+    const long n = (long)d * E;
+    gate_dwg_reduce_kernel<T><<<cdiv(n, 256), 256, 0, s>>>(
+        partial, nchunk, n, static_cast<T*>(dWg));
+    const size_t lds_dx = renorm ? sizeof(float) * 2 * (size_t)k : sizeof(float) * (size_t)E;
+    gate_dx_kernel<T><<<Tn, 256, lds_dx + 16, s>>>(wgt, dl, idx, w, dw, d, E, k,
+                                                    renorm, static_cast<T*>(dx));
+    return launch_status();
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+moe_status moe_gate_topk(const void* x, const void* Wg, const float* logit_bias,
+                         int T, int d, int E, int k, int renorm, moe_dtype dt,
+                         float* logits, int32_t* topk_idx, float* topk_w,
+                         hipStream_t stream) {
+    MOE_CHECK_ARG(T >= 0 && d >= 1 && E >= 1 && E <= 1024 && k >= 1 && k <= E);
+    MOE_CHECK_ARG((long long)T * k < (1ll << 31) && (long long)T * E < (1ll << 40));
+    MOE_CHECK_ARG(dt == MOE_F32 || dt == MOE_BF16);
+    if (T == 0) return MOE_OK;
+    MOE_CHECK_ARG(x && Wg && logits && topk_idx && topk_w);
+    MOE_CHECK_DEVICE();
+    moe_status st = dt == MOE_BF16
+        ? launch_logits<bf16_t>(x, Wg, logit_bias, T, d, E, logits, stream)
+        : launch_logits<float>(x, Wg, logit_bias, T, d, E, logits, stream);
+    if (st != MOE_OK) return st;
+    return launch_topk(logits, T, E, k, renorm, topk_idx, topk_w, stream);
+}
+
+size_t moe_gate_bwd_workspace_bytes(int T, int d, int E) {
+    if (T < 0 || d < 1 || E < 1) return 0;
+    return gate_bwd_layout(T, d, E).total;
+}
+
+moe_status moe_gate_topk_bwd(const void* x, const void* Wg, const float* logits,
+                             const int32_t* topk_idx, const float* topk_w,
+                             const float* d_topk_w, int T, int d, int E, int k,
+                             int renorm, moe_dtype dt, void* dx, void* dWg,
+                             void* ws, size_t ws_bytes, hipStream_t stream) {
+    MOE_CHECK_ARG(T >= 0 && d >= 1 && E >= 1 && E <= 1024 && k >= 1 && k <= E);
+    MOE_CHECK_ARG((long long)T * k < (1ll << 31));
+    MOE_CHECK_ARG(dt == MOE_F32 || dt == MOE_BF16);
+    const int vec = dt == MOE_BF16 ? 8 : 4;
+    MOE_CHECK_ARG(d % vec == 0);
+    MOE_CHECK_ARG(x && Wg && logits && topk_idx && topk_w && d_topk_w && dWg);
+    MOE_CHECK_ARG(T == 0 || dx);
+    MOE_CHECK_ARG(dx == nullptr || aligned16(dx));
+    if (ws_bytes < moe_gate_bwd_workspace_bytes(T, d, E) || !ws) return MOE_ERR_WORKSPACE;
+    MOE_CHECK_DEVICE();
+    return dt == MOE_BF16
+        ? launch_gate_bwd<bf16_t>(x, Wg, logits, topk_idx, topk_w, d_topk_w, T, d,
+                                  E, k, renorm, dx, dWg, ws, stream)
+        : launch_gate_bwd<float>(x, Wg, logits, topk_idx, topk_w, d_topk_w, T, d,
+                                 E, k, renorm, dx, dWg, ws, stream);
+}
+
+}  // extern "C"

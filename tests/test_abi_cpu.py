@@ -1,0 +1,100 @@
+"""The C-ABI library loads, exports every entry point include/moe.h
+declares, and rejects bad arguments on the host before any launch (CPU only:
+no compute call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_layer_permute_amd as M
+from mixture_experts_layer_permute_amd import _lib, build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        build.build()
+    return M.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("moe_gate_topk", "moe_permute", "moe_expert_ffn_fwd",
+              "moe_expert_ffn_bwd", "moe_combine", "moe_unpermute_grad",
+              "moe_combine_bwd", "moe_gate_topk_bwd"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+        assert n in _lib.SIGNATURES, "binding lacks " + n
+
+
+def test_binding_names_match_c_names():
+    for n in ("moe_gate_topk", "moe_permute", "moe_expert_ffn_fwd",
+              "moe_expert_ffn_bwd", "moe_combine", "moe_unpermute_grad",
+              "moe_combine_bwd", "moe_gate_topk_bwd", "moe_init"):
+        assert callable(getattr(M, n))
+
+
+def test_status_strings_and_version(lib):
+    assert lib.moe_abi_version() == 1
+    for s in (0, -1, -2, -3, -4):
+        assert lib.moe_status_string(s)
+
+
+def test_workspace_queries(lib):
+    assert lib.moe_permute_workspace_bytes(8192, 8, 2) > 0
+    assert lib.moe_permute_workspace_bytes(-1, 8, 2) == 0
+    # backward FFN workspace holds dH [R, f] (x2 for SwiGLU)
+    R, E, d, f = 16384, 8, 1024, 4096
+    bw = lib.moe_ffn_workspace_bytes(R, E, d, f, 0, 1, 1)
+    assert bw >= 2 * R * f
+    assert lib.moe_ffn_workspace_bytes(R, E, d, f, 1, 1, 1) >= 4 * R * f
+    assert lib.moe_ffn_workspace_bytes(R, E, d, 100, 0, 1, 0) == 0   # f % 64
+    assert lib.moe_gate_bwd_workspace_bytes(8192, 1024, 8) > 0
+
+
+def test_invalid_arguments_rejected_before_launch(lib):
+    N = None
+    INV = _lib.MOE_ERR_INVALID_ARG
+    # k > E
+    assert lib.moe_gate_topk(N, N, N, 10, 64, 4, 5, 1, 0, N, N, N, N) == INV
+    # E > 1024
+    assert lib.moe_gate_topk(N, N, N, 10, 64, 2000, 2, 1, 0, N, N, N, N) == INV
+    # bad dtype
+    assert lib.moe_gate_topk(N, N, N, 10, 64, 4, 1, 1, 7, N, N, N, N) == INV
+    # T = 0 is a no-op
+    assert lib.moe_gate_topk(N, N, N, 0, 64, 4, 1, 1, 0, N, N, N, N) == 0
+    # null pointers
+    assert lib.moe_gate_topk(N, N, N, 10, 64, 4, 1, 1, 0, N, N, N, N) == INV
+    # d not a multiple of 64 for the row kernels
+    assert lib.moe_combine(N, N, N, 10, 2, 100, 1, N, N) == INV
+    assert lib.moe_unpermute_grad(N, N, 10, 2, 100, 1, N, 0, N) == INV
+    # f not a multiple of 64
+    assert lib.moe_expert_ffn_fwd(N, N, 10, 2, 64, 100, 0, 1, N, N, N, N, N, N, N, 0,
+                                  N) == INV
+    # workspace too small
+    buf = ctypes.create_string_buffer(64)
+    p = ctypes.addressof(buf)
+    assert lib.moe_permute(p, p, 100, 64, 4, 2, 0, p, p, p, p, p, p, 0, N) == \
+        _lib.MOE_ERR_WORKSPACE
+
+
+def test_no_gpu_means_error_not_fallback(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("GPU present")
+    # valid arguments reach the device check, which fails without a GPU
+    assert lib.moe_init(0) in (_lib.MOE_ERR_HIP, _lib.MOE_ERR_UNSUPPORTED)

@@ -1,0 +1,63 @@
+"""Whole-layer parity: the eight entry points chained exactly as the
+benchmark chains them, on the workloads' own shapes and seeded inputs,
+against the oracle run on the host copy of the same inputs."""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_permute_amd as M
+import oracle
+from moe_inputs import CONFIGS, device, rng
+
+from _gpu import assert_close, assert_equal_i, banner, host, needs_gpu
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+
+def run_layer(cfg):
+    t = device.gen_all(cfg)
+    layer = M.MoELayer(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.act,
+                       device.torch_dtype(cfg), cfg.renorm)
+    layer.bind(t["x"], t["Wg"], t["W1"], t["W2"], t["W3"], t["bias"], t["dy"])
+    layer.step()
+    torch.cuda.synchronize()
+    return layer, t
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "moe_s_like"])
+def test_layer_full(name):
+    cfg = CONFIGS[name]
+    banner("layer full", name)
+    layer, t = run_layer(cfg)
+    x, Wg, dy = (rng.gen(cfg, n) for n in ("x", "Wg", "dy"))
+    W1, W2 = rng.gen_experts(cfg, "W1"), rng.gen_experts(cfg, "W2")
+    # the device generator reproduces the host inputs bit for bit
+    assert torch.equal(t["x"].cpu().float(), torch.from_numpy(x))
+    assert torch.equal(t["W2"].cpu().float(), torch.from_numpy(W2))
+    bias = rng.logit_bias(cfg)
+    fw = oracle.layer_forward(x, Wg, W1, W2, None, k=cfg.k, act=cfg.act, bias=bias,
+                              renorm=cfg.renorm)
+    gr = oracle.layer_backward(fw, dy, x, Wg, W1, W2, None, act=cfg.act,
+                               renorm=cfg.renorm)
+    dt = cfg.dtype
+    assert_equal_i(layer.logits.cpu().numpy().view(np.uint32),
+                   fw["logits"].view(np.uint32), "logits")
+    for n in ("idx", "counts", "offsets", "dest", "src"):
+        got = {"idx": layer.topk_idx}.get(n, getattr(layer, n, None))
+        assert_equal_i(got, fw[n], n)
+    assert_close(layer.topk_w, fw["w"], "f32", "topk_w")
+    assert_close(layer.x_perm, fw["x_perm"], dt, "x_perm")
+    assert_close(layer.h_save, fw["H"], dt, "H")
+    assert_close(layer.a_save, fw["A"], dt, "A")
+    assert_close(layer.out_perm, fw["out_perm"], dt, "out_perm")
+    assert_close(layer.y, fw["y"], dt, "y")
+    assert_close(layer.d_out_perm, gr["d_out_perm"], dt, "d_out_perm")
+    assert_close(layer.d_topk_w, gr["dw"], dt, "d_topk_w")
+    assert_close(layer.dx_perm, gr["dx_perm"], dt, "dx_perm")
+    assert_close(layer.dW1, gr["dW1"], dt, "dW1")
+    assert_close(layer.dW2, gr["dW2"], dt, "dW2")
+    assert_close(layer.dx, gr["dx"], dt, "dx")
+    if cfg.k > 1:
+        assert_close(layer.dWg, gr["dWg"], dt, "dWg")
+    else:
+        assert np.all(host(layer.dWg) == 0)
