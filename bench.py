@@ -1,0 +1,218 @@
+#!/usr/bin/env python3
+"""One MoE layer forward + backward step on one MI355X, timed.
+
+A step is the whole path: moe_gate_topk -> moe_permute -> moe_expert_ffn_fwd
+-> moe_combine -> moe_combine_bwd -> moe_expert_ffn_bwd -> moe_unpermute_grad
+-> moe_gate_topk_bwd, on inputs already resident in HBM.  Default workload:
+the MoE-S-like layer (T=8192 tokens, d=1024, f=4096, 8 experts, top-2,
+GeLU, bf16 storage with fp32 accumulation), seeded synthetic inputs.
+
+Prints ONE JSON line.  Besides tokens/s it reports the grouped-GEMM TFLOP/s,
+a per-kernel table from HIP events recorded around every kernel launch in a
+second timed pass, the roofline of the dominant kernel, and the CPU oracle
+timed on a bounded sample of the same workload (--no-cpu-baseline to skip).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("MoE layer fwd+bwd tokens/s and grouped-GEMM TFLOP/s "
+          "(% of bf16 MFMA peak)")
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA, 256 CU x 2.4 GHz
+PEAK_F32_TFLOPS = 157.3       # fp32 vector
+PEAK_HBM_GBS = 8000.0
+
+
+def kernel_work(cfg):
+    """Algorithmic work of one launch of each kernel: (amount, unit)."""
+    R, T, d, f, E, k = cfg.R, cfg.T, cfg.d, cfg.f, cfg.E, cfg.k
+    b = 2 if cfg.dtype == "bf16" else 4
+    g = 2.0 * R * d * f
+    w = {
+        "gemm_up_gelu": (g, "flop"), "gemm_up_swiglu": (2 * g, "flop"),
+        "gemm_down": (g, "flop"), "gemm_dA_gelu": (g, "flop"),
+        "gemm_dA_swiglu": (g, "flop"), "gemm_dW2": (g, "flop"),
+        "gemm_dW1": (g, "flop"), "gemm_dW3": (g, "flop"),
+        "gemm_dX": ((2 * g if cfg.swiglu else g), "flop"),
+        # bytes every memory-bound kernel must move at least once
+        "perm_copy": (T * d * b + R * d * b + 4 * R, "byte"),
+        "combine": (R * d * b + T * d * b + 8 * R, "byte"),
+        "combine_bwd": (T * d * b + 2 * R * d * b + 12 * R, "byte"),
+        "unpermute_grad": (R * d * b + T * d * b + 4 * R, "byte"),
+    }
+    return w
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="moe_s_like",
+                    help="workload name (moe_inputs.configs)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU work for the oracle baseline")
+    return ap.parse_args()
+
+
+def cpu_baseline(cfg, budget_s):
+    """The oracle, as it stands, on the host cores: full layer fwd+bwd."""
+    import numpy as np
+    import oracle
+    from moe_inputs import rng
+    from threadpoolctl import threadpool_info
+
+    # bounded sample: the first Ts tokens of the workload (all of it when it
+    # fits the budget); weights are the workload's own
+    Ts = cfg.T
+    x = rng.gen(cfg, "x")[:Ts]
+    dy = rng.gen(cfg, "dy")[:Ts]
+    Wg = rng.gen(cfg, "Wg")
+    W1 = rng.gen_experts(cfg, "W1")
+    W2 = rng.gen_experts(cfg, "W2")
+    W3 = rng.gen_experts(cfg, "W3") if cfg.swiglu else None
+    bias = rng.logit_bias(cfg)
+    reps, t_tot = 0, 0.0
+    while True:
+        t0 = time.perf_counter()
+        fw = oracle.layer_forward(x, Wg, W1, W2, W3, k=cfg.k, act=cfg.act,
+                                  bias=bias, renorm=cfg.renorm)
+        oracle.layer_backward(fw, dy, x, Wg, W1, W2, W3, act=cfg.act,
+                              renorm=cfg.renorm)
+        t_tot += time.perf_counter() - t0
+        reps += 1
+        if t_tot >= budget_s or reps >= 5:
+            break
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    cores = min(threads, len(os.sched_getaffinity(0)))
+    return {"value": reps * Ts / t_tot, "unit": "tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": "NumPy float64 oracle, full layer fwd+bwd of all %d tokens "
+                      "(%d rep%s, %.1f s)" % (Ts, reps, "s" if reps > 1 else "", t_tot)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(sharding is described in DESIGN.md); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import mixture_experts_layer_permute_amd as M
+    from mixture_experts_layer_permute_amd import _lib
+    from moe_inputs import CONFIGS, device
+
+    cfg = CONFIGS[args.workload]
+    torch.cuda.set_device(0)
+    M.moe_init(0)
+    t = device.gen_all(cfg)
+    layer = M.MoELayer(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.act,
+                       device.torch_dtype(cfg), cfg.renorm)
+    layer.bind(t["x"], t["Wg"], t["W1"], t["W2"], t["W3"], t["bias"], t["dy"])
+    stream = torch.cuda.current_stream()
+    s = stream.cuda_stream
+
+    for _ in range(args.warmup):
+        layer.step(s)
+    torch.cuda.synchronize()
+
+    # ---- headline: K steps, nothing else in the stream
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        layer.step(s)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = ev0.elapsed_time(ev1) / args.steps
+
+    # ---- per-kernel pass: HIP events around every launch, same K steps
+    L = _lib.load()
+    _lib.check(L.moe_profile_enable(args.steps * 40), "moe_profile_enable")
+    for _ in range(args.steps):
+        layer.step(s)
+    torch.cuda.synchronize()
+    recs = _lib.profile_records()
+    L.moe_profile_disable()
+    per = {}
+    for name, kms in recs:
+        per.setdefault(name, []).append(kms)
+    work = kernel_work(cfg)
+    kernels = {}
+    gemm_ms = 0.0
+    for name, v in per.items():
+        avg = sum(v) / len(v)
+        ent = {"avg_ms": round(avg, 5), "launches_per_step": len(v) / args.steps,
+               "ms_per_step": round(sum(v) / args.steps, 5)}
+        if name in work:
+            amt, unit = work[name]
+            if unit == "flop":
+                ent["tflops"] = round(amt / (avg * 1e-3) / 1e12, 2)
+                ent["frac_of_peak"] = round(ent["tflops"] / PEAK_BF16_TFLOPS, 4)
+                gemm_ms += sum(v) / args.steps
+            else:
+                ent["gbs"] = round(amt / (avg * 1e-3) / 1e9, 1)
+                ent["frac_of_peak"] = round(ent["gbs"] / PEAK_HBM_GBS, 4)
+        kernels[name] = ent
+    gemm_flops = cfg.gemm_flops_fwd_bwd()
+    dom = max(kernels, key=lambda n: kernels[n]["ms_per_step"])
+    amt, unit = work.get(dom, (None, None))
+    if unit == "flop":
+        peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+        ach = amt / (kernels[dom]["avg_ms"] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
+                "kernel": dom, "work_per_launch": amt}
+    elif unit == "byte":
+        ach = amt / (kernels[dom]["avg_ms"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                "traffic": None, "kernel": dom, "work_per_launch": amt}
+    else:
+        roof = {"bound": "alu", "achieved": None, "peak": None, "unit": None,
+                "frac": None, "traffic": None, "kernel": dom}
+
+    out = {
+        "metric": METRIC,
+        "value": round(cfg.T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded counter-based generator, inputs resident in HBM)",
+        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "f": cfg.f,
+                   "E": cfg.E, "k": cfg.k, "act": cfg.act, "renorm": cfg.renorm,
+                   "routing_skew_zipf_s": cfg.zipf_s},
+        "gemm_tflops_layer": round(gemm_flops / (ms * 1e-3) / 1e12, 2),
+        "gemm_tflops_kernels": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 2)
+        if gemm_ms else None,
+        "gemm_frac_of_bf16_peak": round(gemm_flops / (gemm_ms * 1e-3) / 1e12
+                                        / PEAK_BF16_TFLOPS, 4) if gemm_ms else None,
+        "wall_s_timed_region": round(wall, 4),
+        "roofline": roof,
+        "kernels": kernels,
+        "load": {"max_over_mean": round(float(layer.counts.max()) * cfg.E / cfg.R, 3),
+                 "empty_experts": int((layer.counts == 0).sum())},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

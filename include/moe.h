@@ -32,9 +32,10 @@
  *    status says why.  No C++ exception crosses this interface.
  *  - Outputs are overwritten unless an argument says "accumulated".
  *  - Bit-reproducible: no float atomics; every reduction has a fixed order.
- *  - Limits: 1 <= k <= E <= 1024; T*k < 2^31; d and f multiples of 64 for
- *    the FFN and for combine/unpermute (any d >= 1 for the gate).  T = 0 is
- *    accepted and launches nothing.
+ *  - Limits: 1 <= k <= E <= 1024; T*k < 2^31; d a multiple of 8 for the gate
+ *    and the permute, of 64 for the FFN, combine and unpermute; f a multiple
+ *    of 64; device pointers to rows 16-byte aligned.  T = 0 is accepted and
+ *    launches nothing.
  *  - Threads: entry points are reentrant; concurrent calls on different
  *    streams must not share output or workspace buffers.
  */
@@ -213,6 +214,23 @@ moe_status moe_gate_topk_bwd(const void *x, const void *Wg, const float *logits,
                              const float *d_topk_w, int T, int d, int E, int k,
                              int renorm, moe_dtype dt, void *dx, void *dWg,
                              void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Kernel timing (benchmark support, off by default).
+ * moe_profile_enable(capacity) creates 2*capacity HIP events; from then on
+ * every kernel the library launches is bracketed by two of them on its
+ * stream, until `capacity` launches have been recorded (later launches run
+ * untimed).  moe_profile_get(i, ...) waits for record i and returns the
+ * kernel's name (static storage) and its duration in milliseconds.
+ * moe_profile_reset() forgets the records and keeps the events;
+ * moe_profile_disable() destroys the events.  Not thread-safe: enable,
+ * launch and read from one host thread.
+ */
+moe_status moe_profile_enable(int capacity);
+void moe_profile_disable(void);
+void moe_profile_reset(void);
+int moe_profile_count(void);
+moe_status moe_profile_get(int i, const char **name, float *ms);
 
 #ifdef __cplusplus
 }

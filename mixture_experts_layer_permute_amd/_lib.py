@@ -35,6 +35,12 @@ SIGNATURES = {
     "moe_gate_bwd_workspace_bytes": (_Z, [_I, _I, _I]),
     "moe_gate_topk_bwd": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P,
                                _P, _Z, _P]),
+    "moe_profile_enable": (_I, [_I]),
+    "moe_profile_disable": (None, []),
+    "moe_profile_reset": (None, []),
+    "moe_profile_count": (_I, []),
+    "moe_profile_get": (_I, [_I, ctypes.POINTER(ctypes.c_char_p),
+                             ctypes.POINTER(ctypes.c_float)]),
 }
 
 _lib = None
@@ -60,6 +66,19 @@ def load(path: str = LIB_PATH):
         fn.argtypes = args
     _lib = lib
     return lib
+
+
+def profile_records():
+    """[(kernel name, ms)] of every launch timed since the last reset."""
+    L = load()
+    out = []
+    name = ctypes.c_char_p()
+    ms = ctypes.c_float()
+    for i in range(L.moe_profile_count()):
+        check(L.moe_profile_get(i, ctypes.byref(name), ctypes.byref(ms)),
+              "moe_profile_get")
+        out.append((name.value.decode(), float(ms.value)))
+    return out
 
 
 def check(status: int, what: str):

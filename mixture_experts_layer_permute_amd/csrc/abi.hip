@@ -1,6 +1,8 @@
 // Library-wide entry points: status text, version, device check.
 #include <string.h>
 
+#include <new>
+
 #include "common.h"
 
 namespace moe {
@@ -28,9 +30,86 @@ int device_cus() {
     return s;
 }
 
+// ------------------------------------------------------------ timing
+bool g_prof_on = false;
+
+namespace {
+struct ProfRec {
+    const char* name;
+    hipEvent_t a, b;
+};
+ProfRec* g_prof = nullptr;
+int g_prof_cap = 0, g_prof_n = 0;
+bool g_prof_open = false;
+}  // namespace
+
+void prof_mark(const char* name, hipStream_t s, int end) {
+    if (!end) {
+        if (g_prof_n >= g_prof_cap) return;
+        g_prof[g_prof_n].name = name;
+        (void)hipEventRecord(g_prof[g_prof_n].a, s);
+        g_prof_open = true;
+    } else {
+        if (!g_prof_open) return;
+        (void)hipEventRecord(g_prof[g_prof_n].b, s);
+        g_prof_open = false;
+        ++g_prof_n;
+    }
+}
+
 }  // namespace moe
 
 extern "C" {
+
+void moe_profile_disable(void) {
+    using namespace moe;
+    g_prof_on = false;
+    for (int i = 0; i < g_prof_cap; ++i) {
+        (void)hipEventDestroy(g_prof[i].a);
+        (void)hipEventDestroy(g_prof[i].b);
+    }
+    delete[] g_prof;
+    g_prof = nullptr;
+    g_prof_cap = g_prof_n = 0;
+    g_prof_open = false;
+}
+
+moe_status moe_profile_enable(int capacity) {
+    using namespace moe;
+    if (capacity < 1) return MOE_ERR_INVALID_ARG;
+    moe_profile_disable();
+    g_prof = new (std::nothrow) ProfRec[capacity];
+    if (!g_prof) return MOE_ERR_INVALID_ARG;
+    for (int i = 0; i < capacity; ++i) {
+        if (hipEventCreate(&g_prof[i].a) != hipSuccess ||
+            hipEventCreate(&g_prof[i].b) != hipSuccess) {
+            g_prof_cap = i;
+            moe_profile_disable();
+            return MOE_ERR_HIP;
+        }
+    }
+    g_prof_cap = capacity;
+    g_prof_n = 0;
+    g_prof_on = true;
+    return MOE_OK;
+}
+
+void moe_profile_reset(void) {
+    moe::g_prof_n = 0;
+    moe::g_prof_open = false;
+}
+
+int moe_profile_count(void) { return moe::g_prof_n; }
+
+moe_status moe_profile_get(int i, const char** name, float* ms) {
+    using namespace moe;
+    if (i < 0 || i >= g_prof_n || !name || !ms) return MOE_ERR_INVALID_ARG;
+    if (hipEventSynchronize(g_prof[i].b) != hipSuccess) return MOE_ERR_HIP;
+    if (hipEventElapsedTime(ms, g_prof[i].a, g_prof[i].b) != hipSuccess) return MOE_ERR_HIP;
+    *name = g_prof[i].name;
+    return MOE_OK;
+}
+
 
 const char* moe_status_string(moe_status s) {
     switch (s) {

@@ -181,13 +181,15 @@ moe_status moe_combine(const void* out_perm, const int32_t* dest,
     MOE_CHECK_ARG(aligned16(out_perm) && aligned16(y));
     MOE_CHECK_DEVICE();
     if (dt == MOE_BF16)
-        combine_kernel<bf16_t><<<cdiv(T, 4), 256, 0, stream>>>(
-            static_cast<const bf16_t*>(out_perm), dest, topk_w, T, k, d,
-            static_cast<bf16_t*>(y));
+        MOE_LAUNCH("combine", stream,
+            combine_kernel<bf16_t><<<cdiv(T, 4), 256, 0, stream>>>(
+                static_cast<const bf16_t*>(out_perm), dest, topk_w, T, k, d,
+                static_cast<bf16_t*>(y)));
     else
-        combine_kernel<float><<<cdiv(T, 4), 256, 0, stream>>>(
-            static_cast<const float*>(out_perm), dest, topk_w, T, k, d,
-            static_cast<float*>(y));
+        MOE_LAUNCH("combine", stream,
+            combine_kernel<float><<<cdiv(T, 4), 256, 0, stream>>>(
+                static_cast<const float*>(out_perm), dest, topk_w, T, k, d,
+                static_cast<float*>(y)));
     return launch_status();
 }
 
@@ -202,13 +204,15 @@ moe_status moe_combine_bwd(const void* dy, const void* out_perm,
     MOE_CHECK_ARG(aligned16(dy) && aligned16(out_perm) && aligned16(d_out_perm));
     MOE_CHECK_DEVICE();
     if (dt == MOE_BF16)
-        combine_bwd_kernel<bf16_t><<<cdiv(T, 4), 256, 0, stream>>>(
-            static_cast<const bf16_t*>(dy), static_cast<const bf16_t*>(out_perm),
-            dest, topk_w, T, k, d, static_cast<bf16_t*>(d_out_perm), d_topk_w);
+        MOE_LAUNCH("combine_bwd", stream,
+            combine_bwd_kernel<bf16_t><<<cdiv(T, 4), 256, 0, stream>>>(
+                static_cast<const bf16_t*>(dy), static_cast<const bf16_t*>(out_perm),
+                dest, topk_w, T, k, d, static_cast<bf16_t*>(d_out_perm), d_topk_w));
     else
-        combine_bwd_kernel<float><<<cdiv(T, 4), 256, 0, stream>>>(
-            static_cast<const float*>(dy), static_cast<const float*>(out_perm),
-            dest, topk_w, T, k, d, static_cast<float*>(d_out_perm), d_topk_w);
+        MOE_LAUNCH("combine_bwd", stream,
+            combine_bwd_kernel<float><<<cdiv(T, 4), 256, 0, stream>>>(
+                static_cast<const float*>(dy), static_cast<const float*>(out_perm),
+                dest, topk_w, T, k, d, static_cast<float*>(d_out_perm), d_topk_w));
     return launch_status();
 }
 
@@ -222,13 +226,15 @@ moe_status moe_unpermute_grad(const void* dx_perm, const int32_t* dest, int T,
     MOE_CHECK_ARG(aligned16(dx_perm) && aligned16(dx));
     MOE_CHECK_DEVICE();
     if (dt == MOE_BF16)
-        unpermute_grad_kernel<bf16_t><<<cdiv(T, 4), 256, 0, stream>>>(
-            static_cast<const bf16_t*>(dx_perm), dest, T, k, d, accumulate,
-            static_cast<bf16_t*>(dx));
+        MOE_LAUNCH("unpermute_grad", stream,
+            unpermute_grad_kernel<bf16_t><<<cdiv(T, 4), 256, 0, stream>>>(
+                static_cast<const bf16_t*>(dx_perm), dest, T, k, d, accumulate,
+                static_cast<bf16_t*>(dx)));
     else
-        unpermute_grad_kernel<float><<<cdiv(T, 4), 256, 0, stream>>>(
-            static_cast<const float*>(dx_perm), dest, T, k, d, accumulate,
-            static_cast<float*>(dx));
+        MOE_LAUNCH("unpermute_grad", stream,
+            unpermute_grad_kernel<float><<<cdiv(T, 4), 256, 0, stream>>>(
+                static_cast<const float*>(dx_perm), dest, T, k, d, accumulate,
+                static_cast<float*>(dx)));
     return launch_status();
 }
 

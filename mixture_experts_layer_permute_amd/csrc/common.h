@@ -21,16 +21,17 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t b) {
     return __uint_as_float(((uint32_t)b) << 16);
 }
 
-// Round to nearest even; NaN stays NaN (quiet).
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (bf16_t)(u >> 16);
-}
+// Round to nearest even (the gfx950 packed convert, NaN stays NaN).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+    return (bf16_t)(pack_bf16x2(f, 0.0f) & 0xffffu);
 }
 
 // Element load/store in fp32 for the two storage types.
@@ -97,12 +98,25 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 inline int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 
+// Kernel timing hooks (see moe_profile_enable).  prof_mark(name, s, 0)
+// before a launch, prof_mark(name, s, 1) after it; no-ops when disabled.
+extern bool g_prof_on;
+void prof_mark(const char* name, hipStream_t s, int end);
+
 inline moe_status launch_status() {
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 }  // namespace moe
+
+// Launch a kernel, bracketed by timing events when profiling is enabled.
+#define MOE_LAUNCH(NAME, STREAM, ...)                                  \
+    do {                                                              \
+        if (moe::g_prof_on) moe::prof_mark(NAME, STREAM, 0);          \
+        __VA_ARGS__;                                                  \
+        if (moe::g_prof_on) moe::prof_mark(NAME, STREAM, 1);          \
+    } while (0)
 
 #define MOE_CHECK_ARG(cond) \
     do { if (!(cond)) return MOE_ERR_INVALID_ARG; } while (0)

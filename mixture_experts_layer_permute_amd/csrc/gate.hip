@@ -19,79 +19,119 @@ namespace moe {
 namespace {
 
 // ------------------------------------------------------------ logits
-// Block: 256 threads.  TE experts per block column (4 per thread), the rest
-// of the threads span tokens (4 per thread).  Feature chunks of KC are
-// staged in LDS; every thread keeps 4x4 independent fp32 chains.
-constexpr int KC = 16;
+// Block: 256 threads.  TE experts per block column (4 per thread); the other
+// thread dimension spans tokens (MT per thread), so every thread carries
+// MT x 4 independent fp32 chains, each summed in increasing feature order.
+// Features come in chunks of GKC: the token rows are copied to LDS as raw
+// 16-byte vectors (padded rows), the gate columns as fp32, and the next
+// chunk is fetched into registers while the current one is consumed.
+constexpr int GKC = 64;
 
-template <typename T, int TE>
+template <typename T, int TE, int MT>
 __global__ __launch_bounds__(256) void gate_logits_kernel(
     const T* __restrict__ x, const T* __restrict__ Wg,
     const float* __restrict__ bias, int Tn, int d, int E,
     float* __restrict__ logits) {
 #pragma clang fp contract(off)
-    constexpr int TX = TE / 4;            // threads across experts
-    constexpr int TY = 256 / TX;          // threads across tokens
-    constexpr int TT = 4 * TY;            // tokens per block
-    __shared__ float xs[KC][TT];
-    __shared__ float ws[KC][TE];
+    constexpr int TX = TE / 4;                 // threads across experts
+    constexpr int TY = 256 / TX;               // threads across tokens
+    constexpr int TT = MT * TY;                // tokens per block
+    constexpr int V = 16 / sizeof(T);          // elements per 16-byte vector
+    constexpr int VPR = GKC / V;               // vectors per token per chunk
+    constexpr int XV = (TT * VPR + 255) / 256; // x vectors per thread per chunk
+    constexpr int XROW = GKC * sizeof(T) + 16; // padded LDS row (bytes)
+    constexpr int WV = (GKC * TE + 255) / 256; // gate elements per thread per chunk
+    __shared__ __attribute__((aligned(16))) uint8_t xs[TT * XROW];
+    __shared__ __attribute__((aligned(16))) float ws[GKC][TE];
+
     const int tid = threadIdx.x;
     const int tx = tid % TX, ty = tid / TX;
     const long t0 = (long)blockIdx.x * TT;
     const int e0 = blockIdx.y * TE;
-    float acc[4][4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = 0.0f;
 
-    for (int k0 = 0; k0 < d; k0 += KC) {
-        const int kmax = min(KC, d - k0);
-        for (int q = tid; q < TT * KC; q += 256) {
-            const int tok = q / KC, kk = q % KC;
+    uint4 xr[XV];
+    float wr[WV];
+    auto fetch = [&](int k0) {
+#pragma unroll
+        for (int q = 0; q < XV; ++q) {
+            const int idx = tid + 256 * q;
+            const int tok = idx / VPR, c = idx % VPR;
             const long t = t0 + tok;
-            float v = 0.0f;
-            if (t < Tn && kk < kmax) v = Elem<T>::ld(x + t * d + k0 + kk);
-            xs[kk][tok] = v;
+            const int k = k0 + c * V;
+            xr[q] = make_uint4(0, 0, 0, 0);
+            if (idx < TT * VPR && t < Tn && k < d)
+                xr[q] = *reinterpret_cast<const uint4*>(x + t * d + k);
         }
-        for (int q = tid; q < KC * TE; q += 256) {
-            const int kk = q / TE, ee = q % TE;
-            float v = 0.0f;
-            if (kk < kmax && e0 + ee < E)
-                v = Elem<T>::ld(Wg + (long)(k0 + kk) * E + e0 + ee);
-            ws[kk][ee] = v;
+#pragma unroll
+        for (int q = 0; q < WV; ++q) {
+            const int idx = tid + 256 * q;
+            const int kk = idx / TE, ee = idx % TE;
+            wr[q] = 0.0f;
+            if (idx < GKC * TE && k0 + kk < d && e0 + ee < E)
+                wr[q] = Elem<T>::ld(Wg + (long)(k0 + kk) * E + e0 + ee);
         }
+    };
+    auto stash = [&]() {
+#pragma unroll
+        for (int q = 0; q < XV; ++q) {
+            const int idx = tid + 256 * q;
+            if (idx < TT * VPR)
+                *reinterpret_cast<uint4*>(xs + (idx / VPR) * XROW + (idx % VPR) * 16) = xr[q];
+        }
+#pragma unroll
+        for (int q = 0; q < WV; ++q) {
+            const int idx = tid + 256 * q;
+            if (idx < GKC * TE) ws[idx / TE][idx % TE] = wr[q];
+        }
+    };
+
+    float acc[MT][4];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[m][b] = 0.0f;
+
+    fetch(0);
+    for (int k0 = 0; k0 < d; k0 += GKC) {
         __syncthreads();
-        for (int kk = 0; kk < kmax; ++kk) {
-            float xv[4], wv[4];
+        stash();
+        __syncthreads();
+        if (k0 + GKC < d) fetch(k0 + GKC);
+        const int kmax = min(GKC, d - k0);          // a multiple of V
+        for (int kv = 0; kv < kmax / V; ++kv) {
+            float xv[MT][V];
 #pragma unroll
-            for (int a = 0; a < 4; ++a) xv[a] = xs[kk][ty * 4 + a];
+            for (int m = 0; m < MT; ++m)
+                Vec16<T>::ld(reinterpret_cast<const T*>(xs + (ty * MT + m) * XROW + kv * 16),
+                             xv[m]);
 #pragma unroll
-            for (int b = 0; b < 4; ++b) wv[b] = ws[kk][tx * 4 + b];
+            for (int q = 0; q < V; ++q) {
+                const float4 w4 = *reinterpret_cast<const float4*>(&ws[kv * V + q][tx * 4]);
+                const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
+                for (int m = 0; m < MT; ++m)
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    if constexpr (sizeof(T) == 2) {
-                        // exact product: one rounding either way
-                        acc[a][b] = __builtin_fmaf(xv[a], wv[b], acc[a][b]);
-                    } else {
-                        float p = xv[a] * wv[b];
-                        acc[a][b] = acc[a][b] + p;
+                    for (int b = 0; b < 4; ++b) {
+                        if constexpr (sizeof(T) == 2) {
+                            // exact product: one rounding either way
+                            acc[m][b] = __builtin_fmaf(xv[m][q], wv[b], acc[m][b]);
+                        } else {
+                            const float pr = xv[m][q] * wv[b];
+                            acc[m][b] = acc[m][b] + pr;
+                        }
                     }
-                }
+            }
         }
-        __syncthreads();
     }
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-        const long t = t0 + ty * 4 + a;
+    for (int m = 0; m < MT; ++m) {
+        const long t = t0 + ty * MT + m;
         if (t >= Tn) continue;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const int e = e0 + tx * 4 + b;
             if (e >= E) continue;
-            float v = acc[a][b];
+            float v = acc[m][b];
             if (bias) v = v + bias[e];
             logits[t * E + e] = v;
         }
@@ -220,13 +260,12 @@ __global__ __launch_bounds__(256) void gate_dlogits_kernel(
 
 // partial[c][i][e] = sum over tokens of chunk c (in order) of x[t,i]*dl[t,e].
 // Thread: one feature i and up to 8 experts; TPI threads share one i.
-constexpr int GB_TC = 1024;     // tokens per chunk
 constexpr int GB_TS = 8;        // tokens staged per LDS round
 
 template <typename T>
 __global__ __launch_bounds__(256) void gate_dwg_partial_kernel(
     const T* __restrict__ x, const float* __restrict__ dl, int Tn, int d,
-    int E, int tpi, float* __restrict__ partial) {
+    int E, int tpi, int tc, float* __restrict__ partial) {
     extern __shared__ float sm[];
     const int iw = 256 / tpi;
     float* xs = sm;                           // [GB_TS][iw]
@@ -235,8 +274,8 @@ __global__ __launch_bounds__(256) void gate_dwg_partial_kernel(
     const int il = tid % iw, eg = tid / iw;
     const int i0 = blockIdx.y * iw;
     const long c = blockIdx.x;
-    const long tbeg = c * GB_TC;
-    const long tend = min((long)Tn, tbeg + GB_TC);
+    const long tbeg = c * tc;
+    const long tend = min((long)Tn, tbeg + tc);
     float acc[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
@@ -353,18 +392,23 @@ moe_status launch_logits(const void* x, const void* Wg, const float* bias,
                          int Tn, int d, int E, float* logits, hipStream_t s) {
     const T* xp = static_cast<const T*>(x);
     const T* wp = static_cast<const T*>(Wg);
+    // tokens per block = MT * 256 / (TE / 4)
     if (E <= 8) {
-        dim3 g(cdiv(Tn, 4 * (256 / 2)), cdiv(E, 8));
-        gate_logits_kernel<T, 8><<<g, 256, 0, s>>>(xp, wp, bias, Tn, d, E, logits);
+        dim3 g(cdiv(Tn, 128), cdiv(E, 8));
+        MOE_LAUNCH("gate_logits", s,
+            gate_logits_kernel<T, 8, 1><<<g, 256, 0, s>>>(xp, wp, bias, Tn, d, E, logits));
     } else if (E <= 16) {
-        dim3 g(cdiv(Tn, 4 * (256 / 4)), cdiv(E, 16));
-        gate_logits_kernel<T, 16><<<g, 256, 0, s>>>(xp, wp, bias, Tn, d, E, logits);
+        dim3 g(cdiv(Tn, 64), cdiv(E, 16));
+        MOE_LAUNCH("gate_logits", s,
+            gate_logits_kernel<T, 16, 1><<<g, 256, 0, s>>>(xp, wp, bias, Tn, d, E, logits));
     } else if (E <= 32) {
-        dim3 g(cdiv(Tn, 4 * (256 / 8)), cdiv(E, 32));
-        gate_logits_kernel<T, 32><<<g, 256, 0, s>>>(xp, wp, bias, Tn, d, E, logits);
+        dim3 g(cdiv(Tn, 64), cdiv(E, 32));
+        MOE_LAUNCH("gate_logits", s,
+            gate_logits_kernel<T, 32, 2><<<g, 256, 0, s>>>(xp, wp, bias, Tn, d, E, logits));
     } else {
-        dim3 g(cdiv(Tn, 4 * (256 / 16)), cdiv(E, 64));
-        gate_logits_kernel<T, 64><<<g, 256, 0, s>>>(xp, wp, bias, Tn, d, E, logits);
+        dim3 g(cdiv(Tn, 32), cdiv(E, 64));
+        MOE_LAUNCH("gate_logits", s,
+            gate_logits_kernel<T, 64, 2><<<g, 256, 0, s>>>(xp, wp, bias, Tn, d, E, logits));
     }
     return launch_status();
 }
@@ -375,15 +419,20 @@ moe_status launch_topk(const float* logits, int Tn, int E, int k, int renorm,
     const size_t lds = sizeof(float) * 4 * (size_t)k;
     const int nv = cdiv(E, 64);
     if (nv <= 1)
-        topk_kernel<1><<<blocks, 256, lds, s>>>(logits, Tn, E, k, renorm, idx, w);
+        MOE_LAUNCH("topk", s,
+            topk_kernel<1><<<blocks, 256, lds, s>>>(logits, Tn, E, k, renorm, idx, w));
     else if (nv <= 2)
-        topk_kernel<2><<<blocks, 256, lds, s>>>(logits, Tn, E, k, renorm, idx, w);
+        MOE_LAUNCH("topk", s,
+            topk_kernel<2><<<blocks, 256, lds, s>>>(logits, Tn, E, k, renorm, idx, w));
     else if (nv <= 4)
-        topk_kernel<4><<<blocks, 256, lds, s>>>(logits, Tn, E, k, renorm, idx, w);
+        MOE_LAUNCH("topk", s,
+            topk_kernel<4><<<blocks, 256, lds, s>>>(logits, Tn, E, k, renorm, idx, w));
     else if (nv <= 8)
-        topk_kernel<8><<<blocks, 256, lds, s>>>(logits, Tn, E, k, renorm, idx, w);
+        MOE_LAUNCH("topk", s,
+            topk_kernel<8><<<blocks, 256, lds, s>>>(logits, Tn, E, k, renorm, idx, w));
     else
-        topk_kernel<16><<<blocks, 256, lds, s>>>(logits, Tn, E, k, renorm, idx, w);
+        MOE_LAUNCH("topk", s,
+            topk_kernel<16><<<blocks, 256, lds, s>>>(logits, Tn, E, k, renorm, idx, w));
     return launch_status();
 }
 
@@ -393,13 +442,22 @@ int threads_per_feature(int E) {
     return tpi;
 }
 
+// Tokens per dWg chunk: enough chunks that chunks x feature tiles gives
+// about 512 workgroups, each chunk a multiple of 64 tokens, at most 4096.
+int gate_chunk(int Tn, int d, int E) {
+    const int ntile = cdiv(d, 256 / threads_per_feature(E));
+    const int want = max(1, 512 / ntile);
+    int tc = cdiv(cdiv(Tn, want), 64) * 64;
+    return min(4096, max(64, tc));
+}
+
 struct GateBwdWs {
     size_t dl, wgt, partial, total;
 };
 
 GateBwdWs gate_bwd_layout(int Tn, int d, int E) {
     GateBwdWs w;
-    const size_t nchunk = (size_t)cdiv(Tn, GB_TC);
+    const size_t nchunk = (size_t)cdiv(Tn, gate_chunk(Tn, d, E));
     w.dl = 0;
     w.wgt = align_up(w.dl + sizeof(float) * (size_t)Tn * E, 256);
     w.partial = align_up(w.wgt + sizeof(float) * (size_t)E * d, 256);
@@ -419,22 +477,28 @@ moe_status launch_gate_bwd(const void* x, const void* Wg, const float* logits,
     float* partial = reinterpret_cast<float*>(base + L.partial);
     const T* xp = static_cast<const T*>(x);
 
-    gate_transpose_kernel<T><<<cdiv((long)d * E, 256), 256, 0, s>>>(
-        static_cast<const T*>(Wg), d, E, wgt);
-    gate_dlogits_kernel<<<cdiv(Tn, 4), 256, sizeof(int) * 4 * (size_t)E, s>>>(
-        logits, idx, w, dw, Tn, E, k, renorm, dl);
+    MOE_LAUNCH("gate_transpose", s,
+        gate_transpose_kernel<T><<<cdiv((long)d * E, 256), 256, 0, s>>>(
+            static_cast<const T*>(Wg), d, E, wgt));
+    MOE_LAUNCH("gate_dlogits", s,
+        gate_dlogits_kernel<<<cdiv(Tn, 4), 256, sizeof(int) * 4 * (size_t)E, s>>>(
+            logits, idx, w, dw, Tn, E, k, renorm, dl));
     const int tpi = threads_per_feature(E);
     const int iw = 256 / tpi;
-    const int nchunk = cdiv(Tn, GB_TC);
+    const int tc = gate_chunk(Tn, d, E);
+    const int nchunk = cdiv(Tn, tc);
     dim3 g(nchunk, cdiv(d, iw));
     const size_t lds = sizeof(float) * (size_t)GB_TS * (iw + E);
-    gate_dwg_partial_kernel<T><<<g, 256, lds, s>>>(xp, dl, Tn, d, E, tpi, partial);
+    MOE_LAUNCH("gate_dwg_partial", s,
+        gate_dwg_partial_kernel<T><<<g, 256, lds, s>>>(xp, dl, Tn, d, E, tpi, tc, partial));
     const long n = (long)d * E;
-    gate_dwg_reduce_kernel<T><<<cdiv(n, 256), 256, 0, s>>>(
-        partial, nchunk, n, static_cast<T*>(dWg));
+    MOE_LAUNCH("gate_dwg_reduce", s,
+        gate_dwg_reduce_kernel<T><<<cdiv(n, 256), 256, 0, s>>>(
+            partial, nchunk, n, static_cast<T*>(dWg)));
     const size_t lds_dx = renorm ? sizeof(float) * 2 * (size_t)k : sizeof(float) * (size_t)E;
-    gate_dx_kernel<T><<<Tn, 256, lds_dx + 16, s>>>(wgt, dl, idx, w, dw, d, E, k,
-                                                    renorm, static_cast<T*>(dx));
+    MOE_LAUNCH("gate_dx", s,
+        gate_dx_kernel<T><<<Tn, 256, lds_dx + 16, s>>>(wgt, dl, idx, w, dw, d, E, k,
+                                                        renorm, static_cast<T*>(dx)));
     return launch_status();
 }
 
@@ -452,8 +516,10 @@ moe_status moe_gate_topk(const void* x, const void* Wg, const float* logit_bias,
     MOE_CHECK_ARG(T >= 0 && d >= 1 && E >= 1 && E <= 1024 && k >= 1 && k <= E);
     MOE_CHECK_ARG((long long)T * k < (1ll << 31) && (long long)T * E < (1ll << 40));
     MOE_CHECK_ARG(dt == MOE_F32 || dt == MOE_BF16);
+    MOE_CHECK_ARG(d % 8 == 0);
     if (T == 0) return MOE_OK;
     MOE_CHECK_ARG(x && Wg && logits && topk_idx && topk_w);
+    MOE_CHECK_ARG(aligned16(x));
     MOE_CHECK_DEVICE();
     moe_status st = dt == MOE_BF16
         ? launch_logits<bf16_t>(x, Wg, logit_bias, T, d, E, logits, stream)

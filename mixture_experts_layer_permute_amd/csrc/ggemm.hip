@@ -72,6 +72,9 @@ struct EpiStore {            // C[e*cstride + row*ldc + col] = v
     __device__ __forceinline__ void operator()(int e, long row, int col, float v) const {
         Elem<T>::st(C + e * cstride + row * ldc + col, v);
     }
+    __device__ __forceinline__ void vec8(int e, long row, int col, const float* v) const {
+        Vec16<T>::st(C + e * cstride + row * ldc + col, v);
+    }
 };
 
 template <typename T>
@@ -82,6 +85,13 @@ struct EpiGeluFwd {          // H = v, A = GeLU(v)
     __device__ __forceinline__ void operator()(int, long row, int col, float v) const {
         Elem<T>::st(H + row * ld + col, v);
         Elem<T>::st(A + row * ld + col, gelu_f(v));
+    }
+    __device__ __forceinline__ void vec8(int, long row, int col, const float* v) const {
+        float a[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) a[q] = gelu_f(v[q]);
+        Vec16<T>::st(H + row * ld + col, v);
+        Vec16<T>::st(A + row * ld + col, a);
     }
 };
 
@@ -96,6 +106,15 @@ struct EpiSwigluFwd {        // H1 = v1, H3 = v3 (row = [H1 | H3]), A = SiLU(v1)
         Elem<T>::st(H + row * 2 * f + f + col, v3);
         Elem<T>::st(A + row * f + col, v1 * sigmoid_f(v1) * v3);
     }
+    __device__ __forceinline__ void vec8(int, long row, int col, const float* v1,
+                                         const float* v3) const {
+        float a[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) a[q] = v1[q] * sigmoid_f(v1[q]) * v3[q];
+        Vec16<T>::st(H + row * 2 * f + col, v1);
+        Vec16<T>::st(H + row * 2 * f + f + col, v3);
+        Vec16<T>::st(A + row * f + col, a);
+    }
 };
 
 template <typename T>
@@ -106,6 +125,13 @@ struct EpiGeluBwd {          // dH = dA * GeLU'(H)
     __device__ __forceinline__ void operator()(int, long row, int col, float v) const {
         const float h = Elem<T>::ld(H + row * ld + col);
         Elem<T>::st(dH + row * ld + col, v * gelu_grad_f(h));
+    }
+    __device__ __forceinline__ void vec8(int, long row, int col, const float* v) const {
+        float h[8], o[8];
+        Vec16<T>::ld(H + row * ld + col, h);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) o[q] = v[q] * gelu_grad_f(h[q]);
+        Vec16<T>::st(dH + row * ld + col, o);
     }
 };
 
@@ -120,6 +146,19 @@ struct EpiSwigluBwd {        // dH1 = dA H3 SiLU'(H1), dH3 = dA SiLU(H1)
         const float s = sigmoid_f(h1);
         Elem<T>::st(dH + row * 2 * f + col, v * h3 * s * (1.0f + h1 * (1.0f - s)));
         Elem<T>::st(dH + row * 2 * f + f + col, v * h1 * s);
+    }
+    __device__ __forceinline__ void vec8(int, long row, int col, const float* v) const {
+        float h1[8], h3[8], o1[8], o3[8];
+        Vec16<T>::ld(H + row * 2 * f + col, h1);
+        Vec16<T>::ld(H + row * 2 * f + f + col, h3);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const float sg = sigmoid_f(h1[q]);
+            o1[q] = v[q] * h3[q] * sg * (1.0f + h1[q] * (1.0f - sg));
+            o3[q] = v[q] * h1[q] * sg;
+        }
+        Vec16<T>::st(dH + row * 2 * f + col, o1);
+        Vec16<T>::st(dH + row * 2 * f + f + col, o3);
     }
 };
 
@@ -184,97 +223,110 @@ __device__ __forceinline__ int swz(int r, int c) {
     return r * 128 + ((c ^ ((r ^ (r >> 3)) & 7)) << 4);
 }
 
-// Registers holding one operand tile between its global load and LDS store.
-// ROWS = extent along M (operand A) or N (operand B).
+// ------------------------------------------------------------- loads
+// Operand tiles are read with raw buffer loads: the descriptor's byte range
+// covers exactly the valid part of the tile, and the hardware returns zeros
+// for any lane whose offset falls outside it.  Ragged segment ends, the end
+// of the reduction, partial M/N tiles and the end of the allocation need no
+// branches.  A descriptor is rebuilt per k-tile from scalar registers.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+constexpr uint32_t OOB = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const bf16_t* base,
+                                                            long nbytes) {
+    const uint32_t n = nbytes <= 0 ? 0u : (uint32_t)nbytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(base), 0, n, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return __builtin_bit_cast(uint4, v);
+}
+
+// One operand tile (ROWS x 64 along M or N by K) in flight between its
+// global load and its LDS store.
+//  KMAJ : elem(row, k) = P[row * ld + k],  rows < row_lim valid
+//  MNMAJ: elem(row, k) = P[k * ld + row],  rows < row_lim, k < k_lim valid
+// P points at the tile origin (first row / first column, k = 0).
 template <int ROWS, int LAY>
-struct OpRegs {
-    // KMAJ: ROWS*8 chunks of 16 B over 256 threads.
-    // MNMAJ: ROWS 8x8 blocks, one per thread while ROWS <= 256.
-    static constexpr int NKM = ROWS * 8 / 256;
-    static constexpr int NREG = LAY == KMAJ ? NKM : 8;
+struct Operand {
+    static constexpr int NB = ROWS / 8;                      // MNMAJ column groups
+    static constexpr int NREG = LAY == KMAJ ? ROWS * 8 / 256 : 8;
+    const bf16_t* P;
+    long ld;
+    int row_lim;
+    long k_lim;
+    uint32_t off0;     // lane offset (bytes) of its first 16-byte piece
     uint4 r[NREG];
-};
 
-// Load the (ROWS x 64) slice starting at reduction index k0.
-//  KMAJ : elem(row, k) = P[(row) * ld + k0 + k], row < row_lim
-//  MNMAJ: elem(row, k) = P[(k0 + k) * ld + row], row < row_lim, k0+k < k_lim
-// P already points at the tile's first row / column.
-template <int ROWS, int LAY>
-__device__ __forceinline__ void op_load(OpRegs<ROWS, LAY>& R, const bf16_t* P, long ld,
-                                        int row_lim, long k0, long k_lim) {
-    const int tid = threadIdx.x;
-    if (LAY == KMAJ) {
-#pragma unroll
-        for (int i = 0; i < R.NREG; ++i) {
-            const int q = tid + 256 * i;
-            const int row = q >> 3, c = q & 7;
-            if (row < row_lim)
-                R.r[i] = *reinterpret_cast<const uint4*>(P + (long)row * ld + k0 + c * 8);
-            else
-                R.r[i] = make_uint4(0, 0, 0, 0);
-        }
-    } else {
-        constexpr int NB = ROWS / 8;         // 8-wide column groups
-        const int cb = tid % NB, kb = tid / NB;
-        const bool act = tid < ROWS;         // ROWS blocks in total
-        const bool col_ok = cb * 8 < row_lim;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const long k = k0 + kb * 8 + i;
-            if (act && col_ok && k < k_lim)
-                R.r[i] = *reinterpret_cast<const uint4*>(P + k * ld + cb * 8);
-            else
-                R.r[i] = make_uint4(0, 0, 0, 0);
+    __device__ __forceinline__ void init(const bf16_t* P_, long ld_, int row_lim_,
+                                         long k_lim_) {
+        P = P_;
+        ld = ld_;
+        row_lim = row_lim_;
+        k_lim = k_lim_;
+        const int tid = threadIdx.x;
+        if (LAY == KMAJ) {
+            off0 = (uint32_t)((tid >> 3) * ld * 2 + (tid & 7) * 16);
+        } else {
+            const int cb = tid % NB, kb = tid / NB;
+            const bool ok = tid < ROWS && cb * 8 < row_lim;
+            off0 = ok ? (uint32_t)(kb * 8 * ld * 2 + cb * 16) : OOB;
         }
     }
-}
 
-__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) {
-    return (a & 0xffffu) | (b << 16);
-}
-__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) {
-    return (a >> 16) | (b & 0xffff0000u);
-}
+    __device__ __forceinline__ void load(long k0) {
+        if (LAY == KMAJ) {
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(P + k0, (long)row_lim * ld * 2 - k0 * 2);
+            const uint32_t step = (uint32_t)(32 * ld * 2);
+#pragma unroll
+            for (int i = 0; i < NREG; ++i) r[i] = bload16(rs, off0 + i * step);
+        } else {
+            const long kv = min((long)BK, k_lim - k0);
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(P + k0 * ld, kv * ld * 2);
+            const uint32_t step = (uint32_t)(ld * 2);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                r[i] = bload16(rs, off0 == OOB ? OOB : off0 + i * step);
+        }
+    }
 
-template <int ROWS, int LAY>
-__device__ __forceinline__ void op_store(const OpRegs<ROWS, LAY>& R, uint8_t* lds) {
-    const int tid = threadIdx.x;
-    if (LAY == KMAJ) {
+    __device__ __forceinline__ void store(uint8_t* lds) const {
+        const int tid = threadIdx.x;
+        if (LAY == KMAJ) {
 #pragma unroll
-        for (int i = 0; i < R.NREG; ++i) {
-            const int q = tid + 256 * i;
-            const int row = q >> 3, c = q & 7;
-            *reinterpret_cast<uint4*>(lds + swz(row, c)) = R.r[i];
-        }
-    } else {
-        constexpr int NB = ROWS / 8;
-        const int cb = tid % NB, kb = tid / NB;
-        if (tid >= ROWS) return;
-        // in[i] = 8 columns at reduction index kb*8+i; out[c] = 8 k values of column c
-        uint32_t w[8][4];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            w[i][0] = R.r[i].x; w[i][1] = R.r[i].y; w[i][2] = R.r[i].z; w[i][3] = R.r[i].w;
-        }
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const int wd = c >> 1;
-            uint4 o;
-            if ((c & 1) == 0) {
-                o.x = lo_pair(w[0][wd], w[1][wd]);
-                o.y = lo_pair(w[2][wd], w[3][wd]);
-                o.z = lo_pair(w[4][wd], w[5][wd]);
-                o.w = lo_pair(w[6][wd], w[7][wd]);
-            } else {
-                o.x = hi_pair(w[0][wd], w[1][wd]);
-                o.y = hi_pair(w[2][wd], w[3][wd]);
-                o.z = hi_pair(w[4][wd], w[5][wd]);
-                o.w = hi_pair(w[6][wd], w[7][wd]);
+            for (int i = 0; i < NREG; ++i) {
+                const int row = (tid >> 3) + 32 * i, c = tid & 7;
+                *reinterpret_cast<uint4*>(lds + swz(row, c)) = r[i];
             }
-            *reinterpret_cast<uint4*>(lds + swz(cb * 8 + c, kb)) = o;
+        } else {
+            if (tid >= ROWS) return;
+            const int cb = tid % NB, kb = tid / NB;
+            // r[i] = 8 columns at reduction index kb*8+i; write 8 k values per column
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const int wd = c >> 1;
+                auto word = [&](int i) -> uint32_t {
+                    const uint4& v = r[i];
+                    return wd == 0 ? v.x : wd == 1 ? v.y : wd == 2 ? v.z : v.w;
+                };
+                uint4 o;
+                if ((c & 1) == 0) {
+                    o.x = (word(0) & 0xffffu) | (word(1) << 16);
+                    o.y = (word(2) & 0xffffu) | (word(3) << 16);
+                    o.z = (word(4) & 0xffffu) | (word(5) << 16);
+                    o.w = (word(6) & 0xffffu) | (word(7) << 16);
+                } else {
+                    o.x = (word(0) >> 16) | (word(1) & 0xffff0000u);
+                    o.y = (word(2) >> 16) | (word(3) & 0xffff0000u);
+                    o.z = (word(4) >> 16) | (word(5) & 0xffff0000u);
+                    o.w = (word(6) >> 16) | (word(7) & 0xffff0000u);
+                }
+                *reinterpret_cast<uint4*>(lds + swz(cb * 8 + c, kb)) = o;
+            }
         }
     }
-}
+};
 
 __device__ __forceinline__ bf16x8 lds_frag(const uint8_t* lds, int row, int chunk) {
     const uint4 v = *reinterpret_cast<const uint4*>(lds + swz(row, chunk));
@@ -298,35 +350,21 @@ __global__ __launch_bounds__(256, 1) void ggemm_bf16_kernel(GemmArgs<bf16_t> p, 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int wm = wv / WN, wn = wv % WN;
 
-    // operand base pointers (first row/column of the tile)
-    const bf16_t* Ap;
-    int a_lim;
-    long a_klim;
+    Operand<BM, ALAY> opA;
+    Operand<BN, BLAY> opB;
+    Operand<BN, BLAY> opB2;    // DUAL: the W3 tile
+    const bf16_t* bsplit[2];   // KSPLIT: B below / above the split of the reduction
     if (MODE == RAGGED_M) {
-        Ap = p.A + ti.r0 * p.lda;           // KMAJ rows of the segment
-        a_lim = ti.rows;
-        a_klim = p.K;
-    } else {
-        Ap = p.A + ti.kbeg * p.lda + ti.m0; // MNMAJ: row k of the segment, column m
-        a_lim = p.M - ti.m0;
-        a_klim = ti.klen;
-    }
-    const bf16_t* Bp;
-    const bf16_t* B2p = nullptr;
-    int b_lim = p.N - ti.n0;
-    if (MODE == RAGGED_M) {
+        opA.init(p.A + ti.r0 * p.lda, p.lda, ti.rows, p.K);
         const long eoff = (long)ti.e * p.bstride;
-        if (BLAY == KMAJ) {
-            Bp = p.B + eoff + (long)ti.n0 * p.ldb;
-            if (KSPLIT) B2p = p.B2 + eoff + (long)ti.n0 * p.ldb;
-        } else {
-            Bp = p.B + eoff + ti.n0;
-            if (DUAL) B2p = p.B2 + eoff + ti.n0;
-        }
+        const long nofs = BLAY == KMAJ ? (long)ti.n0 * p.ldb : (long)ti.n0;
+        opB.init(p.B + eoff + nofs, p.ldb, p.N - ti.n0, p.K);
+        if (DUAL) opB2.init(p.B2 + eoff + nofs, p.ldb, p.N - ti.n0, p.K);
+        if (KSPLIT) bsplit[0] = opB.P, bsplit[1] = p.B2 + eoff + nofs;
     } else {
-        Bp = p.B + ti.kbeg * p.ldb + ti.n0;
+        opA.init(p.A + ti.kbeg * p.lda + ti.m0, p.lda, p.M - ti.m0, ti.klen);
+        opB.init(p.B + ti.kbeg * p.ldb + ti.n0, p.ldb, p.N - ti.n0, ti.klen);
     }
-    const long b_klim = MODE == RAGGED_M ? (long)p.K : (long)ti.klen;
 
     f32x16 acc[FM][FN];
     f32x16 acc2[DUAL ? FM : 1][DUAL ? FN : 1];
@@ -336,38 +374,33 @@ __global__ __launch_bounds__(256, 1) void ggemm_bf16_kernel(GemmArgs<bf16_t> p, 
         for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-    if (DUAL) {
+    if constexpr (DUAL) {
 #pragma unroll
-        for (int i = 0; i < (DUAL ? FM : 1); ++i)
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int j = 0; j < (DUAL ? FN : 1); ++j)
+            for (int j = 0; j < FN; ++j)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc2[i][j][v] = 0.0f;
     }
 
     const int nk = (ti.klen + BK - 1) / BK;
-    OpRegs<BM, ALAY> ra;
-    OpRegs<BN, BLAY> rb;
-    OpRegs<BN, BLAY> rb2;
-
     auto load_stage = [&](int kt) {
         const long k0 = (long)kt * BK;
-        op_load<BM, ALAY>(ra, Ap, p.lda, a_lim, k0, a_klim);
-        if (KSPLIT) {
-            if (k0 >= p.Ksplit)
-                op_load<BN, BLAY>(rb, B2p, p.ldb, b_lim, k0 - p.Ksplit, b_klim);
-            else
-                op_load<BN, BLAY>(rb, Bp, p.ldb, b_lim, k0, b_klim);
+        opA.load(k0);
+        if constexpr (KSPLIT) {
+            const bool hi = k0 >= p.Ksplit;
+            opB.P = bsplit[hi];
+            opB.load(hi ? k0 - p.Ksplit : k0);
         } else {
-            op_load<BN, BLAY>(rb, Bp, p.ldb, b_lim, k0, b_klim);
+            opB.load(k0);
         }
-        if (DUAL) op_load<BN, BLAY>(rb2, B2p, p.ldb, b_lim, k0, b_klim);
+        if constexpr (DUAL) opB2.load(k0);
     };
     auto store_stage = [&](int buf) {
-        uint8_t* s = smem + buf * STAGE;
-        op_store<BM, ALAY>(ra, s);
-        op_store<BN, BLAY>(rb, s + A_BYTES);
-        if (DUAL) op_store<BN, BLAY>(rb2, s + A_BYTES + B_BYTES);
+        uint8_t* sm = smem + buf * STAGE;
+        opA.store(sm);
+        opB.store(sm + A_BYTES);
+        if constexpr (DUAL) opB2.store(sm + A_BYTES + B_BYTES);
     };
 
     if (nk > 0) {
@@ -397,14 +430,14 @@ __global__ __launch_bounds__(256, 1) void ggemm_bf16_kernel(GemmArgs<bf16_t> p, 
                 for (int j = 0; j < FN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j],
                                                                        acc[i][j], 0, 0, 0);
-            if (DUAL) {
+            if constexpr (DUAL) {
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
                     bfr[j] = lds_frag(sB2, wn * WTN + j * 32 + (lane & 31), chunk);
 #pragma unroll
-                for (int i = 0; i < (DUAL ? FM : 1); ++i)
+                for (int i = 0; i < FM; ++i)
 #pragma unroll
-                    for (int j = 0; j < (DUAL ? FN : 1); ++j)
+                    for (int j = 0; j < FN; ++j)
                         acc2[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                             af[i], bfr[j], acc2[i][j], 0, 0, 0);
             }
@@ -413,28 +446,52 @@ __global__ __launch_bounds__(256, 1) void ggemm_bf16_kernel(GemmArgs<bf16_t> p, 
         __syncthreads();
     }
 
-    // epilogue: lane holds column (lane & 31) and rows (v/4)*8 + (lane/32)*4 + v%4
+    // ---- epilogue through LDS: one 32-row slab of the wave tile at a time,
+    // then every lane owns 8 consecutive columns of a row (16-byte stores).
+    // acc layout: lane holds column (lane & 31), rows (v/4)*8 + (lane/32)*4 + v%4.
+    constexpr int LDW = WTN + 4;                     // padded fp32 row
+    constexpr int SLAB = 32 * LDW;                   // floats per wave slab
+    float* slab = reinterpret_cast<float*>(smem) + wv * SLAB * NBT;
+    constexpr int LPR = WTN / 8;                     // lanes per row
+    constexpr int RPP = 64 / LPR;                    // rows per pass
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int col = ti.n0 + wn * WTN + j * 32 + (lane & 31);
-            if (col >= p.N) continue;
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int rl = wm * WTM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-                if (MODE == RAGGED_M) {
-                    if (rl >= ti.rows) continue;
-                    if constexpr (DUAL)
-                        epi(ti.e, ti.r0 + rl, col, acc[i][j][v], acc2[i][j][v]);
-                    else
-                        epi(ti.e, ti.r0 + rl, col, acc[i][j][v]);
+                const int r = (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+                slab[r * LDW + j * 32 + (lane & 31)] = acc[i][j][v];
+                if constexpr (DUAL) slab[SLAB + r * LDW + j * 32 + (lane & 31)] = acc2[i][j][v];
+            }
+        __syncthreads();
+#pragma unroll 1
+        for (int ps = 0; ps < 32 / RPP; ++ps) {
+            const int r = ps * RPP + lane / LPR;
+            const int c0 = (lane % LPR) * 8;
+            const int rl = wm * WTM + i * 32 + r;
+            const int col = ti.n0 + wn * WTN + c0;
+            float v[8];
+            *reinterpret_cast<float4*>(v) = *reinterpret_cast<const float4*>(&slab[r * LDW + c0]);
+            *reinterpret_cast<float4*>(v + 4) =
+                *reinterpret_cast<const float4*>(&slab[r * LDW + c0 + 4]);
+            const bool ok = col < p.N && (MODE == RAGGED_M ? rl < ti.rows : ti.m0 + rl < p.M);
+            if (ok) {
+                if constexpr (DUAL) {
+                    float v3[8];
+                    *reinterpret_cast<float4*>(v3) =
+                        *reinterpret_cast<const float4*>(&slab[SLAB + r * LDW + c0]);
+                    *reinterpret_cast<float4*>(v3 + 4) =
+                        *reinterpret_cast<const float4*>(&slab[SLAB + r * LDW + c0 + 4]);
+                    epi.vec8(ti.e, ti.r0 + rl, col, v, v3);
+                } else if (MODE == RAGGED_M) {
+                    epi.vec8(ti.e, ti.r0 + rl, col, v);
                 } else {
-                    if (ti.m0 + rl >= p.M) continue;
-                    if constexpr (!DUAL) epi(ti.e, (long)ti.m0 + rl, col, acc[i][j][v]);
+                    epi.vec8(ti.e, (long)ti.m0 + rl, col, v);
                 }
             }
         }
+        __syncthreads();
     }
 }
 
@@ -590,7 +647,7 @@ FfnWs ffn_layout(int R, int E, int f, moe_act act, moe_dtype dt, int backward) {
 }
 
 template <int BM, int BN, int MODE, int ALAY, int BLAY, bool DUAL, bool KSPLIT, class Epi>
-void launch_bf16(GemmArgs<bf16_t> p, Epi epi, int R, hipStream_t s) {
+void launch_bf16(GemmArgs<bf16_t> p, Epi epi, int R, hipStream_t s, const char* name) {
     p.nN = (p.N + BN - 1) / BN;
     int blocks;
     if (MODE == RAGGED_M) {
@@ -600,11 +657,12 @@ void launch_bf16(GemmArgs<bf16_t> p, Epi epi, int R, hipStream_t s) {
         blocks = p.E * p.nM * p.nN;
     }
     if (blocks <= 0) return;
-    ggemm_bf16_kernel<BM, BN, MODE, ALAY, BLAY, DUAL, KSPLIT, Epi><<<blocks, 256, 0, s>>>(p, epi);
+    MOE_LAUNCH(name, s,
+               ggemm_bf16_kernel<BM, BN, MODE, ALAY, BLAY, DUAL, KSPLIT, Epi><<<blocks, 256, 0, s>>>(p, epi));
 }
 
 template <int MODE, int ALAY, int BLAY, bool DUAL, bool KSPLIT, class Epi>
-void launch_f32(GemmArgs<float> p, Epi epi, int R, hipStream_t s) {
+void launch_f32(GemmArgs<float> p, Epi epi, int R, hipStream_t s, const char* name) {
     p.nN = (p.N + FB - 1) / FB;
     int blocks;
     if (MODE == RAGGED_M) {
@@ -614,7 +672,7 @@ void launch_f32(GemmArgs<float> p, Epi epi, int R, hipStream_t s) {
         blocks = p.E * p.nM * p.nN;
     }
     if (blocks <= 0) return;
-    ggemm_f32_kernel<MODE, ALAY, BLAY, DUAL, KSPLIT, Epi><<<blocks, 256, 0, s>>>(p, epi);
+    MOE_LAUNCH(name, s, ggemm_f32_kernel<MODE, ALAY, BLAY, DUAL, KSPLIT, Epi><<<blocks, 256, 0, s>>>(p, epi));
 }
 
 template <typename T>
@@ -634,11 +692,11 @@ struct Launch;
 template <>
 struct Launch<bf16_t> {
     template <int MODE, int ALAY, int BLAY, bool DUAL, bool KSPLIT, class Epi>
-    static void go(GemmArgs<bf16_t> p, Epi epi, int R, hipStream_t s) {
+    static void go(GemmArgs<bf16_t> p, Epi epi, int R, hipStream_t s, const char* name) {
         if constexpr (DUAL)
-            launch_bf16<BM_BF16, 128, MODE, ALAY, BLAY, DUAL, KSPLIT>(p, epi, R, s);
+            launch_bf16<BM_BF16, 128, MODE, ALAY, BLAY, DUAL, KSPLIT>(p, epi, R, s, name);
         else
-            launch_bf16<BM_BF16, 256, MODE, ALAY, BLAY, DUAL, KSPLIT>(p, epi, R, s);
+            launch_bf16<BM_BF16, 256, MODE, ALAY, BLAY, DUAL, KSPLIT>(p, epi, R, s, name);
     }
     static constexpr int BM = BM_BF16;
 };
@@ -646,8 +704,8 @@ struct Launch<bf16_t> {
 template <>
 struct Launch<float> {
     template <int MODE, int ALAY, int BLAY, bool DUAL, bool KSPLIT, class Epi>
-    static void go(GemmArgs<float> p, Epi epi, int R, hipStream_t s) {
-        launch_f32<MODE, ALAY, BLAY, DUAL, KSPLIT>(p, epi, R, s);
+    static void go(GemmArgs<float> p, Epi epi, int R, hipStream_t s, const char* name) {
+        launch_f32<MODE, ALAY, BLAY, DUAL, KSPLIT>(p, epi, R, s, name);
     }
     static constexpr int BM = FB;
 };
@@ -661,7 +719,8 @@ moe_status ffn_fwd(const void* x_perm, const int32_t* offsets, int R, int E,
     char* base = static_cast<char*>(ws);
     int32_t* prefix = reinterpret_cast<int32_t*>(base + L.prefix);
     int32_t* order = reinterpret_cast<int32_t*>(base + L.order);
-    ffn_plan_kernel<<<1, 1024, 0, s>>>(offsets, E, Launch<T>::BM, prefix, order);
+    MOE_LAUNCH("ffn_plan", s,
+               ffn_plan_kernel<<<1, 1024, 0, s>>>(offsets, E, Launch<T>::BM, prefix, order));
 
     const T* xp = static_cast<const T*>(x_perm);
     T* H = static_cast<T*>(h_save);
@@ -673,11 +732,11 @@ moe_status ffn_fwd(const void* x_perm, const int32_t* offsets, int R, int E,
     p.N = f; p.K = d;
     if (act == MOE_ACT_GELU) {
         Launch<T>::template go<RAGGED_M, KMAJ, MNMAJ, false, false>(
-            p, EpiGeluFwd<T>{H, A, f}, R, s);
+            p, EpiGeluFwd<T>{H, A, f}, R, s, "gemm_up_gelu");
     } else {
         p.B2 = static_cast<const T*>(W3);
         Launch<T>::template go<RAGGED_M, KMAJ, MNMAJ, true, false>(
-            p, EpiSwigluFwd<T>{H, A, f}, R, s);
+            p, EpiSwigluFwd<T>{H, A, f}, R, s, "gemm_up_swiglu");
     }
     // GEMM2: A [R,f] x W2[e] [f,d]
     GemmArgs<T> q = base_args<T>(offsets, prefix, order, E);
@@ -685,7 +744,7 @@ moe_status ffn_fwd(const void* x_perm, const int32_t* offsets, int R, int E,
     q.B = static_cast<const T*>(W2); q.ldb = d; q.bstride = (long)f * d;
     q.N = d; q.K = f;
     Launch<T>::template go<RAGGED_M, KMAJ, MNMAJ, false, false>(
-        q, EpiStore<T>{static_cast<T*>(out_perm), d, 0}, R, s);
+        q, EpiStore<T>{static_cast<T*>(out_perm), d, 0}, R, s, "gemm_down");
     return launch_status();
 }
 
@@ -702,7 +761,8 @@ moe_status ffn_bwd(const void* d_out, const void* x_perm, const void* h_save,
     T* dH = reinterpret_cast<T*>(base + L.dh);
     const bool sw = act == MOE_ACT_SWIGLU;
     const long ldh = sw ? 2L * f : (long)f;
-    ffn_plan_kernel<<<1, 1024, 0, s>>>(offsets, E, Launch<T>::BM, prefix, order);
+    MOE_LAUNCH("ffn_plan", s,
+               ffn_plan_kernel<<<1, 1024, 0, s>>>(offsets, E, Launch<T>::BM, prefix, order));
 
     const T* dO = static_cast<const T*>(d_out);
     // dA = dO W2[e]^T with the activation derivative in the epilogue -> dH
@@ -713,10 +773,10 @@ moe_status ffn_bwd(const void* d_out, const void* x_perm, const void* h_save,
         p.N = f; p.K = d;
         if (!sw)
             Launch<T>::template go<RAGGED_M, KMAJ, KMAJ, false, false>(
-                p, EpiGeluBwd<T>{static_cast<const T*>(h_save), dH, f}, R, s);
+                p, EpiGeluBwd<T>{static_cast<const T*>(h_save), dH, f}, R, s, "gemm_dA_gelu");
         else
             Launch<T>::template go<RAGGED_M, KMAJ, KMAJ, false, false>(
-                p, EpiSwigluBwd<T>{static_cast<const T*>(h_save), dH, f}, R, s);
+                p, EpiSwigluBwd<T>{static_cast<const T*>(h_save), dH, f}, R, s, "gemm_dA_swiglu");
     }
     // dW2[e] = A_e^T dO_e   [f, d]
     {
@@ -724,7 +784,7 @@ moe_status ffn_bwd(const void* d_out, const void* x_perm, const void* h_save,
         p.A = static_cast<const T*>(a_save); p.lda = f; p.M = f;
         p.B = dO; p.ldb = d; p.N = d;
         Launch<T>::template go<RAGGED_K, MNMAJ, MNMAJ, false, false>(
-            p, EpiStore<T>{static_cast<T*>(dW2), d, (long)f * d}, R, s);
+            p, EpiStore<T>{static_cast<T*>(dW2), d, (long)f * d}, R, s, "gemm_dW2");
     }
     // dW1[e] = X_e^T dH1_e  [d, f]   (dW3 with dH3)
     {
@@ -732,11 +792,11 @@ moe_status ffn_bwd(const void* d_out, const void* x_perm, const void* h_save,
         p.A = static_cast<const T*>(x_perm); p.lda = d; p.M = d;
         p.B = dH; p.ldb = ldh; p.N = f;
         Launch<T>::template go<RAGGED_K, MNMAJ, MNMAJ, false, false>(
-            p, EpiStore<T>{static_cast<T*>(dW1), f, (long)d * f}, R, s);
+            p, EpiStore<T>{static_cast<T*>(dW1), f, (long)d * f}, R, s, "gemm_dW1");
         if (sw) {
             p.B = dH + f;
             Launch<T>::template go<RAGGED_K, MNMAJ, MNMAJ, false, false>(
-                p, EpiStore<T>{static_cast<T*>(dW3), f, (long)d * f}, R, s);
+                p, EpiStore<T>{static_cast<T*>(dW3), f, (long)d * f}, R, s, "gemm_dW3");
         }
     }
     // dX = dH1 W1[e]^T (+ dH3 W3[e]^T)   [R, d]
@@ -748,12 +808,12 @@ moe_status ffn_bwd(const void* d_out, const void* x_perm, const void* h_save,
         EpiStore<T> st{static_cast<T*>(dx_perm), d, 0};
         if (!sw) {
             p.K = f;
-            Launch<T>::template go<RAGGED_M, KMAJ, KMAJ, false, false>(p, st, R, s);
+            Launch<T>::template go<RAGGED_M, KMAJ, KMAJ, false, false>(p, st, R, s, "gemm_dX");
         } else {
             p.K = 2 * f;
             p.Ksplit = f;
             p.B2 = static_cast<const T*>(W3);
-            Launch<T>::template go<RAGGED_M, KMAJ, KMAJ, false, true>(p, st, R, s);
+            Launch<T>::template go<RAGGED_M, KMAJ, KMAJ, false, true>(p, st, R, s, "gemm_dX");
         }
     }
     return launch_status();

@@ -246,22 +246,29 @@ moe_status moe_permute(const int32_t* topk_idx, const void* x, int T, int d,
     if (T == 0) {
         // empty input: counts = 0, offsets = 0 (a tiny scatter launch with no
         // blocks would do nothing, so write them with the scan kernel form)
-        perm_scan_kernel<<<E, 256, 0, stream>>>(bcounts, 0, bbase, counts);
-        perm_scatter_kernel<<<1, 256, sizeof(int) * (5 * (size_t)E + 1), stream>>>(
-            topk_idx, counts, bbase, 0, E, k, tpb, 1, nbits, offsets, dest, src);
+        MOE_LAUNCH("perm_scan", stream,
+            perm_scan_kernel<<<E, 256, 0, stream>>>(bcounts, 0, bbase, counts));
+        MOE_LAUNCH("perm_scatter", stream,
+            perm_scatter_kernel<<<1, 256, sizeof(int) * (5 * (size_t)E + 1), stream>>>(
+                topk_idx, counts, bbase, 0, E, k, tpb, 1, nbits, offsets, dest, src));
         return launch_status();
     }
-    perm_hist_kernel<<<nblk, 256, sizeof(int) * (size_t)E, stream>>>(
-        topk_idx, T, E, k, tpb, nblk, bcounts);
-    perm_scan_kernel<<<E, 256, 0, stream>>>(bcounts, nblk, bbase, counts);
-    perm_scatter_kernel<<<nblk, 256, sizeof(int) * (5 * (size_t)E + 1), stream>>>(
-        topk_idx, counts, bbase, T, E, k, tpb, nblk, nbits, offsets, dest, src);
+    MOE_LAUNCH("perm_hist", stream,
+        perm_hist_kernel<<<nblk, 256, sizeof(int) * (size_t)E, stream>>>(
+            topk_idx, T, E, k, tpb, nblk, bcounts));
+    MOE_LAUNCH("perm_scan", stream,
+        perm_scan_kernel<<<E, 256, 0, stream>>>(bcounts, nblk, bbase, counts));
+    MOE_LAUNCH("perm_scatter", stream,
+        perm_scatter_kernel<<<nblk, 256, sizeof(int) * (5 * (size_t)E + 1), stream>>>(
+            topk_idx, counts, bbase, T, E, k, tpb, nblk, nbits, offsets, dest, src));
     if (dt == MOE_BF16)
-        perm_copy_kernel<bf16_t><<<cdiv(T, 4), 256, 0, stream>>>(
-            static_cast<const bf16_t*>(x), dest, T, d, k, static_cast<bf16_t*>(x_perm));
+        MOE_LAUNCH("perm_copy", stream,
+            perm_copy_kernel<bf16_t><<<cdiv(T, 4), 256, 0, stream>>>(
+                static_cast<const bf16_t*>(x), dest, T, d, k, static_cast<bf16_t*>(x_perm)));
     else
-        perm_copy_kernel<float><<<cdiv(T, 4), 256, 0, stream>>>(
-            static_cast<const float*>(x), dest, T, d, k, static_cast<float*>(x_perm));
+        MOE_LAUNCH("perm_copy", stream,
+            perm_copy_kernel<float><<<cdiv(T, 4), 256, 0, stream>>>(
+                static_cast<const float*>(x), dest, T, d, k, static_cast<float*>(x_perm)));
     return launch_status();
 }
 
