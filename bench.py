@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU work for the oracle baseline")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="run one plain device copy of this many MiB before the "
+                         "steps (a known-size reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -118,6 +121,14 @@ def main():
     layer.bind(t["x"], t["Wg"], t["W1"], t["W2"], t["W3"], t["bias"], t["dy"])
     stream = torch.cuda.current_stream()
     s = stream.cuda_stream
+    if args.calib_copy_mb:
+        n = args.calib_copy_mb << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         layer.step(s)

@@ -174,15 +174,34 @@ struct TileInfo {
     bool live;
 };
 
-template <int MODE, int BM, int BN, typename T>
+// Block -> tile.  Workgroups are dealt to the 8 XCDs round-robin (block b
+// runs on XCD b % 8), and each XCD has its own L2.  The flat block index is
+// therefore re-mapped so that each XCD receives runs of XCD_RUN consecutive
+// logical tiles, and logical tiles are ordered so that a run shares
+// operands: RAGGED_M in groups of GROUP_M row tiles (all N tiles of the
+// group before the next group), RAGGED_K expert by expert, row tiles
+// fastest.  Grids are padded to a multiple of 8 * XCD_RUN.
+constexpr int NXCD = 8;
+constexpr int GROUP_M = 8;
+
+__device__ __forceinline__ int xcd_logical(int b, int run) {
+    const int x = b % NXCD, j = b / NXCD;
+    return ((j / run) * NXCD + x) * run + (j % run);
+}
+
+template <int MODE, int BM, int BN, int XCD_RUN, typename T>
 __device__ __forceinline__ TileInfo decode_tile(const GemmArgs<T>& p) {
     TileInfo ti;
-    const int id = blockIdx.x;
+    const int L = xcd_logical(blockIdx.x, XCD_RUN);
     if (MODE == RAGGED_M) {
-        const int mt = id / p.nN, nt = id % p.nN;
-        const int total = p.tile_prefix[p.E];
-        ti.live = mt < total;
+        const int total = p.tile_prefix[p.E];          // row tiles over all experts
+        ti.live = L < total * p.nN;
         if (!ti.live) return ti;
+        const int per_group = GROUP_M * p.nN;
+        const int first = (L / per_group) * GROUP_M;
+        const int gm = min(GROUP_M, total - first);
+        const int w = L % per_group;
+        const int mt = first + w % gm, nt = w / gm;
         int lo = 0, hi = p.E;                 // largest e with prefix[e] <= mt
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
@@ -198,12 +217,12 @@ __device__ __forceinline__ TileInfo decode_tile(const GemmArgs<T>& p) {
         ti.klen = p.K;
     } else {
         const int per = p.nM * p.nN;
-        const int es = id / per, rem = id % per;
+        const int es = L / per, rem = L % per;
         ti.live = es < p.E;
         if (!ti.live) return ti;
         ti.e = p.order ? p.order[es] : es;
-        ti.m0 = (rem / p.nN) * BM;
-        ti.n0 = (rem % p.nN) * BN;
+        ti.m0 = (rem % p.nM) * BM;
+        ti.n0 = (rem / p.nM) * BN;
         ti.kbeg = p.offsets[ti.e];
         ti.klen = p.offsets[ti.e + 1] - p.offsets[ti.e];
         ti.r0 = 0;
@@ -244,19 +263,36 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 }
 
 // One operand tile (ROWS x 64 along M or N by K) in flight between its
-// global load and its LDS store.
-//  KMAJ : elem(row, k) = P[row * ld + k],  rows < row_lim valid
-//  MNMAJ: elem(row, k) = P[k * ld + row],  rows < row_lim, k < k_lim valid
+// global load and its LDS store, spread over NT threads, 16 bytes a piece.
+//  KMAJ : elem(row, k) = P[row * ld + k],  rows < row_lim valid.  LDS holds
+//         K-contiguous rows of 64 (128 B), 16-byte chunks XOR-swizzled;
+//         MFMA fragments are plain 16-byte reads.
+//  MNMAJ: elem(row, k) = P[k * ld + row],  rows < row_lim, k < k_lim valid.
+//         LDS holds the tile as it lies in memory, 64 rows of ROWS elements
+//         (row pitch padded by 64 B); MFMA fragments come from two gfx950
+//         transposing reads (ds_read_b64_tr_b16) each.
 // P points at the tile origin (first row / first column, k = 0).
+template <int ROWS>
+struct MnLayout {
+    static constexpr int PITCH = ROWS * 2 + 64;        // bytes per k row
+    static constexpr int BYTES = 64 * PITCH;
+};
+
 template <int ROWS, int LAY>
+constexpr int op_lds_bytes() {
+    return LAY == KMAJ ? ROWS * BK * 2 : MnLayout<ROWS>::BYTES;
+}
+
+template <int ROWS, int LAY, int NT>
 struct Operand {
-    static constexpr int NB = ROWS / 8;                      // MNMAJ column groups
-    static constexpr int NREG = LAY == KMAJ ? ROWS * 8 / 256 : 8;
+    static constexpr int NB = ROWS / 8;                        // 16 B pieces per k row
+    static constexpr int NREG = ROWS * 8 / NT;                 // pieces per thread
+    static_assert(ROWS * 8 % NT == 0 && NT % NB == 0, "tile/thread mismatch");
     const bf16_t* P;
     long ld;
     int row_lim;
     long k_lim;
-    uint32_t off0;     // lane offset (bytes) of its first 16-byte piece
+    uint32_t off0;     // lane offset (bytes) of its first piece
     uint4 r[NREG];
 
     __device__ __forceinline__ void init(const bf16_t* P_, long ld_, int row_lim_,
@@ -269,24 +305,24 @@ struct Operand {
         if (LAY == KMAJ) {
             off0 = (uint32_t)((tid >> 3) * ld * 2 + (tid & 7) * 16);
         } else {
-            const int cb = tid % NB, kb = tid / NB;
-            const bool ok = tid < ROWS && cb * 8 < row_lim;
-            off0 = ok ? (uint32_t)(kb * 8 * ld * 2 + cb * 16) : OOB;
+            const int cb = tid % NB, k = tid / NB;
+            off0 = cb * 8 < row_lim ? (uint32_t)(k * ld * 2 + cb * 16) : OOB;
         }
     }
 
     __device__ __forceinline__ void load(long k0) {
         if (LAY == KMAJ) {
-            const __amdgpu_buffer_rsrc_t rs = make_rsrc(P + k0, (long)row_lim * ld * 2 - k0 * 2);
-            const uint32_t step = (uint32_t)(32 * ld * 2);
+            const __amdgpu_buffer_rsrc_t rs =
+                make_rsrc(P + k0, (long)row_lim * ld * 2 - k0 * 2);
+            const uint32_t step = (uint32_t)((NT / 8) * ld * 2);
 #pragma unroll
             for (int i = 0; i < NREG; ++i) r[i] = bload16(rs, off0 + i * step);
         } else {
             const long kv = min((long)BK, k_lim - k0);
             const __amdgpu_buffer_rsrc_t rs = make_rsrc(P + k0 * ld, kv * ld * 2);
-            const uint32_t step = (uint32_t)(ld * 2);
+            const uint32_t step = (uint32_t)((NT / NB) * ld * 2);
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < NREG; ++i)
                 r[i] = bload16(rs, off0 == OOB ? OOB : off0 + i * step);
         }
     }
@@ -296,64 +332,83 @@ struct Operand {
         if (LAY == KMAJ) {
 #pragma unroll
             for (int i = 0; i < NREG; ++i) {
-                const int row = (tid >> 3) + 32 * i, c = tid & 7;
+                const int row = (tid >> 3) + (NT / 8) * i, c = tid & 7;
                 *reinterpret_cast<uint4*>(lds + swz(row, c)) = r[i];
             }
         } else {
-            if (tid >= ROWS) return;
-            const int cb = tid % NB, kb = tid / NB;
-            // r[i] = 8 columns at reduction index kb*8+i; write 8 k values per column
+            const int cb = tid % NB, k = tid / NB;
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const int wd = c >> 1;
-                auto word = [&](int i) -> uint32_t {
-                    const uint4& v = r[i];
-                    return wd == 0 ? v.x : wd == 1 ? v.y : wd == 2 ? v.z : v.w;
-                };
-                uint4 o;
-                if ((c & 1) == 0) {
-                    o.x = (word(0) & 0xffffu) | (word(1) << 16);
-                    o.y = (word(2) & 0xffffu) | (word(3) << 16);
-                    o.z = (word(4) & 0xffffu) | (word(5) << 16);
-                    o.w = (word(6) & 0xffffu) | (word(7) << 16);
-                } else {
-                    o.x = (word(0) >> 16) | (word(1) & 0xffff0000u);
-                    o.y = (word(2) >> 16) | (word(3) & 0xffff0000u);
-                    o.z = (word(4) >> 16) | (word(5) & 0xffff0000u);
-                    o.w = (word(6) >> 16) | (word(7) & 0xffff0000u);
-                }
-                *reinterpret_cast<uint4*>(lds + swz(cb * 8 + c, kb)) = o;
-            }
+            for (int i = 0; i < NREG; ++i)
+                *reinterpret_cast<uint4*>(lds + (k + (NT / NB) * i) * MnLayout<ROWS>::PITCH +
+                                          cb * 16) = r[i];
         }
     }
 };
 
+// Fragment of a 32x32x16 MFMA operand for the wave's 32-row (or -column)
+// block starting at `row0`, reduction step ks: lane l holds rows
+// row0 + (l & 31), reduction indices ks*16 + (l >> 5)*8 + 0..7.
 __device__ __forceinline__ bf16x8 lds_frag(const uint8_t* lds, int row, int chunk) {
     const uint4 v = *reinterpret_cast<const uint4*>(lds + swz(row, chunk));
     return __builtin_bit_cast(bf16x8, v);
 }
 
-template <int BM, int BN, int MODE, int ALAY, int BLAY, bool DUAL, bool KSPLIT,
-          class Epi>
-__global__ __launch_bounds__(256, 1) void ggemm_bf16_kernel(GemmArgs<bf16_t> p, Epi epi) {
-    constexpr int WM = 2, WN = 2;
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+// The same fragment from an MN-major tile.  ds_read_b64_tr_b16 over a group
+// of 16 lanes: lane i receives element (i % 4) of the 8-byte pieces addressed
+// by lanes i/4 + 4q, q = 0..3.  Lane j of the group therefore points at
+// reduction row (base + j/4) and columns (col0 + 4*(j % 4)), which hands lane
+// i the four consecutive reduction indices of column col0 + i.
+template <int ROWS>
+__device__ __forceinline__ bf16x8 lds_frag_tr(const uint8_t* lds, int row0, int ks,
+                                              int lane) {
+    constexpr int PITCH = MnLayout<ROWS>::PITCH;
+    const int kr = ks * 16 + (lane >> 5) * 8 + ((lane & 15) >> 2);
+    const int col = row0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const uint8_t* p0 = lds + kr * PITCH + col * 2;
+    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16_t*)(p0));
+    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16_t*)(p0 + 4 * PITCH));
+    typedef short v8i16_t __attribute__((ext_vector_type(8)));
+    const v8i16_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+template <int ROWS, int LAY>
+__device__ __forceinline__ bf16x8 op_frag(const uint8_t* lds, int row0, int ks, int lane) {
+    if constexpr (LAY == KMAJ)
+        return lds_frag(lds, row0 + (lane & 31), ks * 2 + (lane >> 5));
+    else
+        return lds_frag_tr<ROWS>(lds, row0, ks, lane);
+}
+
+// Block tile BM x BN x 64, WM x WN waves (64 threads each), wave tile
+// (BM/WM) x (BN/WN) of 32x32 MFMA tiles.
+template <int BM, int BN, int WM, int WN, int MODE, int ALAY, int BLAY, bool DUAL,
+          bool KSPLIT, class Epi>
+__global__ __launch_bounds__(64 * WM * WN, 1) void ggemm_bf16_kernel(GemmArgs<bf16_t> p,
+                                                                     Epi epi) {
+    constexpr int NT = 64 * WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
     constexpr int NBT = DUAL ? 2 : 1;
-    constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+    constexpr int A_BYTES = op_lds_bytes<BM, ALAY>(), B_BYTES = op_lds_bytes<BN, BLAY>();
     constexpr int STAGE = A_BYTES + NBT * B_BYTES;
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
 
-    const TileInfo ti = decode_tile<MODE, BM, BN>(p);
+    const TileInfo ti = decode_tile<MODE, BM, BN, (MODE == RAGGED_M ? 32 : 8)>(p);
     if (!ti.live) return;
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int wm = wv / WN, wn = wv % WN;
 
-    Operand<BM, ALAY> opA;
-    Operand<BN, BLAY> opB;
-    Operand<BN, BLAY> opB2;    // DUAL: the W3 tile
-    const bf16_t* bsplit[2];   // KSPLIT: B below / above the split of the reduction
+    Operand<BM, ALAY, NT> opA;
+    Operand<BN, BLAY, NT> opB;
+    Operand<BN, BLAY, NT> opB2;    // DUAL: the W3 tile
+    const bf16_t* bsplit[2];       // KSPLIT: B below / above the split of the reduction
     if (MODE == RAGGED_M) {
         opA.init(p.A + ti.r0 * p.lda, p.lda, ti.rows, p.K);
         const long eoff = (long)ti.e * p.bstride;
@@ -384,6 +439,8 @@ __global__ __launch_bounds__(256, 1) void ggemm_bf16_kernel(GemmArgs<bf16_t> p, 
     }
 
     const int nk = (ti.klen + BK - 1) / BK;
+    // k-tile t+1 is fetched into registers while k-tile t is multiplied out
+    // of LDS stage (t & 1); it is written to the other stage afterwards.
     auto load_stage = [&](int kt) {
         const long k0 = (long)kt * BK;
         opA.load(k0);
@@ -414,84 +471,100 @@ __global__ __launch_bounds__(256, 1) void ggemm_bf16_kernel(GemmArgs<bf16_t> p, 
         const uint8_t* sA = smem + cur * STAGE;
         const uint8_t* sB = sA + A_BYTES;
         const uint8_t* sB2 = sB + B_BYTES;
-#pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            const int chunk = ks * 2 + (lane >> 5);
-            bf16x8 af[FM], bfr[FN];
+        // fragments of k-step ks+1 are read while the MFMAs of ks run
+        bf16x8 af[2][FM], bfr[2][FN], bf2[2][DUAL ? FN : 1];
+        auto read_frags = [&](int ks, int buf) {
 #pragma unroll
             for (int i = 0; i < FM; ++i)
-                af[i] = lds_frag(sA, wm * WTM + i * 32 + (lane & 31), chunk);
+                af[buf][i] = op_frag<BM, ALAY>(sA, wm * WTM + i * 32, ks, lane);
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                bfr[j] = lds_frag(sB, wn * WTN + j * 32 + (lane & 31), chunk);
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j],
-                                                                       acc[i][j], 0, 0, 0);
+                bfr[buf][j] = op_frag<BN, BLAY>(sB, wn * WTN + j * 32, ks, lane);
             if constexpr (DUAL) {
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    bfr[j] = lds_frag(sB2, wn * WTN + j * 32 + (lane & 31), chunk);
+                    bf2[buf][j] = op_frag<BN, BLAY>(sB2, wn * WTN + j * 32, ks, lane);
+            }
+        };
+        read_frags(0, 0);
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            const int cb = ks & 1;
+            if (ks + 1 < BK / 16) read_frags(ks + 1, cb ^ 1);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        af[cb][i], bfr[cb][j], acc[i][j], 0, 0, 0);
+            if constexpr (DUAL) {
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
                     for (int j = 0; j < FN; ++j)
                         acc2[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            af[i], bfr[j], acc2[i][j], 0, 0, 0);
+                            af[cb][i], bf2[cb][j], acc2[i][j], 0, 0, 0);
             }
         }
         if (kt + 1 < nk) store_stage(cur ^ 1);
         __syncthreads();
     }
 
-    // ---- epilogue through LDS: one 32-row slab of the wave tile at a time,
-    // then every lane owns 8 consecutive columns of a row (16-byte stores).
-    // acc layout: lane holds column (lane & 31), rows (v/4)*8 + (lane/32)*4 + v%4.
+    // ---- epilogue through LDS: one 16-row half of a 32-row slab of the wave
+    // tile at a time, then every lane owns 8 consecutive columns of a row
+    // (16-byte stores).  acc layout: lane holds column (lane & 31) and rows
+    // (v/4)*8 + (lane/32)*4 + v%4 of its 32x32 tile; registers v = 8h..8h+7
+    // cover rows 16h..16h+15.
     constexpr int LDW = WTN + 4;                     // padded fp32 row
-    constexpr int SLAB = 32 * LDW;                   // floats per wave slab
+    constexpr int SLAB = 16 * LDW;                   // floats per wave half-slab
     float* slab = reinterpret_cast<float*>(smem) + wv * SLAB * NBT;
     constexpr int LPR = WTN / 8;                     // lanes per row
     constexpr int RPP = 64 / LPR;                    // rows per pass
+    static_assert(NT / 64 * SLAB * NBT * 4 <= 2 * STAGE, "epilogue slab too big");
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+        for (int h = 0; h < 2; ++h) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int r = (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-                slab[r * LDW + j * 32 + (lane & 31)] = acc[i][j][v];
-                if constexpr (DUAL) slab[SLAB + r * LDW + j * 32 + (lane & 31)] = acc2[i][j][v];
-            }
-        __syncthreads();
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int vv = 0; vv < 8; ++vv) {
+                    const int v = h * 8 + vv;
+                    const int r = (vv >> 2) * 8 + (lane >> 5) * 4 + (vv & 3);
+                    slab[r * LDW + j * 32 + (lane & 31)] = acc[i][j][v];
+                    if constexpr (DUAL)
+                        slab[SLAB + r * LDW + j * 32 + (lane & 31)] = acc2[i][j][v];
+                }
+            __syncthreads();
 #pragma unroll 1
-        for (int ps = 0; ps < 32 / RPP; ++ps) {
-            const int r = ps * RPP + lane / LPR;
-            const int c0 = (lane % LPR) * 8;
-            const int rl = wm * WTM + i * 32 + r;
-            const int col = ti.n0 + wn * WTN + c0;
-            float v[8];
-            *reinterpret_cast<float4*>(v) = *reinterpret_cast<const float4*>(&slab[r * LDW + c0]);
-            *reinterpret_cast<float4*>(v + 4) =
-                *reinterpret_cast<const float4*>(&slab[r * LDW + c0 + 4]);
-            const bool ok = col < p.N && (MODE == RAGGED_M ? rl < ti.rows : ti.m0 + rl < p.M);
-            if (ok) {
-                if constexpr (DUAL) {
-                    float v3[8];
-                    *reinterpret_cast<float4*>(v3) =
-                        *reinterpret_cast<const float4*>(&slab[SLAB + r * LDW + c0]);
-                    *reinterpret_cast<float4*>(v3 + 4) =
-                        *reinterpret_cast<const float4*>(&slab[SLAB + r * LDW + c0 + 4]);
-                    epi.vec8(ti.e, ti.r0 + rl, col, v, v3);
-                } else if (MODE == RAGGED_M) {
-                    epi.vec8(ti.e, ti.r0 + rl, col, v);
-                } else {
-                    epi.vec8(ti.e, (long)ti.m0 + rl, col, v);
+            for (int ps = 0; ps < 16 / RPP; ++ps) {
+                const int r = ps * RPP + lane / LPR;
+                const int c0 = (lane % LPR) * 8;
+                const int rl = wm * WTM + i * 32 + h * 16 + r;
+                const int col = ti.n0 + wn * WTN + c0;
+                const float* src = &slab[r * LDW + c0];
+                float v[8];
+                *reinterpret_cast<float4*>(v) = *reinterpret_cast<const float4*>(src);
+                *reinterpret_cast<float4*>(v + 4) = *reinterpret_cast<const float4*>(src + 4);
+                const bool ok =
+                    col < p.N && (MODE == RAGGED_M ? rl < ti.rows : ti.m0 + rl < p.M);
+                if (ok) {
+                    if constexpr (DUAL) {
+                        float v3[8];
+                        *reinterpret_cast<float4*>(v3) =
+                            *reinterpret_cast<const float4*>(src + SLAB);
+                        *reinterpret_cast<float4*>(v3 + 4) =
+                            *reinterpret_cast<const float4*>(src + SLAB + 4);
+                        epi.vec8(ti.e, ti.r0 + rl, col, v, v3);
+                    } else if (MODE == RAGGED_M) {
+                        epi.vec8(ti.e, ti.r0 + rl, col, v);
+                    } else {
+                        epi.vec8(ti.e, (long)ti.m0 + rl, col, v);
+                    }
                 }
             }
+            __syncthreads();
         }
-        __syncthreads();
     }
 }
 
@@ -506,7 +579,7 @@ __global__ __launch_bounds__(256) void ggemm_f32_kernel(GemmArgs<float> p, Epi e
     __shared__ float sA[FK][FB + 4];
     __shared__ float sB[FK][FB + 4];
     __shared__ float sB2[DUAL ? FK : 1][FB + 4];
-    const TileInfo ti = decode_tile<MODE, FB, FB>(p);
+    const TileInfo ti = decode_tile<MODE, FB, FB, 1>(p);
     if (!ti.live) return;
     const int tid = threadIdx.x, tm = tid / 16, tn = tid % 16;
     float acc[4][4], acc2[4][4];
@@ -646,7 +719,8 @@ FfnWs ffn_layout(int R, int E, int f, moe_act act, moe_dtype dt, int backward) {
     return w;
 }
 
-template <int BM, int BN, int MODE, int ALAY, int BLAY, bool DUAL, bool KSPLIT, class Epi>
+template <int BM, int BN, int WM, int WN, int MODE, int ALAY, int BLAY, bool DUAL,
+          bool KSPLIT, class Epi>
 void launch_bf16(GemmArgs<bf16_t> p, Epi epi, int R, hipStream_t s, const char* name) {
     p.nN = (p.N + BN - 1) / BN;
     int blocks;
@@ -657,8 +731,11 @@ void launch_bf16(GemmArgs<bf16_t> p, Epi epi, int R, hipStream_t s, const char* 
         blocks = p.E * p.nM * p.nN;
     }
     if (blocks <= 0) return;
+    const int pad = NXCD * (MODE == RAGGED_M ? 32 : 8);   // whole XCD runs
+    blocks = (blocks + pad - 1) / pad * pad;
     MOE_LAUNCH(name, s,
-               ggemm_bf16_kernel<BM, BN, MODE, ALAY, BLAY, DUAL, KSPLIT, Epi><<<blocks, 256, 0, s>>>(p, epi));
+               ggemm_bf16_kernel<BM, BN, WM, WN, MODE, ALAY, BLAY, DUAL, KSPLIT, Epi>
+               <<<blocks, 64 * WM * WN, 0, s>>>(p, epi));
 }
 
 template <int MODE, int ALAY, int BLAY, bool DUAL, bool KSPLIT, class Epi>
@@ -686,23 +763,34 @@ GemmArgs<T> base_args(const int32_t* offsets, const int32_t* prefix,
     return p;
 }
 
-template <typename T>
+// Tile configuration of the bf16 path: block tile and wave grid for the
+// single-product GEMMs, and for the dual-weight (SwiGLU up) product.
+template <int BM_, int BN_, int WM_, int WN_, int BND_, int WMD_, int WND_>
+struct TileCfg {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr int BND = BND_, WMD = WMD_, WND = WND_;
+};
+using DefaultCfg = TileCfg<256, 256, 4, 2, 128, 4, 2>;
+
+template <typename T, class Cfg>
 struct Launch;
 
-template <>
-struct Launch<bf16_t> {
+template <class Cfg>
+struct Launch<bf16_t, Cfg> {
     template <int MODE, int ALAY, int BLAY, bool DUAL, bool KSPLIT, class Epi>
     static void go(GemmArgs<bf16_t> p, Epi epi, int R, hipStream_t s, const char* name) {
         if constexpr (DUAL)
-            launch_bf16<BM_BF16, 128, MODE, ALAY, BLAY, DUAL, KSPLIT>(p, epi, R, s, name);
+            launch_bf16<Cfg::BM, Cfg::BND, Cfg::WMD, Cfg::WND, MODE, ALAY, BLAY, DUAL, KSPLIT>(
+                p, epi, R, s, name);
         else
-            launch_bf16<BM_BF16, 256, MODE, ALAY, BLAY, DUAL, KSPLIT>(p, epi, R, s, name);
+            launch_bf16<Cfg::BM, Cfg::BN, Cfg::WM, Cfg::WN, MODE, ALAY, BLAY, DUAL, KSPLIT>(
+                p, epi, R, s, name);
     }
-    static constexpr int BM = BM_BF16;
+    static constexpr int BM = Cfg::BM;
 };
 
-template <>
-struct Launch<float> {
+template <class Cfg>
+struct Launch<float, Cfg> {
     template <int MODE, int ALAY, int BLAY, bool DUAL, bool KSPLIT, class Epi>
     static void go(GemmArgs<float> p, Epi epi, int R, hipStream_t s, const char* name) {
         launch_f32<MODE, ALAY, BLAY, DUAL, KSPLIT>(p, epi, R, s, name);
@@ -710,7 +798,7 @@ struct Launch<float> {
     static constexpr int BM = FB;
 };
 
-template <typename T>
+template <typename T, class Cfg = DefaultCfg>
 moe_status ffn_fwd(const void* x_perm, const int32_t* offsets, int R, int E,
                    int d, int f, moe_act act, const void* W1, const void* W3,
                    const void* W2, void* h_save, void* a_save, void* out_perm,
@@ -720,7 +808,7 @@ moe_status ffn_fwd(const void* x_perm, const int32_t* offsets, int R, int E,
     int32_t* prefix = reinterpret_cast<int32_t*>(base + L.prefix);
     int32_t* order = reinterpret_cast<int32_t*>(base + L.order);
     MOE_LAUNCH("ffn_plan", s,
-               ffn_plan_kernel<<<1, 1024, 0, s>>>(offsets, E, Launch<T>::BM, prefix, order));
+               ffn_plan_kernel<<<1, 1024, 0, s>>>(offsets, E, Launch<T, Cfg>::BM, prefix, order));
 
     const T* xp = static_cast<const T*>(x_perm);
     T* H = static_cast<T*>(h_save);
@@ -731,11 +819,11 @@ moe_status ffn_fwd(const void* x_perm, const int32_t* offsets, int R, int E,
     p.B = static_cast<const T*>(W1); p.ldb = f; p.bstride = (long)d * f;
     p.N = f; p.K = d;
     if (act == MOE_ACT_GELU) {
-        Launch<T>::template go<RAGGED_M, KMAJ, MNMAJ, false, false>(
+        Launch<T, Cfg>::template go<RAGGED_M, KMAJ, MNMAJ, false, false>(
             p, EpiGeluFwd<T>{H, A, f}, R, s, "gemm_up_gelu");
     } else {
         p.B2 = static_cast<const T*>(W3);
-        Launch<T>::template go<RAGGED_M, KMAJ, MNMAJ, true, false>(
+        Launch<T, Cfg>::template go<RAGGED_M, KMAJ, MNMAJ, true, false>(
             p, EpiSwigluFwd<T>{H, A, f}, R, s, "gemm_up_swiglu");
     }
     // GEMM2: A [R,f] x W2[e] [f,d]
@@ -743,12 +831,12 @@ moe_status ffn_fwd(const void* x_perm, const int32_t* offsets, int R, int E,
     q.A = A; q.lda = f;
     q.B = static_cast<const T*>(W2); q.ldb = d; q.bstride = (long)f * d;
     q.N = d; q.K = f;
-    Launch<T>::template go<RAGGED_M, KMAJ, MNMAJ, false, false>(
+    Launch<T, Cfg>::template go<RAGGED_M, KMAJ, MNMAJ, false, false>(
         q, EpiStore<T>{static_cast<T*>(out_perm), d, 0}, R, s, "gemm_down");
     return launch_status();
 }
 
-template <typename T>
+template <typename T, class Cfg = DefaultCfg>
 moe_status ffn_bwd(const void* d_out, const void* x_perm, const void* h_save,
                    const void* a_save, const int32_t* offsets, int R, int E,
                    int d, int f, moe_act act, const void* W1, const void* W3,
@@ -762,7 +850,7 @@ moe_status ffn_bwd(const void* d_out, const void* x_perm, const void* h_save,
     const bool sw = act == MOE_ACT_SWIGLU;
     const long ldh = sw ? 2L * f : (long)f;
     MOE_LAUNCH("ffn_plan", s,
-               ffn_plan_kernel<<<1, 1024, 0, s>>>(offsets, E, Launch<T>::BM, prefix, order));
+               ffn_plan_kernel<<<1, 1024, 0, s>>>(offsets, E, Launch<T, Cfg>::BM, prefix, order));
 
     const T* dO = static_cast<const T*>(d_out);
     // dA = dO W2[e]^T with the activation derivative in the epilogue -> dH
@@ -772,10 +860,10 @@ moe_status ffn_bwd(const void* d_out, const void* x_perm, const void* h_save,
         p.B = static_cast<const T*>(W2); p.ldb = d; p.bstride = (long)f * d;
         p.N = f; p.K = d;
         if (!sw)
-            Launch<T>::template go<RAGGED_M, KMAJ, KMAJ, false, false>(
+            Launch<T, Cfg>::template go<RAGGED_M, KMAJ, KMAJ, false, false>(
                 p, EpiGeluBwd<T>{static_cast<const T*>(h_save), dH, f}, R, s, "gemm_dA_gelu");
         else
-            Launch<T>::template go<RAGGED_M, KMAJ, KMAJ, false, false>(
+            Launch<T, Cfg>::template go<RAGGED_M, KMAJ, KMAJ, false, false>(
                 p, EpiSwigluBwd<T>{static_cast<const T*>(h_save), dH, f}, R, s, "gemm_dA_swiglu");
     }
     // dW2[e] = A_e^T dO_e   [f, d]
@@ -783,7 +871,7 @@ moe_status ffn_bwd(const void* d_out, const void* x_perm, const void* h_save,
         GemmArgs<T> p = base_args<T>(offsets, prefix, order, E);
         p.A = static_cast<const T*>(a_save); p.lda = f; p.M = f;
         p.B = dO; p.ldb = d; p.N = d;
-        Launch<T>::template go<RAGGED_K, MNMAJ, MNMAJ, false, false>(
+        Launch<T, Cfg>::template go<RAGGED_K, MNMAJ, MNMAJ, false, false>(
             p, EpiStore<T>{static_cast<T*>(dW2), d, (long)f * d}, R, s, "gemm_dW2");
     }
     // dW1[e] = X_e^T dH1_e  [d, f]   (dW3 with dH3)
@@ -791,11 +879,11 @@ moe_status ffn_bwd(const void* d_out, const void* x_perm, const void* h_save,
         GemmArgs<T> p = base_args<T>(offsets, prefix, order, E);
         p.A = static_cast<const T*>(x_perm); p.lda = d; p.M = d;
         p.B = dH; p.ldb = ldh; p.N = f;
-        Launch<T>::template go<RAGGED_K, MNMAJ, MNMAJ, false, false>(
+        Launch<T, Cfg>::template go<RAGGED_K, MNMAJ, MNMAJ, false, false>(
             p, EpiStore<T>{static_cast<T*>(dW1), f, (long)d * f}, R, s, "gemm_dW1");
         if (sw) {
             p.B = dH + f;
-            Launch<T>::template go<RAGGED_K, MNMAJ, MNMAJ, false, false>(
+            Launch<T, Cfg>::template go<RAGGED_K, MNMAJ, MNMAJ, false, false>(
                 p, EpiStore<T>{static_cast<T*>(dW3), f, (long)d * f}, R, s, "gemm_dW3");
         }
     }
@@ -808,12 +896,12 @@ moe_status ffn_bwd(const void* d_out, const void* x_perm, const void* h_save,
         EpiStore<T> st{static_cast<T*>(dx_perm), d, 0};
         if (!sw) {
             p.K = f;
-            Launch<T>::template go<RAGGED_M, KMAJ, KMAJ, false, false>(p, st, R, s, "gemm_dX");
+            Launch<T, Cfg>::template go<RAGGED_M, KMAJ, KMAJ, false, false>(p, st, R, s, "gemm_dX");
         } else {
             p.K = 2 * f;
             p.Ksplit = f;
             p.B2 = static_cast<const T*>(W3);
-            Launch<T>::template go<RAGGED_M, KMAJ, KMAJ, false, true>(p, st, R, s, "gemm_dX");
+            Launch<T, Cfg>::template go<RAGGED_M, KMAJ, KMAJ, false, true>(p, st, R, s, "gemm_dX");
         }
     }
     return launch_status();
