@@ -62,21 +62,43 @@ def stream_key(seed: int, tensor: int, expert: int = 0) -> int:
                              np.array([tensor * 65536 + expert]))[0])
 
 
+def _fill_chunk(out, key, start, lo, n, sc):
+    mask = np.uint64(0xFFFF)
+    h = splitmix64_at(key, np.arange(start + lo, start + lo + n, dtype=np.uint64))
+    s = ((h & mask) + ((h >> np.uint64(16)) & mask)
+         + ((h >> np.uint64(32)) & mask) + (h >> np.uint64(48)))
+    dd = s.astype(np.int64) + 2 - 131072
+    z = dd.astype(np.float32) * C0
+    out[lo:lo + n] = z * sc
+
+
+def _threads():
+    import os
+    try:
+        return max(1, min(16, len(os.sched_getaffinity(0))))
+    except AttributeError:
+        return 1
+
+
 def normal_f32(key: int, start: int, count: int, scale: float,
-               chunk: int = 1 << 22) -> np.ndarray:
-    """``count`` deviates of stream ``key`` from element ``start`` on, fp32."""
+               chunk: int = 1 << 20) -> np.ndarray:
+    """``count`` deviates of stream ``key`` from element ``start`` on, fp32.
+
+    Large requests are split into chunks filled by a thread pool (NumPy
+    releases the GIL); every element depends only on its own counter, so
+    the result does not depend on the chunking.
+    """
     out = np.empty(count, dtype=np.float32)
     sc = np.float32(scale)
-    mask = np.uint64(0xFFFF)
-    for lo in range(0, count, chunk):
-        n = min(chunk, count - lo)
-        h = splitmix64_at(key, np.arange(start + lo, start + lo + n,
-                                         dtype=np.uint64))
-        s = ((h & mask) + ((h >> np.uint64(16)) & mask)
-             + ((h >> np.uint64(32)) & mask) + (h >> np.uint64(48)))
-        dd = s.astype(np.int64) + 2 - 131072
-        z = dd.astype(np.float32) * C0
-        out[lo:lo + n] = z * sc
+    starts = list(range(0, count, chunk))
+    if len(starts) <= 2:
+        for lo in starts:
+            _fill_chunk(out, key, start, lo, min(chunk, count - lo), sc)
+        return out
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(lambda lo: _fill_chunk(out, key, start, lo,
+                                           min(chunk, count - lo), sc), starts))
     return out
 
 
@@ -87,6 +109,23 @@ def bf16_round_bits(a: np.ndarray) -> np.ndarray:
     return ((u + r) >> np.uint32(16)).astype(np.uint16)
 
 
+def _round_inplace_bf16(a: np.ndarray) -> np.ndarray:
+    """Round an fp32 array to bf16 values in place (chunked, threaded)."""
+    flat = a.reshape(-1)
+    step = 1 << 22
+
+    def one(lo):
+        seg = flat[lo:lo + step]
+        seg[:] = bf16_bits_to_f32(bf16_round_bits(seg))
+    if flat.size <= 2 * step:
+        one(0) if flat.size <= step else (one(0), one(step))
+        return a
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(one, range(0, flat.size, step)))
+    return a
+
+
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
 
@@ -95,6 +134,8 @@ def round_to_dtype(a: np.ndarray, dtype: str) -> np.ndarray:
     """Values exactly representable in ``dtype``, held as fp32."""
     if dtype == "f32":
         return a
+    if a.size > (1 << 23):
+        return _round_inplace_bf16(np.ascontiguousarray(a, dtype=np.float32))
     return bf16_bits_to_f32(bf16_round_bits(a))
 
 

@@ -228,6 +228,30 @@ def ffn_bwd_segment(dO, xs, W1e, W2e, W3e=None, act="gelu", saved=None):
     return dX, dW1, dW3, dW2
 
 
+def ffn_bwd_columns(dO, xs, W1e, W2e, W3e=None, act="gelu", cols=None):
+    """Weight gradients of one expert restricted to hidden units ``cols``.
+
+    Hidden unit c of an expert touches only column c of W1 (and W3) and row c
+    of W2, so dW1[:, c], dW3[:, c] and dW2[c, :] follow from the expert's
+    rows exactly as in ``ffn_bwd_segment`` without forming the other units.
+    Returns (dW1[:, cols], dW3[:, cols] or None, dW2[cols, :]), float64.
+    """
+    cols = np.asarray(cols, dtype=np.int64)
+    dO = np.asarray(dO, F64)
+    xs = np.asarray(xs, F64)
+    H = xs @ np.asarray(W1e, F64)[:, cols]
+    dA = dO @ np.asarray(W2e, F64)[cols, :].T
+    if act == "gelu":
+        A = gelu(H)
+        dH = dA * gelu_grad(H)
+        return xs.T @ dH, None, A.T @ dO
+    H3 = xs @ np.asarray(W3e, F64)[:, cols]
+    A = silu(H) * H3
+    dH1 = dA * H3 * silu_grad(H)
+    dH3 = dA * silu(H)
+    return xs.T @ dH1, xs.T @ dH3, A.T @ dO
+
+
 def _w(W, e):
     """Expert e's matrix from a stacked array or a mapping/callable."""
     if W is None:

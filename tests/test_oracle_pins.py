@@ -207,3 +207,49 @@ def test_zero_load_expert_has_zero_weight_grad():
     assert list(fw["counts"]) == [6, 0, 0, 0]
     for e in (1, 2, 3):
         assert np.all(gr["dW1"][e] == 0) and np.all(gr["dW2"][e] == 0)
+
+
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
+def test_column_restricted_expert_grads_equal_full(act):
+    # the restricted form is the full segment backward read at a few hidden
+    # units (pinned here against ffn_bwd_segment, itself pinned by finite
+    # differences and torch autograd above)
+    g = np.random.default_rng(70)
+    n, d, f = 13, 6, 9
+    xs = g.standard_normal((n, d))
+    dO = g.standard_normal((n, d))
+    W1, W3 = g.standard_normal((d, f)), g.standard_normal((d, f))
+    W2 = g.standard_normal((f, d))
+    _, dW1, dW3, dW2 = oracle.ffn_bwd_segment(dO, xs, W1, W2, W3, act)
+    cols = np.array([0, 4, 8, 5])
+    c1, c3, c2 = oracle.ffn_bwd_columns(dO, xs, W1, W2, W3, act, cols)
+    assert np.allclose(c1, dW1[:, cols], rtol=1e-13, atol=1e-13)
+    assert np.allclose(c2, dW2[cols, :], rtol=1e-13, atol=1e-13)
+    if act == "swiglu":
+        assert np.allclose(c3, dW3[:, cols], rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
+def test_column_restricted_expert_grads_torch(act):
+    # the same quantities from torch float64 autograd of L = <dO, FFN(x)>
+    import torch
+    g = np.random.default_rng(71)
+    n, d, f = 11, 5, 7
+    xs = g.standard_normal((n, d))
+    dO = g.standard_normal((n, d))
+    t = lambda a: torch.tensor(a, requires_grad=True)
+    W1, W3, W2 = t(g.standard_normal((d, f))), t(g.standard_normal((d, f))), \
+        t(g.standard_normal((f, d)))
+    X = torch.tensor(xs)
+    h = X @ W1
+    a = torch.nn.functional.gelu(h) if act == "gelu" else \
+        torch.nn.functional.silu(h) * (X @ W3)
+    ((a @ W2) * torch.tensor(dO)).sum().backward()
+    cols = np.array([6, 1, 3])
+    c1, c3, c2 = oracle.ffn_bwd_columns(dO, xs, W1.detach().numpy(),
+                                        W2.detach().numpy(),
+                                        W3.detach().numpy(), act, cols)
+    assert np.allclose(c1, W1.grad.numpy()[:, cols], rtol=1e-12, atol=1e-12)
+    assert np.allclose(c2, W2.grad.numpy()[cols, :], rtol=1e-12, atol=1e-12)
+    if act == "swiglu":
+        assert np.allclose(c3, W3.grad.numpy()[:, cols], rtol=1e-12, atol=1e-12)
