@@ -27,6 +27,32 @@ PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA, 256 CU x 2.4 GHz
 PEAK_F32_TFLOPS = 157.3       # fp32 vector
 PEAK_HBM_GBS = 8000.0
 
+# HBM bytes per launch (fetch + write) of the FFN and row kernels on the
+# MoE-S-like workload, from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs
+# scaled by the readings of a plain 1 GiB device copy (factors 6.0 and 1.5);
+# see profiles/hbm_traffic_moe_s_like.md.  Valid only for the kernel sources
+# whose SHA-256 prefix is TRAFFIC_SRC; null once they change.
+TRAFFIC_SRC = "41a03a652cb41189"
+TRAFFIC_SOURCES = ("ggemm.hip", "common.h", "permute.hip", "combine.hip")
+TRAFFIC = {"gemm_up_gelu": 1174509062, "gemm_down": 830728245,
+           "gemm_dA_gelu": 1392432808, "gemm_dW1": 1610767075,
+           "gemm_dW2": 1610767075, "gemm_dX": 830736232, "perm_copy": 101567255,
+           "combine": 127494818, "combine_bwd": 203230211,
+           "unpermute_grad": 126719206}
+
+
+def traffic_for(kernel, workload):
+    """Measured HBM bytes per launch, or None if stale or not measured."""
+    import hashlib
+    if workload != "moe_s_like" or kernel not in TRAFFIC:
+        return None
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, "mixture_experts_layer_permute_amd", "csrc", f),
+                  "rb") as fh:
+            h.update(fh.read())
+    return TRAFFIC[kernel] if h.hexdigest()[:16] == TRAFFIC_SRC else None
+
 
 def kernel_work(cfg):
     """Algorithmic work of one launch of each kernel: (amount, unit)."""
@@ -122,11 +148,13 @@ def main():
     stream = torch.cuda.current_stream()
     s = stream.cuda_stream
     if args.calib_copy_mb:
-        n = args.calib_copy_mb << 20
-        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        # plain elementwise copy (ordinary loads and stores) of a known size:
+        # reads and writes calib_copy_mb MiB each
+        n = (args.calib_copy_mb << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        dst.copy_(src)
+        torch.add(src, 0.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
 
@@ -182,13 +210,15 @@ def main():
         peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
         ach = amt / (kernels[dom]["avg_ms"] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(ach / peak, 4),
+                "traffic": traffic_for(dom, cfg.name),
                 "kernel": dom, "work_per_launch": amt}
     elif unit == "byte":
         ach = amt / (kernels[dom]["avg_ms"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
-                "traffic": None, "kernel": dom, "work_per_launch": amt}
+                "traffic": traffic_for(dom, cfg.name), "kernel": dom,
+                "work_per_launch": amt}
     else:
         roof = {"bound": "alu", "achieved": None, "peak": None, "unit": None,
                 "frac": None, "traffic": None, "kernel": dom}
