@@ -188,40 +188,57 @@ def main():
         per.setdefault(name, []).append(kms)
     work = kernel_work(cfg)
     kernels = {}
-    gemm_ms = 0.0
     for name, v in per.items():
-        avg = sum(v) / len(v)
-        ent = {"avg_ms": round(avg, 5), "launches_per_step": len(v) / args.steps,
-               "ms_per_step": round(sum(v) / args.steps, 5)}
-        if name in work:
-            amt, unit = work[name]
-            if unit == "flop":
-                ent["tflops"] = round(amt / (avg * 1e-3) / 1e12, 2)
-                ent["frac_of_peak"] = round(ent["tflops"] / PEAK_BF16_TFLOPS, 4)
-                gemm_ms += sum(v) / args.steps
-            else:
-                ent["gbs"] = round(amt / (avg * 1e-3) / 1e9, 1)
-                ent["frac_of_peak"] = round(ent["gbs"] / PEAK_HBM_GBS, 4)
-        kernels[name] = ent
+        kernels[name] = {"avg_ms": round(sum(v) / len(v), 5),
+                         "launches_per_step": len(v) / args.steps,
+                         "ms_per_step": round(sum(v) / args.steps, 5)}
+    # A grouped GEMM whose last round of workgroups would be nearly empty is
+    # launched as a main kernel plus a narrow-tile "<name>_tail" kernel; its
+    # work and rates belong to the pair (one launch of each per call).
+    parts = {}
+    for name in kernels:
+        base = name[:-5] if name.endswith("_tail") else name
+        parts.setdefault(base, []).append(name)
+    gemm_ms = 0.0
+    stage_ms = {}          # per call of the stage (main + tail)
+    for base, names in parts.items():
+        if base not in work:
+            continue
+        calls = kernels[base]["launches_per_step"] if base in kernels else 1.0
+        per_call = sum(kernels[n]["ms_per_step"] for n in names) / calls
+        stage_ms[base] = per_call
+        amt, unit = work[base]
+        ent = kernels[base] if base in kernels else kernels[names[0]]
+        if len(names) > 1:
+            ent["with_tail_avg_ms"] = round(per_call, 5)
+            for n in names:
+                if n != base:
+                    kernels[n]["part_of"] = base
+        if unit == "flop":
+            ent["tflops"] = round(amt / (per_call * 1e-3) / 1e12, 2)
+            ent["frac_of_peak"] = round(ent["tflops"] / PEAK_BF16_TFLOPS, 4)
+            gemm_ms += per_call * calls
+        else:
+            ent["gbs"] = round(amt / (per_call * 1e-3) / 1e9, 1)
+            ent["frac_of_peak"] = round(ent["gbs"] / PEAK_HBM_GBS, 4)
     gemm_flops = cfg.gemm_flops_fwd_bwd()
-    dom = max(kernels, key=lambda n: kernels[n]["ms_per_step"])
-    amt, unit = work.get(dom, (None, None))
+    dom = max(stage_ms, key=lambda n: stage_ms[n] * kernels.get(n, {}).get(
+        "launches_per_step", 1.0))
+    amt, unit = work[dom]
+    launches = sorted(parts[dom])
     if unit == "flop":
         peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
-        ach = amt / (kernels[dom]["avg_ms"] * 1e-3) / 1e12
+        ach = amt / (stage_ms[dom] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(ach / peak, 4),
                 "traffic": traffic_for(dom, cfg.name),
-                "kernel": dom, "work_per_launch": amt}
-    elif unit == "byte":
-        ach = amt / (kernels[dom]["avg_ms"] * 1e-3) / 1e9
+                "kernel": dom, "launches": launches, "work_per_launch": amt}
+    else:
+        ach = amt / (stage_ms[dom] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
                 "traffic": traffic_for(dom, cfg.name), "kernel": dom,
-                "work_per_launch": amt}
-    else:
-        roof = {"bound": "alu", "achieved": None, "peak": None, "unit": None,
-                "frac": None, "traffic": None, "kernel": dom}
+                "launches": launches, "work_per_launch": amt}
 
     out = {
         "metric": METRIC,

@@ -35,7 +35,8 @@
  *  - Limits: 1 <= k <= E <= 1024; T*k < 2^31; d a multiple of 8 for the gate
  *    and the permute, of 64 for the FFN, combine and unpermute; f a multiple
  *    of 64; device pointers to rows 16-byte aligned.  T = 0 is accepted and
- *    launches nothing.
+ *    launches nothing, except that the gate backward still writes its dWg
+ *    (all zeros).
  *  - Threads: entry points are reentrant; concurrent calls on different
  *    streams must not share output or workspace buffers.
  */

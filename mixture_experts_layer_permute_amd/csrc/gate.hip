@@ -19,21 +19,25 @@ namespace moe {
 namespace {
 
 // ------------------------------------------------------------ logits
-// Block: 256 threads.  TE experts per block column (4 per thread); the other
-// thread dimension spans tokens (MT per thread), so every thread carries
-// MT x 4 independent fp32 chains, each summed in increasing feature order.
-// Features come in chunks of GKC: the token rows are copied to LDS as raw
-// 16-byte vectors (padded rows), the gate columns as fp32, and the next
-// chunk is fetched into registers while the current one is consumed.
+// Block: 256 threads.  TE experts per block column, EPT of them per thread
+// (experts tx, tx + TX, ...: rows a TX apart keep the LDS reads spread);
+// the other thread dimension spans tokens (MT per thread), so every thread
+// carries MT x EPT independent fp32 chains, each summed in increasing
+// feature order.  Features come in chunks of GKC: the token rows are copied
+// to LDS as raw 16-byte vectors (padded rows), the gate columns as fp32
+// transposed to [expert][feature] so that one 16-byte read yields four
+// consecutive features of one expert; the next chunk is fetched into
+// registers while the current one is consumed.
 constexpr int GKC = 64;
+constexpr int GWP = GKC + 4;                   // padded LDS row of a gate column
 
-template <typename T, int TE, int MT>
+template <typename T, int TE, int EPT, int MT>
 __global__ __launch_bounds__(256) void gate_logits_kernel(
     const T* __restrict__ x, const T* __restrict__ Wg,
     const float* __restrict__ bias, int Tn, int d, int E,
     float* __restrict__ logits) {
 #pragma clang fp contract(off)
-    constexpr int TX = TE / 4;                 // threads across experts
+    constexpr int TX = TE / EPT;               // threads across experts
     constexpr int TY = 256 / TX;               // threads across tokens
     constexpr int TT = MT * TY;                // tokens per block
     constexpr int V = 16 / sizeof(T);          // elements per 16-byte vector
@@ -41,8 +45,9 @@ __global__ __launch_bounds__(256) void gate_logits_kernel(
     constexpr int XV = (TT * VPR + 255) / 256; // x vectors per thread per chunk
     constexpr int XROW = GKC * sizeof(T) + 16; // padded LDS row (bytes)
     constexpr int WV = (GKC * TE + 255) / 256; // gate elements per thread per chunk
+    static_assert(TE % EPT == 0 && 256 % TX == 0, "thread layout");
     __shared__ __attribute__((aligned(16))) uint8_t xs[TT * XROW];
-    __shared__ __attribute__((aligned(16))) float ws[GKC][TE];
+    __shared__ __attribute__((aligned(16))) float ws[TE * GWP];
 
     const int tid = threadIdx.x;
     const int tx = tid % TX, ty = tid / TX;
@@ -81,15 +86,15 @@ __global__ __launch_bounds__(256) void gate_logits_kernel(
 #pragma unroll
         for (int q = 0; q < WV; ++q) {
             const int idx = tid + 256 * q;
-            if (idx < GKC * TE) ws[idx / TE][idx % TE] = wr[q];
+            if (idx < GKC * TE) ws[(idx % TE) * GWP + idx / TE] = wr[q];
         }
     };
 
-    float acc[MT][4];
+    float acc[MT][EPT];
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[m][b] = 0.0f;
+        for (int b = 0; b < EPT; ++b) acc[m][b] = 0.0f;
 
     fetch(0);
     for (int k0 = 0; k0 < d; k0 += GKC) {
@@ -105,21 +110,29 @@ __global__ __launch_bounds__(256) void gate_logits_kernel(
                 Vec16<T>::ld(reinterpret_cast<const T*>(xs + (ty * MT + m) * XROW + kv * 16),
                              xv[m]);
 #pragma unroll
-            for (int q = 0; q < V; ++q) {
-                const float4 w4 = *reinterpret_cast<const float4*>(&ws[kv * V + q][tx * 4]);
-                const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
+            for (int q4 = 0; q4 < V / 4; ++q4) {
+                float wv[EPT][4];
 #pragma unroll
-                for (int m = 0; m < MT; ++m)
+                for (int b = 0; b < EPT; ++b) {
+                    const float4 w4 = *reinterpret_cast<const float4*>(
+                        &ws[(tx + TX * b) * GWP + kv * V + q4 * 4]);
+                    wv[b][0] = w4.x; wv[b][1] = w4.y; wv[b][2] = w4.z; wv[b][3] = w4.w;
+                }
 #pragma unroll
-                    for (int b = 0; b < 4; ++b) {
-                        if constexpr (sizeof(T) == 2) {
-                            // exact product: one rounding either way
-                            acc[m][b] = __builtin_fmaf(xv[m][q], wv[b], acc[m][b]);
-                        } else {
-                            const float pr = xv[m][q] * wv[b];
-                            acc[m][b] = acc[m][b] + pr;
+                for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+                    for (int m = 0; m < MT; ++m)
+#pragma unroll
+                        for (int b = 0; b < EPT; ++b) {
+                            const float xq = xv[m][q4 * 4 + qq];
+                            if constexpr (sizeof(T) == 2) {
+                                // exact product: one rounding either way
+                                acc[m][b] = __builtin_fmaf(xq, wv[b][qq], acc[m][b]);
+                            } else {
+                                const float pr = xq * wv[b][qq];
+                                acc[m][b] = acc[m][b] + pr;
+                            }
                         }
-                    }
             }
         }
     }
@@ -128,8 +141,8 @@ __global__ __launch_bounds__(256) void gate_logits_kernel(
         const long t = t0 + ty * MT + m;
         if (t >= Tn) continue;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int e = e0 + tx * 4 + b;
+        for (int b = 0; b < EPT; ++b) {
+            const int e = e0 + tx + TX * b;
             if (e >= E) continue;
             float v = acc[m][b];
             if (bias) v = v + bias[e];
@@ -258,67 +271,121 @@ __global__ __launch_bounds__(256) void gate_dlogits_kernel(
     }
 }
 
-// partial[c][i][e] = sum over tokens of chunk c (in order) of x[t,i]*dl[t,e].
-// Thread: one feature i and up to 8 experts; TPI threads share one i.
-constexpr int GB_TS = 8;        // tokens staged per LDS round
+// partial[c][i][e] = sum over the tokens of chunk c of x[t,i] * dl[t,e], on
+// the fp32 matrix cores (v_mfma_f32_32x32x2_f32: features are the rows,
+// experts the columns, tokens the reduction).  One wave owns 128 features
+// and 32 experts of one chunk.  Lane l reads 4 consecutive features of token
+// 2p + l/32 in one load and feeds feature 4*(l%32) + j to feature tile j,
+// so row m of tile j is feature 4m + j.  The next DW_TS tokens are loaded
+// while the current ones are multiplied.
+constexpr int DW_FT = 4;        // feature tiles per wave (4 consecutive features per lane)
+constexpr int DW_TS = 32;       // tokens per register batch (16 MFMA steps)
+
+template <typename T> struct Quad;
+template <> struct Quad<float> {
+    typedef float4 raw;
+    static __device__ __forceinline__ raw ld(const float* p) { return *reinterpret_cast<const float4*>(p); }
+    static __device__ __forceinline__ float get(const raw& r, int j) {
+        return j == 0 ? r.x : j == 1 ? r.y : j == 2 ? r.z : r.w;
+    }
+};
+template <> struct Quad<bf16_t> {
+    typedef uint2 raw;
+    static __device__ __forceinline__ raw ld(const bf16_t* p) { return *reinterpret_cast<const uint2*>(p); }
+    static __device__ __forceinline__ float get(const raw& r, int j) {
+        const uint32_t w = j < 2 ? r.x : r.y;
+        return __uint_as_float(j & 1 ? w & 0xFFFF0000u : w << 16);
+    }
+};
 
 template <typename T>
 __global__ __launch_bounds__(256) void gate_dwg_partial_kernel(
     const T* __restrict__ x, const float* __restrict__ dl, int Tn, int d,
-    int E, int tpi, int tc, float* __restrict__ partial) {
-    extern __shared__ float sm[];
-    const int iw = 256 / tpi;
-    float* xs = sm;                           // [GB_TS][iw]
-    float* ds = sm + GB_TS * iw;              // [GB_TS][E]
-    const int tid = threadIdx.x;
-    const int il = tid % iw, eg = tid / iw;
-    const int i0 = blockIdx.y * iw;
-    const long c = blockIdx.x;
+    int E, int tc, int nft, float* __restrict__ partial) {
+    typedef typename Quad<T>::raw raw;
+    const int lane = threadIdx.x & 63;
+    const int ft = blockIdx.x * 4 + (threadIdx.x >> 6);   // feature group of this wave
+    if (ft >= nft) return;                                 // whole wave leaves
+    const int e0 = blockIdx.y * 32;
+    const long c = blockIdx.z;
     const long tbeg = c * tc;
     const long tend = min((long)Tn, tbeg + tc);
-    float acc[8];
+    const int col = lane & 31, half = lane >> 5;
+    const int fbase = ft * 32 * DW_FT;
+    const int i = fbase + 4 * col;                          // d % 4 == 0: all 4 or none
+    const int e = e0 + col;
+
+    f32x16 acc[DW_FT];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
-    for (long ts0 = tbeg; ts0 < tend; ts0 += GB_TS) {
-        const int nts = (int)min((long)GB_TS, tend - ts0);
-        for (int q = tid; q < GB_TS * iw; q += 256) {
-            const int tt = q / iw, ii = q % iw;
-            float v = 0.0f;
-            if (tt < nts && i0 + ii < d) v = Elem<T>::ld(x + (ts0 + tt) * d + i0 + ii);
-            xs[q] = v;
-        }
-        for (int q = tid; q < GB_TS * E; q += 256) {
-            const int tt = q / E, e = q % E;
-            ds[q] = tt < nts ? dl[(ts0 + tt) * E + e] : 0.0f;
-        }
-        __syncthreads();
-        for (int tt = 0; tt < nts; ++tt) {
-            const float xv = xs[tt * iw + il];
+    for (int j = 0; j < DW_FT; ++j)
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int e = eg * 8 + q;
-                if (e < E) acc[q] = fmaf(xv, ds[tt * E + e], acc[q]);
-            }
+        for (int v = 0; v < 16; ++v) acc[j][v] = 0.0f;
+
+    constexpr int NP = DW_TS / 2;
+    raw xa[NP];
+    float da[NP];
+    auto load = [&](long t0) {
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const long t = t0 + 2 * p + half;
+            const bool tok = t < tend;
+            da[p] = tok && e < E ? dl[t * E + e] : 0.0f;
+            xa[p] = raw{};
+            if (tok && i < d) xa[p] = Quad<T>::ld(x + t * d + i);
         }
-        __syncthreads();
+    };
+    load(tbeg);
+    for (long t0 = tbeg; t0 < tend; t0 += DW_TS) {
+        raw xc[NP];
+        float dc[NP];
+#pragma unroll
+        for (int p = 0; p < NP; ++p) xc[p] = xa[p], dc[p] = da[p];
+        if (t0 + DW_TS < tend) load(t0 + DW_TS);
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+#pragma unroll
+            for (int j = 0; j < DW_FT; ++j)
+                acc[j] = __builtin_amdgcn_mfma_f32_32x32x2f32(Quad<T>::get(xc[p], j), dc[p],
+                                                             acc[j], 0, 0, 0);
     }
-    const int i = i0 + il;
-    if (i >= d) return;
+    // acc[j][v]: row m = (v/4)*8 + half*4 + v%4 of tile j = feature fbase + 4m + j
+    if (e >= E) return;
+    float* out = partial + c * (long)d * E;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const int e = eg * 8 + q;
-        if (e < E) partial[(c * d + i) * E + e] = acc[q];
-    }
+    for (int j = 0; j < DW_FT; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int fi = fbase + 4 * ((v >> 2) * 8 + half * 4 + (v & 3)) + j;
+            if (fi < d) out[(long)fi * E + e] = acc[j][v];
+        }
 }
 
+// dWg[q] = sum over chunks c in increasing order of partial[c][q], regrouped:
+// thread (g, column) sums chunks g, g+16, ... of 4 consecutive outputs, then
+// the 16 group sums are added in order g = 0..15.  Same order every run.
+constexpr int DW_RG = 16;
+
 template <typename T>
-__global__ void gate_dwg_reduce_kernel(const float* __restrict__ partial,
-                                       int nchunk, long n, T* __restrict__ dWg) {
-    const long q = (long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (q >= n) return;
-    float s = 0.0f;
-    for (int c = 0; c < nchunk; ++c) s += partial[(long)c * n + q];
-    Elem<T>::st(dWg + q, s);
+__global__ __launch_bounds__(256) void gate_dwg_reduce_kernel(const float* __restrict__ partial,
+                                                              int nchunk, long n,
+                                                              T* __restrict__ dWg) {
+    __shared__ f32x4 part[DW_RG][256 / DW_RG];
+    const int g = threadIdx.x / (256 / DW_RG), cl = threadIdx.x % (256 / DW_RG);
+    const long q = ((long)blockIdx.x * (256 / DW_RG) + cl) * 4;    // n % 4 == 0
+    f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (q < n) {
+#pragma unroll 4
+        for (int c = g; c < nchunk; c += DW_RG)
+            s += *reinterpret_cast<const f32x4*>(partial + (long)c * n + q);
+    }
+    part[g][cl] = s;
+    __syncthreads();
+    if (g != 0 || q >= n) return;
+    f32x4 tot = part[0][cl];
+#pragma unroll
+    for (int h = 1; h < DW_RG; ++h) tot += part[h][cl];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) Elem<T>::st(dWg + q + v, tot[v]);
 }
 
 // WgT[e][i] = Wg[i][e] in fp32, so a gate column is contiguous.
@@ -392,23 +459,24 @@ moe_status launch_logits(const void* x, const void* Wg, const float* bias,
                          int Tn, int d, int E, float* logits, hipStream_t s) {
     const T* xp = static_cast<const T*>(x);
     const T* wp = static_cast<const T*>(Wg);
-    // tokens per block = MT * 256 / (TE / 4)
+    // tokens per block = MT * 256 / (TE / EPT); one expert per thread for
+    // small E keeps the grid at Tn/32 or more blocks
     if (E <= 8) {
-        dim3 g(cdiv(Tn, 128), cdiv(E, 8));
+        dim3 g(cdiv(Tn, 32), cdiv(E, 8));
         MOE_LAUNCH("gate_logits", s,
-            gate_logits_kernel<T, 8, 1><<<g, 256, 0, s>>>(xp, wp, bias, Tn, d, E, logits));
+            gate_logits_kernel<T, 8, 1, 1><<<g, 256, 0, s>>>(xp, wp, bias, Tn, d, E, logits));
     } else if (E <= 16) {
-        dim3 g(cdiv(Tn, 64), cdiv(E, 16));
+        dim3 g(cdiv(Tn, 16), cdiv(E, 16));
         MOE_LAUNCH("gate_logits", s,
-            gate_logits_kernel<T, 16, 1><<<g, 256, 0, s>>>(xp, wp, bias, Tn, d, E, logits));
+            gate_logits_kernel<T, 16, 1, 1><<<g, 256, 0, s>>>(xp, wp, bias, Tn, d, E, logits));
     } else if (E <= 32) {
-        dim3 g(cdiv(Tn, 64), cdiv(E, 32));
+        dim3 g(cdiv(Tn, 16), cdiv(E, 32));
         MOE_LAUNCH("gate_logits", s,
-            gate_logits_kernel<T, 32, 2><<<g, 256, 0, s>>>(xp, wp, bias, Tn, d, E, logits));
+            gate_logits_kernel<T, 32, 2, 1><<<g, 256, 0, s>>>(xp, wp, bias, Tn, d, E, logits));
     } else {
-        dim3 g(cdiv(Tn, 32), cdiv(E, 64));
+        dim3 g(cdiv(Tn, 16), cdiv(E, 64));
         MOE_LAUNCH("gate_logits", s,
-            gate_logits_kernel<T, 64, 2><<<g, 256, 0, s>>>(xp, wp, bias, Tn, d, E, logits));
+            gate_logits_kernel<T, 64, 4, 1><<<g, 256, 0, s>>>(xp, wp, bias, Tn, d, E, logits));
     }
     return launch_status();
 }
@@ -436,19 +504,19 @@ moe_status launch_topk(const float* logits, int Tn, int E, int k, int renorm,
     return launch_status();
 }
 
-int threads_per_feature(int E) {
-    int need = (E + 7) / 8, tpi = 1;
-    while (tpi < need) tpi *= 2;
-    return tpi;
-}
-
-// Tokens per dWg chunk: enough chunks that chunks x feature tiles gives
-// about 512 workgroups, each chunk a multiple of 64 tokens, at most 4096.
-int gate_chunk(int Tn, int d, int E) {
-    const int ntile = cdiv(d, 256 / threads_per_feature(E));
-    const int want = max(1, 512 / ntile);
-    int tc = cdiv(cdiv(Tn, want), 64) * 64;
-    return min(4096, max(64, tc));
+// dWg work split: feature groups of 32*DW_FT, expert tiles of 32, and token
+// chunks (multiples of DW_TS) so that the grid holds about 1024 waves.
+struct DwgSplit {
+    int nft, net, tc, nchunk;
+};
+DwgSplit dwg_split(int Tn, int d, int E) {
+    DwgSplit z;
+    z.nft = cdiv(d, 32 * DW_FT);
+    z.net = cdiv(E, 32);
+    const int want = max(1, 1024 / (z.nft * z.net));
+    z.tc = max(DW_TS, cdiv(cdiv(max(Tn, 1), want), DW_TS) * DW_TS);
+    z.nchunk = max(1, cdiv(Tn, z.tc));
+    return z;
 }
 
 struct GateBwdWs {
@@ -457,7 +525,7 @@ struct GateBwdWs {
 
 GateBwdWs gate_bwd_layout(int Tn, int d, int E) {
     GateBwdWs w;
-    const size_t nchunk = (size_t)cdiv(Tn, gate_chunk(Tn, d, E));
+    const size_t nchunk = (size_t)dwg_split(Tn, d, E).nchunk;
     w.dl = 0;
     w.wgt = align_up(w.dl + sizeof(float) * (size_t)Tn * E, 256);
     w.partial = align_up(w.wgt + sizeof(float) * (size_t)E * d, 256);
@@ -480,25 +548,23 @@ moe_status launch_gate_bwd(const void* x, const void* Wg, const float* logits,
     MOE_LAUNCH("gate_transpose", s,
         gate_transpose_kernel<T><<<cdiv((long)d * E, 256), 256, 0, s>>>(
             static_cast<const T*>(Wg), d, E, wgt));
-    MOE_LAUNCH("gate_dlogits", s,
-        gate_dlogits_kernel<<<cdiv(Tn, 4), 256, sizeof(int) * 4 * (size_t)E, s>>>(
-            logits, idx, w, dw, Tn, E, k, renorm, dl));
-    const int tpi = threads_per_feature(E);
-    const int iw = 256 / tpi;
-    const int tc = gate_chunk(Tn, d, E);
-    const int nchunk = cdiv(Tn, tc);
-    dim3 g(nchunk, cdiv(d, iw));
-    const size_t lds = sizeof(float) * (size_t)GB_TS * (iw + E);
+    if (Tn > 0)
+        MOE_LAUNCH("gate_dlogits", s,
+            gate_dlogits_kernel<<<cdiv(Tn, 4), 256, sizeof(int) * 4 * (size_t)E, s>>>(
+                logits, idx, w, dw, Tn, E, k, renorm, dl));
+    const DwgSplit z = dwg_split(Tn, d, E);
+    dim3 g(cdiv(z.nft, 4), z.net, z.nchunk);
     MOE_LAUNCH("gate_dwg_partial", s,
-        gate_dwg_partial_kernel<T><<<g, 256, lds, s>>>(xp, dl, Tn, d, E, tpi, tc, partial));
+        gate_dwg_partial_kernel<T><<<g, 256, 0, s>>>(xp, dl, Tn, d, E, z.tc, z.nft, partial));
     const long n = (long)d * E;
     MOE_LAUNCH("gate_dwg_reduce", s,
-        gate_dwg_reduce_kernel<T><<<cdiv(n, 256), 256, 0, s>>>(
-            partial, nchunk, n, static_cast<T*>(dWg)));
+        gate_dwg_reduce_kernel<T><<<cdiv(n / 4, 256 / DW_RG), 256, 0, s>>>(
+            partial, z.nchunk, n, static_cast<T*>(dWg)));
     const size_t lds_dx = renorm ? sizeof(float) * 2 * (size_t)k : sizeof(float) * (size_t)E;
-    MOE_LAUNCH("gate_dx", s,
-        gate_dx_kernel<T><<<Tn, 256, lds_dx + 16, s>>>(wgt, dl, idx, w, dw, d, E, k,
-                                                        renorm, static_cast<T*>(dx)));
+    if (Tn > 0)     // no tokens: dWg is zero (one empty chunk), dx is empty
+        MOE_LAUNCH("gate_dx", s,
+            gate_dx_kernel<T><<<Tn, 256, lds_dx + 16, s>>>(wgt, dl, idx, w, dw, d, E, k,
+                                                            renorm, static_cast<T*>(dx)));
     return launch_status();
 }
 
@@ -544,6 +610,7 @@ moe_status moe_gate_topk_bwd(const void* x, const void* Wg, const float* logits,
     const int vec = dt == MOE_BF16 ? 8 : 4;
     MOE_CHECK_ARG(d % vec == 0);
     MOE_CHECK_ARG(x && Wg && logits && topk_idx && topk_w && d_topk_w && dWg);
+    MOE_CHECK_ARG(aligned16(x));
     MOE_CHECK_ARG(T == 0 || dx);
     MOE_CHECK_ARG(dx == nullptr || aligned16(dx));
     if (ws_bytes < moe_gate_bwd_workspace_bytes(T, d, E) || !ws) return MOE_ERR_WORKSPACE;

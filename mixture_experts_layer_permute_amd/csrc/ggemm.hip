@@ -49,21 +49,73 @@ struct GemmArgs {
     const int32_t* offsets;      // [E+1]
     const int32_t* tile_prefix;  // [E+1] per-expert prefix of M tiles (RAGGED_M)
     const int32_t* order;        // [E] experts heaviest first (RAGGED_K)
+    const int32_t* full_prefix;  // [E+1] per-expert prefix of full M tiles
+    const int32_t* part_list;    // experts with a partial last tile; count at [E]
     int E, M, N, K, Ksplit;
     int nM, nN;
+    int part_mode;       // RAGGED_M: 0 all row tiles, 1 full tiles only,
+                         // 2 partial tiles cut into BM-row slices
+    int bm_plan;         // row tile of the plan (part_mode 2)
+    int xcd_run;         // logical tiles per XCD run (block -> tile remap)
 };
 
 // ------------------------------------------------------------ epilogues
 
-__device__ __forceinline__ float gelu_f(float z) {
+// fp32 tensors: the library erff / expf and an IEEE division.
+__device__ __forceinline__ float gelu_exact(float z) {
     return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
 }
-__device__ __forceinline__ float gelu_grad_f(float z) {
+__device__ __forceinline__ float gelu_grad_exact(float z) {
     const float cdf = 0.5f * (1.0f + erff(z * 0.70710678118654752f));
     const float pdf = 0.3989422804014327f * expf(-0.5f * z * z);
     return cdf + z * pdf;
 }
-__device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + expf(-z)); }
+__device__ __forceinline__ float sigmoid_exact(float z) { return 1.0f / (1.0f + expf(-z)); }
+
+// bf16 tensors (results rounded to 8 significant bits): the standard normal
+// CDF from the rational approximation of erf in Abramowitz & Stegun,
+// Handbook of Mathematical Functions, formula 7.1.26 (after Hastings):
+// erfc(x) ~= t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-x^2),
+// t = 1 / (1 + p x), x >= 0, absolute error at most 1.5e-7.  With
+// x = |z| / sqrt(2) the factor exp(-x^2) = exp(-z^2/2) is also the unscaled
+// normal density, so one hardware exp2 serves both Phi(z) and phi(z).
+struct NormCP {
+    float cdf, pdf;
+};
+__device__ __forceinline__ NormCP norm_fast(float z) {
+    constexpr float P = 0.3275911f;
+    constexpr float A1 = 0.254829592f, A2 = -0.284496736f, A3 = 1.421413741f,
+                    A4 = -1.453152027f, A5 = 1.061405429f;
+    const float x = fabsf(z) * 0.70710678118654752f;
+    const float t = __builtin_amdgcn_rcpf(fmaf(P, x, 1.0f));
+    const float poly = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, A5, A4), A3), A2), A1);
+    const float g = __builtin_amdgcn_exp2f(z * z * -0.72134752044448170f);  // e^(-z^2/2)
+    const float tail = 0.5f * poly * g;                                       // Q(|z|)
+    return {z >= 0.0f ? 1.0f - tail : tail, 0.3989422804014327f * g};
+}
+__device__ __forceinline__ float sigmoid_fast(float z) {
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
+}
+
+template <typename T>
+__device__ __forceinline__ float gelu_f(float z) {
+    if constexpr (sizeof(T) == 2) return z * norm_fast(z).cdf;
+    else return gelu_exact(z);
+}
+template <typename T>
+__device__ __forceinline__ float gelu_grad_f(float z) {
+    if constexpr (sizeof(T) == 2) {
+        const NormCP n = norm_fast(z);
+        return fmaf(z, n.pdf, n.cdf);
+    } else {
+        return gelu_grad_exact(z);
+    }
+}
+template <typename T>
+__device__ __forceinline__ float sigmoid_f(float z) {
+    if constexpr (sizeof(T) == 2) return sigmoid_fast(z);
+    else return sigmoid_exact(z);
+}
 
 template <typename T>
 struct EpiStore {            // C[e*cstride + row*ldc + col] = v
@@ -84,12 +136,12 @@ struct EpiGeluFwd {          // H = v, A = GeLU(v)
     long ld;
     __device__ __forceinline__ void operator()(int, long row, int col, float v) const {
         Elem<T>::st(H + row * ld + col, v);
-        Elem<T>::st(A + row * ld + col, gelu_f(v));
+        Elem<T>::st(A + row * ld + col, gelu_f<T>(v));
     }
     __device__ __forceinline__ void vec8(int, long row, int col, const float* v) const {
         float a[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) a[q] = gelu_f(v[q]);
+        for (int q = 0; q < 8; ++q) a[q] = gelu_f<T>(v[q]);
         Vec16<T>::st(H + row * ld + col, v);
         Vec16<T>::st(A + row * ld + col, a);
     }
@@ -104,13 +156,13 @@ struct EpiSwigluFwd {        // H1 = v1, H3 = v3 (row = [H1 | H3]), A = SiLU(v1)
                                                float v3) const {
         Elem<T>::st(H + row * 2 * f + col, v1);
         Elem<T>::st(H + row * 2 * f + f + col, v3);
-        Elem<T>::st(A + row * f + col, v1 * sigmoid_f(v1) * v3);
+        Elem<T>::st(A + row * f + col, v1 * sigmoid_f<T>(v1) * v3);
     }
     __device__ __forceinline__ void vec8(int, long row, int col, const float* v1,
                                          const float* v3) const {
         float a[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) a[q] = v1[q] * sigmoid_f(v1[q]) * v3[q];
+        for (int q = 0; q < 8; ++q) a[q] = v1[q] * sigmoid_f<T>(v1[q]) * v3[q];
         Vec16<T>::st(H + row * 2 * f + col, v1);
         Vec16<T>::st(H + row * 2 * f + f + col, v3);
         Vec16<T>::st(A + row * f + col, a);
@@ -124,13 +176,13 @@ struct EpiGeluBwd {          // dH = dA * GeLU'(H)
     long ld;
     __device__ __forceinline__ void operator()(int, long row, int col, float v) const {
         const float h = Elem<T>::ld(H + row * ld + col);
-        Elem<T>::st(dH + row * ld + col, v * gelu_grad_f(h));
+        Elem<T>::st(dH + row * ld + col, v * gelu_grad_f<T>(h));
     }
     __device__ __forceinline__ void vec8(int, long row, int col, const float* v) const {
         float h[8], o[8];
         Vec16<T>::ld(H + row * ld + col, h);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) o[q] = v[q] * gelu_grad_f(h[q]);
+        for (int q = 0; q < 8; ++q) o[q] = v[q] * gelu_grad_f<T>(h[q]);
         Vec16<T>::st(dH + row * ld + col, o);
     }
 };
@@ -143,7 +195,7 @@ struct EpiSwigluBwd {        // dH1 = dA H3 SiLU'(H1), dH3 = dA SiLU(H1)
     __device__ __forceinline__ void operator()(int, long row, int col, float v) const {
         const float h1 = Elem<T>::ld(H + row * 2 * f + col);
         const float h3 = Elem<T>::ld(H + row * 2 * f + f + col);
-        const float s = sigmoid_f(h1);
+        const float s = sigmoid_f<T>(h1);
         Elem<T>::st(dH + row * 2 * f + col, v * h3 * s * (1.0f + h1 * (1.0f - s)));
         Elem<T>::st(dH + row * 2 * f + f + col, v * h1 * s);
     }
@@ -153,7 +205,7 @@ struct EpiSwigluBwd {        // dH1 = dA H3 SiLU'(H1), dH3 = dA SiLU(H1)
         Vec16<T>::ld(H + row * 2 * f + f + col, h3);
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-            const float sg = sigmoid_f(h1[q]);
+            const float sg = sigmoid_f<T>(h1[q]);
             o1[q] = v[q] * h3[q] * sg * (1.0f + h1[q] * (1.0f - sg));
             o3[q] = v[q] * h1[q] * sg;
         }
@@ -180,7 +232,9 @@ struct TileInfo {
 // logical tiles, and logical tiles are ordered so that a run shares
 // operands: RAGGED_M in groups of GROUP_M row tiles (all N tiles of the
 // group before the next group), RAGGED_K expert by expert, row tiles
-// fastest.  Grids are padded to a multiple of 8 * XCD_RUN.
+// fastest.  Grids are padded to a multiple of 8 * XCD_RUN.  A RAGGED_M
+// launch covers all row tiles, only the full ones, or only the partial last
+// tiles of the experts, cut into BM-row slices (part_mode 0, 1, 2).
 constexpr int NXCD = 8;
 constexpr int GROUP_M = 8;
 
@@ -189,12 +243,15 @@ __device__ __forceinline__ int xcd_logical(int b, int run) {
     return ((j / run) * NXCD + x) * run + (j % run);
 }
 
-template <int MODE, int BM, int BN, int XCD_RUN, typename T>
+template <int MODE, int BM, int BN, typename T>
 __device__ __forceinline__ TileInfo decode_tile(const GemmArgs<T>& p) {
     TileInfo ti;
-    const int L = xcd_logical(blockIdx.x, XCD_RUN);
+    const int L = xcd_logical(blockIdx.x, p.xcd_run);
     if (MODE == RAGGED_M) {
-        const int total = p.tile_prefix[p.E];          // row tiles over all experts
+        const int sub = p.part_mode == 2 ? p.bm_plan / BM : 1;   // slices per partial tile
+        const int total = p.part_mode == 0 ? p.tile_prefix[p.E]
+                        : p.part_mode == 1 ? p.full_prefix[p.E]
+                                           : p.part_list[p.E] * sub;
         ti.live = L < total * p.nN;
         if (!ti.live) return ti;
         const int per_group = GROUP_M * p.nN;
@@ -202,15 +259,30 @@ __device__ __forceinline__ TileInfo decode_tile(const GemmArgs<T>& p) {
         const int gm = min(GROUP_M, total - first);
         const int w = L % per_group;
         const int mt = first + w % gm, nt = w / gm;
-        int lo = 0, hi = p.E;                 // largest e with prefix[e] <= mt
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (p.tile_prefix[mid] <= mt) lo = mid; else hi = mid;
+        if (p.part_mode == 2) {
+            const int e = p.part_list[mt / sub];
+            const int seg0 = p.offsets[e], seg1 = p.offsets[e + 1];
+            const int nfull = (seg1 - seg0) / p.bm_plan;
+            const int lo = nfull * p.bm_plan + (mt % sub) * BM;   // slice start in segment
+            ti.e = e;
+            ti.r0 = (long)seg0 + lo;
+            ti.rows = min(BM, seg1 - seg0 - lo);
+            if (ti.rows <= 0) {
+                ti.live = false;
+                return ti;
+            }
+        } else {
+            const int32_t* pre = p.part_mode == 0 ? p.tile_prefix : p.full_prefix;
+            int lo = 0, hi = p.E;                 // largest e with pre[e] <= mt
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (pre[mid] <= mt) lo = mid; else hi = mid;
+            }
+            ti.e = lo;
+            const int seg0 = p.offsets[lo], seg1 = p.offsets[lo + 1];
+            ti.r0 = (long)seg0 + (long)(mt - pre[lo]) * BM;
+            ti.rows = (int)min((long)BM, (long)seg1 - ti.r0);
         }
-        ti.e = lo;
-        const int seg0 = p.offsets[lo], seg1 = p.offsets[lo + 1];
-        ti.r0 = (long)seg0 + (long)(mt - p.tile_prefix[lo]) * BM;
-        ti.rows = (int)min((long)BM, (long)seg1 - ti.r0);
         ti.n0 = nt * BN;
         ti.m0 = 0;
         ti.kbeg = 0;
@@ -399,7 +471,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ggemm_bf16_kernel(GemmArgs<bf
     constexpr int STAGE = A_BYTES + NBT * B_BYTES;
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
 
-    const TileInfo ti = decode_tile<MODE, BM, BN, (MODE == RAGGED_M ? 32 : 8)>(p);
+    const TileInfo ti = decode_tile<MODE, BM, BN>(p);
     if (!ti.live) return;
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -569,6 +641,323 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ggemm_bf16_kernel(GemmArgs<bf
 }
 
 // =====================================================================
+// bf16 MFMA kernel, direct-to-LDS variant
+// =====================================================================
+// Operand tiles go from HBM straight into LDS with buffer_load_dwordx4 ...
+// lds (each wave instruction fills 1 KB: lane l's 16 bytes land at base +
+// 16*l), through a ring of NSTG stages of BKD reduction steps.  No register
+// staging; a stage is loaded NSTG-1 stages ahead of its use.  The stages are
+// separate LDS objects so the compiler can tell that a load into one stage
+// does not alias reads of another.
+constexpr int BKD = 32;
+constexpr int NSTG = 4;
+
+// K-major stage tile: rows of 32 bf16 (64 B), 16-byte chunks XOR-swizzled
+// by (row ^ row/4) mod 4 so that 16 consecutive rows hit distinct banks.
+__device__ __forceinline__ int swz32(int r, int c) {
+    return r * 64 + ((c ^ ((r ^ (r >> 2)) & 3)) << 4);
+}
+// M/N-major stage tile: BKD rows of ROWS elements; chunk c of row k is
+// stored at chunk c ^ 4*(k mod 4), which spreads the four rows a transposing
+// read touches over distinct banks.
+template <int ROWS>
+__device__ __forceinline__ int mnoff(int k, int c) {
+    return k * ROWS * 2 + ((c ^ ((k & 3) << 2)) << 4);
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// The four words of a raw buffer resource: base address, stride 0,
+// num_records = nbytes (clamped at 0), and the same format word as
+// make_rsrc().  Reads at offsets >= nbytes return zero.
+__device__ __forceinline__ i32x4_t rsrc_words(const bf16_t* base, long nbytes) {
+    const uint64_t a = (uint64_t)base;
+    const uint32_t n = nbytes <= 0 ? 0u : (uint32_t)nbytes;
+    return i32x4_t{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xFFFFu), (int)n, 0x00020000};
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const lds_void_t*)p;
+}
+// One wave-wide 16-byte-per-lane load from a buffer straight into LDS: lane
+// l's bytes at voff land at lds + 16*l.  Issued from inline assembly so that
+// the compiler does not tie every later LDS read to its completion; callers
+// wait on vmcnt themselves (stage_barrier) before reading the stage.
+__device__ __forceinline__ void lds_dma16(i32x4_t rs, uint32_t voff, uint32_t lds) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds"
+        :
+        : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rs)
+        : "memory", "m0");
+}
+
+template <int ROWS, int LAY, int NT>
+struct DmaOperand {
+    static constexpr int NW = NT / 64;
+    static constexpr int TILE = ROWS * BKD * 2;           // bytes per stage
+    static constexpr int NLOAD = TILE / 1024 / NW;        // 1 KB loads per wave
+    static_assert(TILE % (1024 * NW) == 0, "tile/wave mismatch");
+    static_assert(LAY == KMAJ || ROWS >= 128, "M/N-major swizzle needs 16 chunks per row");
+    static_assert(TILE >= 1024 * NW, "every wave loads at least 1 KB per stage");
+    const bf16_t* P;
+    long ld;
+    int row_lim;
+    long k_lim;
+    uint32_t off[NLOAD];
+
+    __device__ __forceinline__ void init(const bf16_t* P_, long ld_, int row_lim_,
+                                         long k_lim_) {
+        P = P_;
+        ld = ld_;
+        row_lim = row_lim_;
+        k_lim = k_lim_;
+        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+        for (int i = 0; i < NLOAD; ++i) {
+            const int blk = w + NW * i;                    // 1 KB block of the stage
+            if (LAY == KMAJ) {
+                const int row = blk * 16 + (lane >> 2);
+                const int c = (lane & 3) ^ ((row ^ (row >> 2)) & 3);
+                off[i] = (uint32_t)(row * ld * 2 + c * 16);
+            } else {
+                constexpr int NC = ROWS / 8;               // chunks per row
+                constexpr int RB = 1024 / (ROWS * 2);      // rows per block
+                const int k = blk * RB + lane / NC;
+                const int c = (lane % NC) ^ ((k & 3) << 2);
+                off[i] = c * 8 < row_lim ? (uint32_t)(k * ld * 2 + c * 16) : OOB;
+            }
+        }
+    }
+
+    __device__ __forceinline__ void dma(long k0, uint8_t* stage) const {
+        const bf16_t* base;
+        long nbytes;
+        if (LAY == KMAJ) {
+            base = P + k0;
+            nbytes = (long)row_lim * ld * 2 - k0 * 2;
+        } else {
+            base = P + k0 * ld;
+            nbytes = min((long)BKD, k_lim - k0) * ld * 2;
+        }
+        const i32x4_t rs = rsrc_words(base, nbytes);
+        const uint32_t lds0 = lds_addr(stage) + (uint32_t)((threadIdx.x >> 6) * 1024);
+#pragma unroll
+        for (int i = 0; i < NLOAD; ++i) lds_dma16(rs, off[i], lds0 + NW * i * 1024);
+    }
+};
+
+template <int ROWS, int LAY>
+__device__ __forceinline__ bf16x8 dma_frag(const uint8_t* lds, int row0, int ks, int lane) {
+    if constexpr (LAY == KMAJ) {
+        const uint4 v = *reinterpret_cast<const uint4*>(
+            lds + swz32(row0 + (lane & 31), ks * 2 + (lane >> 5)));
+        return __builtin_bit_cast(bf16x8, v);
+    } else {
+        const int k = ks * 16 + (lane >> 5) * 8 + ((lane & 15) >> 2);
+        const int col = row0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        const uint8_t* p0 = lds + mnoff<ROWS>(k, col >> 3) + (col & 7) * 2;
+        const uint8_t* p1 = lds + mnoff<ROWS>(k + 4, col >> 3) + (col & 7) * 2;
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)p0);
+        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)p1);
+        typedef short v8i16_t __attribute__((ext_vector_type(8)));
+        const v8i16_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return __builtin_bit_cast(bf16x8, v);
+    }
+}
+
+// Wait until at most N direct-to-LDS loads of this wave are in flight and
+// its LDS reads have returned, then meet the other waves of the block.
+template <int N>
+__device__ __forceinline__ void stage_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+template <int BM, int BN, int WM, int WN, int MODE, int ALAY, int BLAY, bool DUAL,
+          bool KSPLIT, class Epi>
+__global__ __launch_bounds__(64 * WM * WN, 1) void ggemm_bf16_dma_kernel(GemmArgs<bf16_t> p,
+                                                                         Epi epi) {
+    constexpr int NT = 64 * WM * WN;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int FM = WTM / 32, FN = WTN / 32;
+    constexpr int NBT = DUAL ? 2 : 1;
+    constexpr int A_BYTES = BM * BKD * 2, B_BYTES = BN * BKD * 2;
+    constexpr int STAGE = A_BYTES + NBT * B_BYTES;
+    __shared__ __attribute__((aligned(1024))) uint8_t st0[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t st1[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t st2[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t st3[STAGE];
+
+    const TileInfo ti = decode_tile<MODE, BM, BN>(p);
+    if (!ti.live) return;
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int wm = wv / WN, wn = wv % WN;
+
+    DmaOperand<BM, ALAY, NT> opA;
+    DmaOperand<BN, BLAY, NT> opB;
+    DmaOperand<BN, BLAY, NT> opB2;
+    const bf16_t* bsplit[2];
+    if (MODE == RAGGED_M) {
+        opA.init(p.A + ti.r0 * p.lda, p.lda, ti.rows, p.K);
+        const long eoff = (long)ti.e * p.bstride;
+        const long nofs = BLAY == KMAJ ? (long)ti.n0 * p.ldb : (long)ti.n0;
+        opB.init(p.B + eoff + nofs, p.ldb, p.N - ti.n0, p.K);
+        if (DUAL) opB2.init(p.B2 + eoff + nofs, p.ldb, p.N - ti.n0, p.K);
+        if (KSPLIT) bsplit[0] = opB.P, bsplit[1] = p.B2 + eoff + nofs;
+    } else {
+        opA.init(p.A + ti.kbeg * p.lda + ti.m0, p.lda, p.M - ti.m0, ti.klen);
+        opB.init(p.B + ti.kbeg * p.ldb + ti.n0, p.ldb, p.N - ti.n0, ti.klen);
+    }
+    constexpr int NL = DmaOperand<BM, ALAY, NT>::NLOAD + NBT * DmaOperand<BN, BLAY, NT>::NLOAD;
+
+    f32x16 acc[FM][FN];
+    f32x16 acc2[DUAL ? FM : 1][DUAL ? FN : 1];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    if constexpr (DUAL) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc2[i][j][v] = 0.0f;
+    }
+
+    auto issue = [&](uint8_t* stg, int j) {
+        const long k0 = (long)j * BKD;
+        opA.dma(k0, stg);
+        if constexpr (KSPLIT) {
+            const bool hi = k0 >= p.Ksplit;
+            opB.P = bsplit[hi];
+            opB.dma(hi ? k0 - p.Ksplit : k0, stg + A_BYTES);
+        } else {
+            opB.dma(k0, stg + A_BYTES);
+        }
+        if constexpr (DUAL) opB2.dma(k0, stg + A_BYTES + B_BYTES);
+    };
+    auto compute = [&](const uint8_t* stg) {
+        const uint8_t* sA = stg;
+        const uint8_t* sB = stg + A_BYTES;
+        const uint8_t* sB2 = sB + B_BYTES;
+        bf16x8 af[2][FM], bfr[2][FN], bf2[2][DUAL ? FN : 1];
+        auto read_frags = [&](int ks, int buf) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                af[buf][i] = dma_frag<BM, ALAY>(sA, wm * WTM + i * 32, ks, lane);
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                bfr[buf][j] = dma_frag<BN, BLAY>(sB, wn * WTN + j * 32, ks, lane);
+            if constexpr (DUAL) {
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    bf2[buf][j] = dma_frag<BN, BLAY>(sB2, wn * WTN + j * 32, ks, lane);
+            }
+        };
+        read_frags(0, 0);
+#pragma unroll
+        for (int ks = 0; ks < BKD / 16; ++ks) {
+            const int cb = ks & 1;
+            if (ks + 1 < BKD / 16) read_frags(ks + 1, cb ^ 1);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        af[cb][i], bfr[cb][j], acc[i][j], 0, 0, 0);
+            if constexpr (DUAL) {
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        acc2[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            af[cb][i], bf2[cb][j], acc2[i][j], 0, 0, 0);
+            }
+        }
+    };
+    // one step of the ring: wait for stage j, publish it, refill the stage
+    // freed by step j-1 with sub-tile j+3, multiply stage j
+    const int nj = (ti.klen + BKD - 1) / BKD;
+    auto step = [&](uint8_t* cur, uint8_t* refill, int j) {
+        const int ahead = min(nj - 1 - j, NSTG - 2);      // later sub-tiles in flight
+        if (ahead >= 2) stage_barrier<2 * NL>();
+        else if (ahead == 1) stage_barrier<NL>();
+        else stage_barrier<0>();
+        if (j + NSTG - 1 < nj) issue(refill, j + NSTG - 1);
+        compute(cur);
+    };
+    auto ring = [&](int q) -> uint8_t* {
+        return q == 0 ? st0 : q == 1 ? st1 : q == 2 ? st2 : st3;
+    };
+    if (nj > 0) issue(st0, 0);
+    if (nj > 1) issue(st1, 1);
+    if (nj > 2) issue(st2, 2);
+#pragma unroll 1
+    for (int j = 0; j < nj; ++j)
+        step(ring(j & 3), ring((j + 3) & 3), j);
+    __syncthreads();
+
+    // ---- epilogue through LDS (same scheme as the register kernel)
+    constexpr int LDW = WTN + 4;
+    constexpr int SLAB = 16 * LDW;                   // floats per wave half-slab
+    constexpr int WPS = STAGE / (SLAB * NBT * 4);    // wave slabs per stage array
+    static_assert(WPS * NSTG >= NT / 64, "epilogue slabs do not fit");
+    uint8_t* home = wv / WPS == 0 ? st0 : wv / WPS == 1 ? st1 : wv / WPS == 2 ? st2 : st3;
+    float* slab = reinterpret_cast<float*>(home) + (wv % WPS) * SLAB * NBT;
+    constexpr int LPR = WTN / 8;
+    constexpr int RPP = 64 / LPR;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int vv = 0; vv < 8; ++vv) {
+                    const int v = h * 8 + vv;
+                    const int r = (vv >> 2) * 8 + (lane >> 5) * 4 + (vv & 3);
+                    slab[r * LDW + j * 32 + (lane & 31)] = acc[i][j][v];
+                    if constexpr (DUAL)
+                        slab[SLAB + r * LDW + j * 32 + (lane & 31)] = acc2[i][j][v];
+                }
+            __syncthreads();
+#pragma unroll 1
+            for (int ps = 0; ps < 16 / RPP; ++ps) {
+                const int r = ps * RPP + lane / LPR;
+                const int c0 = (lane % LPR) * 8;
+                const int rl = wm * WTM + i * 32 + h * 16 + r;
+                const int col = ti.n0 + wn * WTN + c0;
+                const float* src = &slab[r * LDW + c0];
+                float v[8];
+                *reinterpret_cast<float4*>(v) = *reinterpret_cast<const float4*>(src);
+                *reinterpret_cast<float4*>(v + 4) = *reinterpret_cast<const float4*>(src + 4);
+                const bool ok =
+                    col < p.N && (MODE == RAGGED_M ? rl < ti.rows : ti.m0 + rl < p.M);
+                if (ok) {
+                    if constexpr (DUAL) {
+                        float v3[8];
+                        *reinterpret_cast<float4*>(v3) =
+                            *reinterpret_cast<const float4*>(src + SLAB);
+                        *reinterpret_cast<float4*>(v3 + 4) =
+                            *reinterpret_cast<const float4*>(src + SLAB + 4);
+                        epi.vec8(ti.e, ti.r0 + rl, col, v, v3);
+                    } else if (MODE == RAGGED_M) {
+                        epi.vec8(ti.e, ti.r0 + rl, col, v);
+                    } else {
+                        epi.vec8(ti.e, (long)ti.m0 + rl, col, v);
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// =====================================================================
 // fp32 SIMT kernel (correctness path for fp32 layers)
 // =====================================================================
 
@@ -579,7 +968,7 @@ __global__ __launch_bounds__(256) void ggemm_f32_kernel(GemmArgs<float> p, Epi e
     __shared__ float sA[FK][FB + 4];
     __shared__ float sB[FK][FB + 4];
     __shared__ float sB2[DUAL ? FK : 1][FB + 4];
-    const TileInfo ti = decode_tile<MODE, FB, FB, 1>(p);
+    const TileInfo ti = decode_tile<MODE, FB, FB>(p);
     if (!ti.live) return;
     const int tid = threadIdx.x, tm = tid / 16, tn = tid % 16;
     float acc[4][4], acc2[4][4];
@@ -673,18 +1062,25 @@ __global__ __launch_bounds__(256) void ggemm_f32_kernel(GemmArgs<float> p, Epi e
 __global__ __launch_bounds__(1024) void ffn_plan_kernel(const int32_t* __restrict__ offsets,
                                                         int E, int bm,
                                                         int32_t* __restrict__ tile_prefix,
-                                                        int32_t* __restrict__ order) {
+                                                        int32_t* __restrict__ order,
+                                                        int32_t* __restrict__ full_prefix,
+                                                        int32_t* __restrict__ part_list) {
     __shared__ int cnt[1024];
     const int e = threadIdx.x;
     if (e < E) cnt[e] = offsets[e + 1] - offsets[e];
     __syncthreads();
     if (e == 0) {
-        int run = 0;
+        int run = 0, full = 0, np = 0;
         for (int q = 0; q < E; ++q) {
             tile_prefix[q] = run;
+            full_prefix[q] = full;
             run += (cnt[q] + bm - 1) / bm;
+            full += cnt[q] / bm;
+            if (cnt[q] % bm) part_list[np++] = q;
         }
         tile_prefix[E] = run;
+        full_prefix[E] = full;
+        part_list[E] = np;
     }
     if (e < E) {
         const int c = cnt[e];
@@ -702,14 +1098,16 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(const int32_t* __restric
 constexpr int BM_BF16 = 256;
 
 struct FfnWs {
-    size_t prefix, order, dh, total;
+    size_t prefix, order, full, part, dh, total;
 };
 
 FfnWs ffn_layout(int R, int E, int f, moe_act act, moe_dtype dt, int backward) {
     FfnWs w;
     w.prefix = 0;
     w.order = align_up(sizeof(int32_t) * (E + 1), 256);
-    w.dh = align_up(w.order + sizeof(int32_t) * E, 256);
+    w.full = align_up(w.order + sizeof(int32_t) * E, 256);
+    w.part = align_up(w.full + sizeof(int32_t) * (E + 1), 256);
+    w.dh = align_up(w.part + sizeof(int32_t) * (E + 1), 256);
     size_t dh = 0;
     if (backward) {
         const size_t es = dt == MOE_BF16 ? 2 : 4;
@@ -719,28 +1117,39 @@ FfnWs ffn_layout(int R, int E, int f, moe_act act, moe_dtype dt, int backward) {
     return w;
 }
 
-template <int BM, int BN, int WM, int WN, int MODE, int ALAY, int BLAY, bool DUAL,
+template <int BM, int BN, int WM, int WN, bool DMA, int MODE, int ALAY, int BLAY, bool DUAL,
           bool KSPLIT, class Epi>
 void launch_bf16(GemmArgs<bf16_t> p, Epi epi, int R, hipStream_t s, const char* name) {
     p.nN = (p.N + BN - 1) / BN;
     int blocks;
     if (MODE == RAGGED_M) {
-        blocks = ((R + BM - 1) / BM + p.E) * p.nN;
+        // row tiles at most: all < ceil(R/BM) + E, full <= R/BM, partial <= min(E, R)
+        const int rt = p.part_mode == 0 ? (R + BM - 1) / BM + p.E
+                     : p.part_mode == 1 ? R / BM
+                                        : min(p.E, R) * (p.bm_plan / BM);
+        blocks = rt * p.nN;
     } else {
         p.nM = (p.M + BM - 1) / BM;
         blocks = p.E * p.nM * p.nN;
     }
     if (blocks <= 0) return;
-    const int pad = NXCD * (MODE == RAGGED_M ? 32 : 8);   // whole XCD runs
+    if (p.xcd_run <= 0) p.xcd_run = MODE == RAGGED_M ? 32 : 8;
+    const int pad = NXCD * p.xcd_run;                      // whole XCD runs
     blocks = (blocks + pad - 1) / pad * pad;
-    MOE_LAUNCH(name, s,
-               ggemm_bf16_kernel<BM, BN, WM, WN, MODE, ALAY, BLAY, DUAL, KSPLIT, Epi>
-               <<<blocks, 64 * WM * WN, 0, s>>>(p, epi));
+    if constexpr (DMA)
+        MOE_LAUNCH(name, s,
+                   ggemm_bf16_dma_kernel<BM, BN, WM, WN, MODE, ALAY, BLAY, DUAL, KSPLIT, Epi>
+                   <<<blocks, 64 * WM * WN, 0, s>>>(p, epi));
+    else
+        MOE_LAUNCH(name, s,
+                   ggemm_bf16_kernel<BM, BN, WM, WN, MODE, ALAY, BLAY, DUAL, KSPLIT, Epi>
+                   <<<blocks, 64 * WM * WN, 0, s>>>(p, epi));
 }
 
 template <int MODE, int ALAY, int BLAY, bool DUAL, bool KSPLIT, class Epi>
 void launch_f32(GemmArgs<float> p, Epi epi, int R, hipStream_t s, const char* name) {
     p.nN = (p.N + FB - 1) / FB;
+    p.xcd_run = 1;
     int blocks;
     if (MODE == RAGGED_M) {
         blocks = ((R + FB - 1) / FB + p.E) * p.nN;
@@ -752,25 +1161,56 @@ void launch_f32(GemmArgs<float> p, Epi epi, int R, hipStream_t s, const char* na
     MOE_LAUNCH(name, s, ggemm_f32_kernel<MODE, ALAY, BLAY, DUAL, KSPLIT, Epi><<<blocks, 256, 0, s>>>(p, epi));
 }
 
+struct Plan {
+    const int32_t *prefix, *order, *full, *part;
+};
+
 template <typename T>
-GemmArgs<T> base_args(const int32_t* offsets, const int32_t* prefix,
-                      const int32_t* order, int E) {
+GemmArgs<T> base_args(const int32_t* offsets, const Plan& pl, int E) {
     GemmArgs<T> p = {};
     p.offsets = offsets;
-    p.tile_prefix = prefix;
-    p.order = order;
+    p.tile_prefix = pl.prefix;
+    p.order = pl.order;
+    p.full_prefix = pl.full;
+    p.part_list = pl.part;
     p.E = E;
+    p.part_mode = 0;
+    p.bm_plan = 0;
+    p.xcd_run = 0;
     return p;
 }
 
 // Tile configuration of the bf16 path: block tile and wave grid for the
-// single-product GEMMs, and for the dual-weight (SwiGLU up) product.
-template <int BM_, int BN_, int WM_, int WN_, int BND_, int WMD_, int WND_>
+// single-product GEMMs, for the dual-weight (SwiGLU up) product, and for the
+// tail launch of a split RAGGED_M product (BMT = 0: never split), in a wide
+// (BNT) and a narrow (BNN) column variant.
+template <int BM_, int BN_, int WM_, int WN_, int BND_, int WMD_, int WND_, bool DMA_ = false,
+          int BMT_ = 0, int BNT_ = 0, int WMT_ = 0, int WNT_ = 0, int BNN_ = 0, int WNN_ = 0>
 struct TileCfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
     static constexpr int BND = BND_, WMD = WMD_, WND = WND_;
+    static constexpr bool DMA = DMA_;     // direct-to-LDS ring instead of register staging
+    static constexpr int BMT = BMT_, BNT = BNT_, WMT = WMT_, WNT = WNT_;
+    static constexpr int BNN = BNN_, WNN = WNN_;
 };
-using DefaultCfg = TileCfg<256, 256, 4, 2, 128, 4, 2>;
+using DefaultCfg = TileCfg<256, 256, 2, 4, 128, 2, 4, true, 64, 256, 1, 4, 128, 4>;
+
+// Wave quantisation.  A RAGGED_M product has between ceil(R/BM) and
+// ceil(R/BM) + E - 1 row tiles, since each expert's last tile is usually
+// partial; with nN column tiles per row tile the last round of workgroups
+// is often nearly empty (e.g. 72 x 4 tiles on 256 compute units: two rounds
+// for 1.125 rounds of work), and the partial tiles cost as much as full
+// ones.  Split: one launch multiplies the full row tiles of all experts,
+// a second one only the partial last tiles, cut into BMT-row slices (empty
+// slices exit at once) with BNT-wide columns, or BNN-wide ones when the
+// wide tail would leave most compute units idle, spread over all XCDs.
+// Every output element is still one fixed-order sum over k: identical
+// results.
+inline int xcd_run_for(long tiles) {
+    int run = 1;
+    while (run < 32 && (long)run * 2 * NXCD <= tiles) run *= 2;
+    return run;
+}
 
 template <typename T, class Cfg>
 struct Launch;
@@ -778,13 +1218,37 @@ struct Launch;
 template <class Cfg>
 struct Launch<bf16_t, Cfg> {
     template <int MODE, int ALAY, int BLAY, bool DUAL, bool KSPLIT, class Epi>
-    static void go(GemmArgs<bf16_t> p, Epi epi, int R, hipStream_t s, const char* name) {
-        if constexpr (DUAL)
-            launch_bf16<Cfg::BM, Cfg::BND, Cfg::WMD, Cfg::WND, MODE, ALAY, BLAY, DUAL, KSPLIT>(
-                p, epi, R, s, name);
-        else
-            launch_bf16<Cfg::BM, Cfg::BN, Cfg::WM, Cfg::WN, MODE, ALAY, BLAY, DUAL, KSPLIT>(
-                p, epi, R, s, name);
+    static void go(GemmArgs<bf16_t> p, Epi epi, int R, hipStream_t s, const char* name,
+                   const char* tail_name = nullptr) {
+        if constexpr (DUAL) {
+            launch_bf16<Cfg::BM, Cfg::BND, Cfg::WMD, Cfg::WND, Cfg::DMA, MODE, ALAY, BLAY, DUAL,
+                        KSPLIT>(p, epi, R, s, name);
+        } else {
+            if constexpr (MODE == RAGGED_M && Cfg::BMT > 0) {
+                if (tail_name) {
+                    GemmArgs<bf16_t> q = p;
+                    q.part_mode = 1;
+                    q.bm_plan = Cfg::BM;
+                    launch_bf16<Cfg::BM, Cfg::BN, Cfg::WM, Cfg::WN, Cfg::DMA, MODE, ALAY, BLAY,
+                                DUAL, KSPLIT>(q, epi, R, s, name);
+                    q.part_mode = 2;
+                    // expected live slices: about half of the slots of the partial tiles
+                    const long slices = (long)min(p.E, R) * (Cfg::BM / Cfg::BMT) / 2;
+                    if (Cfg::BNN > 0 && slices * cdiv(p.N, Cfg::BNT) < device_cus()) {
+                        q.xcd_run = xcd_run_for(slices * cdiv(p.N, Cfg::BNN));
+                        launch_bf16<Cfg::BMT, Cfg::BNN, Cfg::WMT, Cfg::WNN, Cfg::DMA, MODE,
+                                    ALAY, BLAY, DUAL, KSPLIT>(q, epi, R, s, tail_name);
+                    } else {
+                        q.xcd_run = xcd_run_for(slices * cdiv(p.N, Cfg::BNT));
+                        launch_bf16<Cfg::BMT, Cfg::BNT, Cfg::WMT, Cfg::WNT, Cfg::DMA, MODE,
+                                    ALAY, BLAY, DUAL, KSPLIT>(q, epi, R, s, tail_name);
+                    }
+                    return;
+                }
+            }
+            launch_bf16<Cfg::BM, Cfg::BN, Cfg::WM, Cfg::WN, Cfg::DMA, MODE, ALAY, BLAY, DUAL,
+                        KSPLIT>(p, epi, R, s, name);
+        }
     }
     static constexpr int BM = Cfg::BM;
 };
@@ -792,7 +1256,8 @@ struct Launch<bf16_t, Cfg> {
 template <class Cfg>
 struct Launch<float, Cfg> {
     template <int MODE, int ALAY, int BLAY, bool DUAL, bool KSPLIT, class Epi>
-    static void go(GemmArgs<float> p, Epi epi, int R, hipStream_t s, const char* name) {
+    static void go(GemmArgs<float> p, Epi epi, int R, hipStream_t s, const char* name,
+                   const char* = nullptr) {
         launch_f32<MODE, ALAY, BLAY, DUAL, KSPLIT>(p, epi, R, s, name);
     }
     static constexpr int BM = FB;
@@ -807,32 +1272,36 @@ moe_status ffn_fwd(const void* x_perm, const int32_t* offsets, int R, int E,
     char* base = static_cast<char*>(ws);
     int32_t* prefix = reinterpret_cast<int32_t*>(base + L.prefix);
     int32_t* order = reinterpret_cast<int32_t*>(base + L.order);
+    int32_t* full = reinterpret_cast<int32_t*>(base + L.full);
+    int32_t* part = reinterpret_cast<int32_t*>(base + L.part);
+    const Plan pl{prefix, order, full, part};
     MOE_LAUNCH("ffn_plan", s,
-               ffn_plan_kernel<<<1, 1024, 0, s>>>(offsets, E, Launch<T, Cfg>::BM, prefix, order));
+               ffn_plan_kernel<<<1, 1024, 0, s>>>(offsets, E, Launch<T, Cfg>::BM, prefix,
+                                                  order, full, part));
 
     const T* xp = static_cast<const T*>(x_perm);
     T* H = static_cast<T*>(h_save);
     T* A = static_cast<T*>(a_save);
     // GEMM1 (+ activation): [R,d] x W1[e] [d,f]
-    GemmArgs<T> p = base_args<T>(offsets, prefix, order, E);
+    GemmArgs<T> p = base_args<T>(offsets, pl, E);
     p.A = xp; p.lda = d;
     p.B = static_cast<const T*>(W1); p.ldb = f; p.bstride = (long)d * f;
     p.N = f; p.K = d;
     if (act == MOE_ACT_GELU) {
         Launch<T, Cfg>::template go<RAGGED_M, KMAJ, MNMAJ, false, false>(
-            p, EpiGeluFwd<T>{H, A, f}, R, s, "gemm_up_gelu");
+            p, EpiGeluFwd<T>{H, A, f}, R, s, "gemm_up_gelu", "gemm_up_gelu_tail");
     } else {
         p.B2 = static_cast<const T*>(W3);
         Launch<T, Cfg>::template go<RAGGED_M, KMAJ, MNMAJ, true, false>(
             p, EpiSwigluFwd<T>{H, A, f}, R, s, "gemm_up_swiglu");
     }
     // GEMM2: A [R,f] x W2[e] [f,d]
-    GemmArgs<T> q = base_args<T>(offsets, prefix, order, E);
+    GemmArgs<T> q = base_args<T>(offsets, pl, E);
     q.A = A; q.lda = f;
     q.B = static_cast<const T*>(W2); q.ldb = d; q.bstride = (long)f * d;
     q.N = d; q.K = f;
     Launch<T, Cfg>::template go<RAGGED_M, KMAJ, MNMAJ, false, false>(
-        q, EpiStore<T>{static_cast<T*>(out_perm), d, 0}, R, s, "gemm_down");
+        q, EpiStore<T>{static_cast<T*>(out_perm), d, 0}, R, s, "gemm_down", "gemm_down_tail");
     return launch_status();
 }
 
@@ -846,29 +1315,35 @@ moe_status ffn_bwd(const void* d_out, const void* x_perm, const void* h_save,
     char* base = static_cast<char*>(ws);
     int32_t* prefix = reinterpret_cast<int32_t*>(base + L.prefix);
     int32_t* order = reinterpret_cast<int32_t*>(base + L.order);
+    int32_t* full = reinterpret_cast<int32_t*>(base + L.full);
+    int32_t* part = reinterpret_cast<int32_t*>(base + L.part);
+    const Plan pl{prefix, order, full, part};
     T* dH = reinterpret_cast<T*>(base + L.dh);
     const bool sw = act == MOE_ACT_SWIGLU;
     const long ldh = sw ? 2L * f : (long)f;
     MOE_LAUNCH("ffn_plan", s,
-               ffn_plan_kernel<<<1, 1024, 0, s>>>(offsets, E, Launch<T, Cfg>::BM, prefix, order));
+               ffn_plan_kernel<<<1, 1024, 0, s>>>(offsets, E, Launch<T, Cfg>::BM, prefix,
+                                                  order, full, part));
 
     const T* dO = static_cast<const T*>(d_out);
     // dA = dO W2[e]^T with the activation derivative in the epilogue -> dH
     {
-        GemmArgs<T> p = base_args<T>(offsets, prefix, order, E);
+        GemmArgs<T> p = base_args<T>(offsets, pl, E);
         p.A = dO; p.lda = d;
         p.B = static_cast<const T*>(W2); p.ldb = d; p.bstride = (long)f * d;
         p.N = f; p.K = d;
         if (!sw)
             Launch<T, Cfg>::template go<RAGGED_M, KMAJ, KMAJ, false, false>(
-                p, EpiGeluBwd<T>{static_cast<const T*>(h_save), dH, f}, R, s, "gemm_dA_gelu");
+                p, EpiGeluBwd<T>{static_cast<const T*>(h_save), dH, f}, R, s, "gemm_dA_gelu",
+                "gemm_dA_gelu_tail");
         else
             Launch<T, Cfg>::template go<RAGGED_M, KMAJ, KMAJ, false, false>(
-                p, EpiSwigluBwd<T>{static_cast<const T*>(h_save), dH, f}, R, s, "gemm_dA_swiglu");
+                p, EpiSwigluBwd<T>{static_cast<const T*>(h_save), dH, f}, R, s, "gemm_dA_swiglu",
+                "gemm_dA_swiglu_tail");
     }
     // dW2[e] = A_e^T dO_e   [f, d]
     {
-        GemmArgs<T> p = base_args<T>(offsets, prefix, order, E);
+        GemmArgs<T> p = base_args<T>(offsets, pl, E);
         p.A = static_cast<const T*>(a_save); p.lda = f; p.M = f;
         p.B = dO; p.ldb = d; p.N = d;
         Launch<T, Cfg>::template go<RAGGED_K, MNMAJ, MNMAJ, false, false>(
@@ -876,7 +1351,7 @@ moe_status ffn_bwd(const void* d_out, const void* x_perm, const void* h_save,
     }
     // dW1[e] = X_e^T dH1_e  [d, f]   (dW3 with dH3)
     {
-        GemmArgs<T> p = base_args<T>(offsets, prefix, order, E);
+        GemmArgs<T> p = base_args<T>(offsets, pl, E);
         p.A = static_cast<const T*>(x_perm); p.lda = d; p.M = d;
         p.B = dH; p.ldb = ldh; p.N = f;
         Launch<T, Cfg>::template go<RAGGED_K, MNMAJ, MNMAJ, false, false>(
@@ -889,19 +1364,21 @@ moe_status ffn_bwd(const void* d_out, const void* x_perm, const void* h_save,
     }
     // dX = dH1 W1[e]^T (+ dH3 W3[e]^T)   [R, d]
     {
-        GemmArgs<T> p = base_args<T>(offsets, prefix, order, E);
+        GemmArgs<T> p = base_args<T>(offsets, pl, E);
         p.A = dH; p.lda = ldh;
         p.B = static_cast<const T*>(W1); p.ldb = f; p.bstride = (long)d * f;
         p.N = d;
         EpiStore<T> st{static_cast<T*>(dx_perm), d, 0};
         if (!sw) {
             p.K = f;
-            Launch<T, Cfg>::template go<RAGGED_M, KMAJ, KMAJ, false, false>(p, st, R, s, "gemm_dX");
+            Launch<T, Cfg>::template go<RAGGED_M, KMAJ, KMAJ, false, false>(p, st, R, s, "gemm_dX",
+                                                                            "gemm_dX_tail");
         } else {
             p.K = 2 * f;
             p.Ksplit = f;
             p.B2 = static_cast<const T*>(W3);
-            Launch<T, Cfg>::template go<RAGGED_M, KMAJ, KMAJ, false, true>(p, st, R, s, "gemm_dX");
+            Launch<T, Cfg>::template go<RAGGED_M, KMAJ, KMAJ, false, true>(p, st, R, s, "gemm_dX",
+                                                                           "gemm_dX_tail");
         }
     }
     return launch_status();

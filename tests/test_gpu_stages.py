@@ -93,6 +93,11 @@ FFN_CASES = [  # counts per expert, d, f
     ([256, 256], 64, 64),
     ([0, 0, 70], 256, 320),
     ([1], 64, 128),
+    # partial last tiles of every size class for the 64-row slices of the
+    # split launch (64, 63, 65, 192, 1, 255, 64, ...), more partial experts
+    # than one row-tile group, and one expert with 8 full tiles + 130 rows
+    ([64, 63, 65, 192, 257, 511, 320, 0, 1, 700, 130, 5], 128, 256),
+    ([2178], 64, 128),
 ]
 
 
