@@ -840,65 +840,83 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ggemm_bf16_dma_kernel(GemmArg
         }
         if constexpr (DUAL) opB2.dma(k0, stg + A_BYTES + B_BYTES);
     };
-    auto compute = [&](const uint8_t* stg) {
+    // Fragments are double-buffered across k-steps and across stages: the
+    // first fragments of stage j+1 are read while the last MFMAs of stage j
+    // run, so the matrix pipe never waits for a stage boundary.
+    constexpr int KS = BKD / 16;                       // MFMA k-steps per stage
+    static_assert(KS % 2 == 0, "fragment buffer parity assumes an even count");
+    bf16x8 af[2][FM], bfr[2][FN], bf2[2][DUAL ? FN : 1];
+    auto read_frags = [&](const uint8_t* stg, int ks, int buf) {
         const uint8_t* sA = stg;
         const uint8_t* sB = stg + A_BYTES;
-        const uint8_t* sB2 = sB + B_BYTES;
-        bf16x8 af[2][FM], bfr[2][FN], bf2[2][DUAL ? FN : 1];
-        auto read_frags = [&](int ks, int buf) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
-                af[buf][i] = dma_frag<BM, ALAY>(sA, wm * WTM + i * 32, ks, lane);
+        for (int i = 0; i < FM; ++i)
+            af[buf][i] = dma_frag<BM, ALAY>(sA, wm * WTM + i * 32, ks, lane);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            bfr[buf][j] = dma_frag<BN, BLAY>(sB, wn * WTN + j * 32, ks, lane);
+        if constexpr (DUAL) {
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                bfr[buf][j] = dma_frag<BN, BLAY>(sB, wn * WTN + j * 32, ks, lane);
-            if constexpr (DUAL) {
+                bf2[buf][j] = dma_frag<BN, BLAY>(sB + B_BYTES, wn * WTN + j * 32, ks, lane);
+        }
+    };
+    auto mfmas = [&](int buf) {
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    bf2[buf][j] = dma_frag<BN, BLAY>(sB2, wn * WTN + j * 32, ks, lane);
-            }
-        };
-        read_frags(0, 0);
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int ks = 0; ks < BKD / 16; ++ks) {
-            const int cb = ks & 1;
-            if (ks + 1 < BKD / 16) read_frags(ks + 1, cb ^ 1);
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][i], bfr[buf][j],
+                                                                   acc[i][j], 0, 0, 0);
+        if constexpr (DUAL) {
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        af[cb][i], bfr[cb][j], acc[i][j], 0, 0, 0);
-            if constexpr (DUAL) {
-#pragma unroll
-                for (int i = 0; i < FM; ++i)
-#pragma unroll
-                    for (int j = 0; j < FN; ++j)
-                        acc2[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            af[cb][i], bf2[cb][j], acc2[i][j], 0, 0, 0);
-            }
+                    acc2[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        af[buf][i], bf2[buf][j], acc2[i][j], 0, 0, 0);
         }
-    };
-    // one step of the ring: wait for stage j, publish it, refill the stage
-    // freed by step j-1 with sub-tile j+3, multiply stage j
-    const int nj = (ti.klen + BKD - 1) / BKD;
-    auto step = [&](uint8_t* cur, uint8_t* refill, int j) {
-        const int ahead = min(nj - 1 - j, NSTG - 2);      // later sub-tiles in flight
-        if (ahead >= 2) stage_barrier<2 * NL>();
-        else if (ahead == 1) stage_barrier<NL>();
-        else stage_barrier<0>();
-        if (j + NSTG - 1 < nj) issue(refill, j + NSTG - 1);
-        compute(cur);
     };
     auto ring = [&](int q) -> uint8_t* {
         return q == 0 ? st0 : q == 1 ? st1 : q == 2 ? st2 : st3;
     };
+    // Ring of NSTG = 4 stages: while stage j is multiplied, stage j+1 has
+    // landed, j+2 is in flight and j+3 is issued once every wave is past the
+    // reads of stage j-1 (whose buffer it reuses).
+    const int nj = (ti.klen + BKD - 1) / BKD;
     if (nj > 0) issue(st0, 0);
     if (nj > 1) issue(st1, 1);
     if (nj > 2) issue(st2, 2);
+    if (nj > 2) stage_barrier<2 * NL>();               // stage 0 landed
+    else if (nj > 1) stage_barrier<NL>();
+    else stage_barrier<0>();
+    if (nj > 0) read_frags(st0, 0, 0);
+    // all stages but the last; the last one is peeled off so that the loop
+    // body has one path and the compiler's LDS waits before its final MFMAs
+    // do not cover the reads of the next stage
 #pragma unroll 1
-    for (int j = 0; j < nj; ++j)
-        step(ring(j & 3), ring((j + 3) & 3), j);
+    for (int j = 0; j + 1 < nj; ++j) {
+        const uint8_t* cur = ring(j & 3);
+#pragma unroll
+        for (int ks = 0; ks + 1 < KS; ++ks) {
+            read_frags(cur, ks + 1, (ks + 1) & 1);
+            mfmas(ks & 1);
+        }
+        if (j + 2 < nj) stage_barrier<NL>();            // stage j+1 landed
+        else stage_barrier<0>();
+        if (j + 3 < nj) issue(ring((j + 3) & 3), j + 3);
+        read_frags(ring((j + 1) & 3), 0, 0);
+        mfmas((KS - 1) & 1);
+    }
+    if (nj > 0) {
+        const uint8_t* cur = ring((nj - 1) & 3);
+#pragma unroll
+        for (int ks = 0; ks + 1 < KS; ++ks) {
+            read_frags(cur, ks + 1, (ks + 1) & 1);
+            mfmas(ks & 1);
+        }
+        mfmas((KS - 1) & 1);
+    }
     __syncthreads();
 
     // ---- epilogue through LDS (same scheme as the register kernel)
@@ -1193,7 +1211,7 @@ struct TileCfg {
     static constexpr int BMT = BMT_, BNT = BNT_, WMT = WMT_, WNT = WNT_;
     static constexpr int BNN = BNN_, WNN = WNN_;
 };
-using DefaultCfg = TileCfg<256, 256, 2, 4, 128, 2, 4, true, 64, 256, 1, 4, 128, 4>;
+using DefaultCfg = TileCfg<256, 256, 4, 2, 128, 4, 2, true, 64, 256, 1, 4, 128, 4>;
 
 // Wave quantisation.  A RAGGED_M product has between ceil(R/BM) and
 // ceil(R/BM) + E - 1 row tiles, since each expert's last tile is usually
