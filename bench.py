@@ -82,6 +82,9 @@ def parse():
     ap.add_argument("--workload", default="moe_s_like",
                     help="workload name (moe_inputs.configs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--serial", action="store_true",
+                    help="run every kernel on one stream (moe_set_overlap(0)) in the "
+                         "headline too; the per-kernel pass is always serial")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU work for the oracle baseline")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
@@ -141,6 +144,7 @@ def main():
     cfg = CONFIGS[args.workload]
     torch.cuda.set_device(0)
     M.moe_init(0)
+    M.moe_set_overlap(not args.serial)
     t = device.gen_all(cfg)
     layer = M.MoELayer(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.act,
                        device.torch_dtype(cfg), cfg.renorm)
@@ -255,7 +259,7 @@ def main():
         "data": "synthetic (seeded counter-based generator, inputs resident in HBM)",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "f": cfg.f,
                    "E": cfg.E, "k": cfg.k, "act": cfg.act, "renorm": cfg.renorm,
-                   "routing_skew_zipf_s": cfg.zipf_s},
+                   "routing_skew_zipf_s": cfg.zipf_s, "stream_overlap": not args.serial},
         "gemm_tflops_layer": round(gemm_flops / (ms * 1e-3) / 1e12, 2),
         "gemm_tflops_kernels": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 2)
         if gemm_ms else None,

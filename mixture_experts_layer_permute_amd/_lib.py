@@ -21,6 +21,7 @@ SIGNATURES = {
     "moe_status_string": (ctypes.c_char_p, [_I]),
     "moe_abi_version": (_I, []),
     "moe_init": (_I, [_I]),
+    "moe_set_overlap": (_I, [_I]),
     "moe_gate_topk": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P]),
     "moe_permute_workspace_bytes": (_Z, [_I, _I, _I]),
     "moe_permute": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _Z, _P]),

@@ -1,6 +1,8 @@
 // Library-wide entry points: status text, version, device check.
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
 #include <new>
 
 #include "common.h"
@@ -28,6 +30,70 @@ int device_cus() {
     }
     __atomic_store_n(&g_dev_state[dev], s, __ATOMIC_RELEASE);
     return s;
+}
+
+// ------------------------------------------------------- side streams
+namespace {
+struct SideState {
+    std::mutex mu;
+    hipStream_t s = nullptr;
+    hipEvent_t ev[4] = {};   // 0 fork, 1..2 marks, 3 join
+    bool made = false;
+};
+SideState g_side[kMaxDevices];
+}  // namespace
+
+std::atomic<int> g_overlap{1};
+
+SideStream::SideStream(hipStream_t main) : main_(main) {
+    if (!g_overlap.load(std::memory_order_relaxed) || g_prof_on) return;   // caller's stream only
+    int d = -1;
+    if (hipGetDevice(&d) != hipSuccess || d < 0 || d >= kMaxDevices) return;
+    SideState& st = g_side[d];
+    std::unique_lock<std::mutex> lk(st.mu);
+    if (!st.made) {
+        // (a failure leaves what was made for the next attempt to complete)
+        if (!st.s && hipStreamCreateWithFlags(&st.s, hipStreamNonBlocking) != hipSuccess) {
+            st.s = nullptr;
+            return;
+        }
+        for (int i = 0; i < 4; ++i)
+            if (!st.ev[i] &&
+                hipEventCreateWithFlags(&st.ev[i], hipEventDisableTiming) != hipSuccess) {
+                st.ev[i] = nullptr;
+                return;
+            }
+        st.made = true;
+    }
+    if (hipEventRecord(st.ev[0], main_) != hipSuccess ||
+        hipStreamWaitEvent(st.s, st.ev[0], 0) != hipSuccess)
+        return;
+    side_ = st.s;
+    ev_ = st.ev;
+    ok_ = true;
+    dev_ = d;
+    lk.release();                 // held until the destructor
+}
+
+bool SideStream::mark(int i) {
+    return ok_ && i >= 1 && i <= 2 && hipEventRecord(ev_[i], side_) == hipSuccess;
+}
+
+bool SideStream::wait(int i) {
+    return ok_ && i >= 1 && i <= 2 && hipStreamWaitEvent(main_, ev_[i], 0) == hipSuccess;
+}
+
+bool SideStream::join() {
+    if (!ok_ || joined_) return ok_;
+    joined_ = true;
+    return hipEventRecord(ev_[3], side_) == hipSuccess &&
+           hipStreamWaitEvent(main_, ev_[3], 0) == hipSuccess;
+}
+
+SideStream::~SideStream() {
+    if (dev_ < 0) return;
+    if (ok_) join();
+    g_side[dev_].mu.unlock();
 }
 
 // ------------------------------------------------------------ timing
@@ -122,7 +188,12 @@ const char* moe_status_string(moe_status s) {
     return "unknown status";
 }
 
-int moe_abi_version(void) { return 1; }
+int moe_abi_version(void) { return 2; }
+
+moe_status moe_set_overlap(int enable) {
+    moe::g_overlap.store(enable != 0 ? 1 : 0, std::memory_order_relaxed);
+    return MOE_OK;
+}
 
 moe_status moe_init(int device) {
     int cur = 0;

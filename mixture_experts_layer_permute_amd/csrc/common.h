@@ -98,6 +98,30 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 inline int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 
+// Per-device side stream for launches that overlap the caller's stream
+// (kernels with no data dependence on each other).  A SideStream object
+// locks the device's side stream for the duration of one call, makes it wait
+// for all work queued on the caller's stream so far (fork), and makes the
+// caller's stream wait for everything queued on it (join) when finished, so
+// the whole call stays ordered on the caller's stream.
+class SideStream {
+   public:
+    explicit SideStream(hipStream_t main);
+    ~SideStream();
+    bool ok() const { return ok_; }
+    hipStream_t get() const { return side_; }
+    // record mark i (0..2) on the side stream / make the caller's stream wait for it
+    bool mark(int i);
+    bool wait(int i);
+    bool join();
+
+   private:
+    hipStream_t main_, side_ = nullptr;
+    hipEvent_t* ev_ = nullptr;
+    int dev_ = -1;
+    bool ok_ = false, joined_ = false;
+};
+
 // Kernel timing hooks (see moe_profile_enable).  prof_mark(name, s, 0)
 // before a launch, prof_mark(name, s, 1) after it; no-ops when disabled.
 extern bool g_prof_on;

@@ -1237,7 +1237,8 @@ template <class Cfg>
 struct Launch<bf16_t, Cfg> {
     template <int MODE, int ALAY, int BLAY, bool DUAL, bool KSPLIT, class Epi>
     static void go(GemmArgs<bf16_t> p, Epi epi, int R, hipStream_t s, const char* name,
-                   const char* tail_name = nullptr) {
+                   const char* tail_name = nullptr, hipStream_t ts = nullptr) {
+        if (!ts) ts = s;           // stream of the tail launch
         if constexpr (DUAL) {
             launch_bf16<Cfg::BM, Cfg::BND, Cfg::WMD, Cfg::WND, Cfg::DMA, MODE, ALAY, BLAY, DUAL,
                         KSPLIT>(p, epi, R, s, name);
@@ -1255,11 +1256,11 @@ struct Launch<bf16_t, Cfg> {
                     if (Cfg::BNN > 0 && slices * cdiv(p.N, Cfg::BNT) < device_cus()) {
                         q.xcd_run = xcd_run_for(slices * cdiv(p.N, Cfg::BNN));
                         launch_bf16<Cfg::BMT, Cfg::BNN, Cfg::WMT, Cfg::WNN, Cfg::DMA, MODE,
-                                    ALAY, BLAY, DUAL, KSPLIT>(q, epi, R, s, tail_name);
+                                    ALAY, BLAY, DUAL, KSPLIT>(q, epi, R, ts, tail_name);
                     } else {
                         q.xcd_run = xcd_run_for(slices * cdiv(p.N, Cfg::BNT));
                         launch_bf16<Cfg::BMT, Cfg::BNT, Cfg::WMT, Cfg::WNT, Cfg::DMA, MODE,
-                                    ALAY, BLAY, DUAL, KSPLIT>(q, epi, R, s, tail_name);
+                                    ALAY, BLAY, DUAL, KSPLIT>(q, epi, R, ts, tail_name);
                     }
                     return;
                 }
@@ -1275,7 +1276,7 @@ template <class Cfg>
 struct Launch<float, Cfg> {
     template <int MODE, int ALAY, int BLAY, bool DUAL, bool KSPLIT, class Epi>
     static void go(GemmArgs<float> p, Epi epi, int R, hipStream_t s, const char* name,
-                   const char* = nullptr) {
+                   const char* = nullptr, hipStream_t = nullptr) {
         launch_f32<MODE, ALAY, BLAY, DUAL, KSPLIT>(p, epi, R, s, name);
     }
     static constexpr int BM = FB;
@@ -1305,21 +1306,28 @@ moe_status ffn_fwd(const void* x_perm, const int32_t* offsets, int R, int E,
     p.A = xp; p.lda = d;
     p.B = static_cast<const T*>(W1); p.ldb = f; p.bstride = (long)d * f;
     p.N = f; p.K = d;
-    if (act == MOE_ACT_GELU) {
-        Launch<T, Cfg>::template go<RAGGED_M, KMAJ, MNMAJ, false, false>(
-            p, EpiGeluFwd<T>{H, A, f}, R, s, "gemm_up_gelu", "gemm_up_gelu_tail");
-    } else {
-        p.B2 = static_cast<const T*>(W3);
-        Launch<T, Cfg>::template go<RAGGED_M, KMAJ, MNMAJ, true, false>(
-            p, EpiSwigluFwd<T>{H, A, f}, R, s, "gemm_up_swiglu");
-    }
     // GEMM2: A [R,f] x W2[e] [f,d]
     GemmArgs<T> q = base_args<T>(offsets, pl, E);
     q.A = A; q.lda = f;
     q.B = static_cast<const T*>(W2); q.ldb = d; q.bstride = (long)f * d;
     q.N = d; q.K = f;
+    if (act == MOE_ACT_SWIGLU) {       // one launch over all rows, before the fork
+        p.B2 = static_cast<const T*>(W3);
+        Launch<T, Cfg>::template go<RAGGED_M, KMAJ, MNMAJ, true, false>(
+            p, EpiSwigluFwd<T>{H, A, f}, R, s, "gemm_up_swiglu");
+    }
+    // The rows of the experts' full tiles (main launches, caller's stream)
+    // and of their partial last tiles (tail launches, side stream) are
+    // independent all the way through both GEMMs.
+    SideStream side(s);
+    hipStream_t ts = side.ok() ? side.get() : s;
+    if (act == MOE_ACT_GELU)
+        Launch<T, Cfg>::template go<RAGGED_M, KMAJ, MNMAJ, false, false>(
+            p, EpiGeluFwd<T>{H, A, f}, R, s, "gemm_up_gelu", "gemm_up_gelu_tail", ts);
     Launch<T, Cfg>::template go<RAGGED_M, KMAJ, MNMAJ, false, false>(
-        q, EpiStore<T>{static_cast<T*>(out_perm), d, 0}, R, s, "gemm_down", "gemm_down_tail");
+        q, EpiStore<T>{static_cast<T*>(out_perm), d, 0}, R, s, "gemm_down", "gemm_down_tail",
+        ts);
+    if (side.ok() && !side.join()) return MOE_ERR_HIP;
     return launch_status();
 }
 
@@ -1344,6 +1352,11 @@ moe_status ffn_bwd(const void* d_out, const void* x_perm, const void* h_save,
                                                   order, full, part));
 
     const T* dO = static_cast<const T*>(d_out);
+    // Caller's stream: dA (full tiles) -> dX (full tiles) -> dW1, dW3.
+    // Side stream:     dA (partial tiles) -> dW2 -> dX (partial tiles).
+    // dW2 depends on neither dA nor dX; dW1/dW3 need every row of dH.
+    SideStream side(s);
+    hipStream_t ts = side.ok() ? side.get() : s;
     // dA = dO W2[e]^T with the activation derivative in the epilogue -> dH
     {
         GemmArgs<T> p = base_args<T>(offsets, pl, E);
@@ -1353,11 +1366,12 @@ moe_status ffn_bwd(const void* d_out, const void* x_perm, const void* h_save,
         if (!sw)
             Launch<T, Cfg>::template go<RAGGED_M, KMAJ, KMAJ, false, false>(
                 p, EpiGeluBwd<T>{static_cast<const T*>(h_save), dH, f}, R, s, "gemm_dA_gelu",
-                "gemm_dA_gelu_tail");
+                "gemm_dA_gelu_tail", ts);
         else
             Launch<T, Cfg>::template go<RAGGED_M, KMAJ, KMAJ, false, false>(
                 p, EpiSwigluBwd<T>{static_cast<const T*>(h_save), dH, f}, R, s, "gemm_dA_swiglu",
-                "gemm_dA_swiglu_tail");
+                "gemm_dA_swiglu_tail", ts);
+        if (side.ok() && !side.mark(1)) return MOE_ERR_HIP;  // dH of the partial tiles
     }
     // dW2[e] = A_e^T dO_e   [f, d]
     {
@@ -1365,9 +1379,29 @@ moe_status ffn_bwd(const void* d_out, const void* x_perm, const void* h_save,
         p.A = static_cast<const T*>(a_save); p.lda = f; p.M = f;
         p.B = dO; p.ldb = d; p.N = d;
         Launch<T, Cfg>::template go<RAGGED_K, MNMAJ, MNMAJ, false, false>(
-            p, EpiStore<T>{static_cast<T*>(dW2), d, (long)f * d}, R, s, "gemm_dW2");
+            p, EpiStore<T>{static_cast<T*>(dW2), d, (long)f * d}, R, ts, "gemm_dW2");
     }
-    // dW1[e] = X_e^T dH1_e  [d, f]   (dW3 with dH3)
+    // dX = dH1 W1[e]^T (+ dH3 W3[e]^T)   [R, d]
+    {
+        GemmArgs<T> p = base_args<T>(offsets, pl, E);
+        p.A = dH; p.lda = ldh;
+        p.B = static_cast<const T*>(W1); p.ldb = f; p.bstride = (long)d * f;
+        p.N = d;
+        EpiStore<T> st{static_cast<T*>(dx_perm), d, 0};
+        if (!sw) {
+            p.K = f;
+            Launch<T, Cfg>::template go<RAGGED_M, KMAJ, KMAJ, false, false>(p, st, R, s, "gemm_dX",
+                                                                            "gemm_dX_tail", ts);
+        } else {
+            p.K = 2 * f;
+            p.Ksplit = f;
+            p.B2 = static_cast<const T*>(W3);
+            Launch<T, Cfg>::template go<RAGGED_M, KMAJ, KMAJ, false, true>(p, st, R, s, "gemm_dX",
+                                                                           "gemm_dX_tail", ts);
+        }
+    }
+    // dW1[e] = X_e^T dH1_e  [d, f]   (dW3 with dH3): needs the side's part of dH
+    if (side.ok() && !side.wait(1)) return MOE_ERR_HIP;
     {
         GemmArgs<T> p = base_args<T>(offsets, pl, E);
         p.A = static_cast<const T*>(x_perm); p.lda = d; p.M = d;
@@ -1380,25 +1414,7 @@ moe_status ffn_bwd(const void* d_out, const void* x_perm, const void* h_save,
                 p, EpiStore<T>{static_cast<T*>(dW3), f, (long)d * f}, R, s, "gemm_dW3");
         }
     }
-    // dX = dH1 W1[e]^T (+ dH3 W3[e]^T)   [R, d]
-    {
-        GemmArgs<T> p = base_args<T>(offsets, pl, E);
-        p.A = dH; p.lda = ldh;
-        p.B = static_cast<const T*>(W1); p.ldb = f; p.bstride = (long)d * f;
-        p.N = d;
-        EpiStore<T> st{static_cast<T*>(dx_perm), d, 0};
-        if (!sw) {
-            p.K = f;
-            Launch<T, Cfg>::template go<RAGGED_M, KMAJ, KMAJ, false, false>(p, st, R, s, "gemm_dX",
-                                                                            "gemm_dX_tail");
-        } else {
-            p.K = 2 * f;
-            p.Ksplit = f;
-            p.B2 = static_cast<const T*>(W3);
-            Launch<T, Cfg>::template go<RAGGED_M, KMAJ, KMAJ, false, true>(p, st, R, s, "gemm_dX",
-                                                                           "gemm_dX_tail");
-        }
-    }
+    if (side.ok() && !side.join()) return MOE_ERR_HIP;
     return launch_status();
 }
 

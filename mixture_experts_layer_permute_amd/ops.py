@@ -51,6 +51,11 @@ def moe_init(device=0):
     check(load().moe_init(int(device)), "moe_init")
 
 
+def moe_set_overlap(enable=True):
+    """Let the FFN calls run independent launches on a side stream (default)."""
+    check(load().moe_set_overlap(1 if enable else 0), "moe_set_overlap")
+
+
 def moe_gate_topk(x, Wg, k, logit_bias=None, renorm=1, logits=None,
                   topk_idx=None, topk_w=None):
     """-> (logits [T,E] f32, topk_idx [T,k] i32, topk_w [T,k] f32)."""

@@ -61,3 +61,26 @@ def test_layer_full(name):
         assert_close(layer.dWg, gr["dWg"], dt, "dWg")
     else:
         assert np.all(host(layer.dWg) == 0)
+
+
+@pytest.mark.parametrize("name", ["moe_s_like", "small_swiglu"])
+def test_stream_overlap_bit_identical(name):
+    """The side-stream schedule (partial tiles and dW2 beside the main
+    launches) gives exactly the bits of the single-stream schedule."""
+    from moe_inputs import small_variant
+    cfg = CONFIGS[name] if name in CONFIGS else small_variant(
+        "long_ctx_swiglu", T=1500, d=256, f=512, E=8)
+    banner("overlap", name, cfg.short())
+    outs = []
+    try:
+        for on in (False, True):
+            M.moe_set_overlap(on)
+            layer, _ = run_layer(cfg)
+            outs.append({n: getattr(layer, n).clone() for n in
+                         ("h_save", "a_save", "out_perm", "y", "dx_perm", "dW1", "dW2",
+                          "dW3", "dx", "dWg") if getattr(layer, n) is not None})
+            del layer
+    finally:
+        M.moe_set_overlap(True)
+    for n in outs[0]:
+        assert torch.equal(outs[0][n], outs[1][n]), n
