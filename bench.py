@@ -27,18 +27,19 @@ PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA, 256 CU x 2.4 GHz
 PEAK_F32_TFLOPS = 157.3       # fp32 vector
 PEAK_HBM_GBS = 8000.0
 
-# HBM bytes per launch (fetch + write) of the FFN and row kernels on the
-# MoE-S-like workload, from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs
-# scaled by the readings of a plain 1 GiB device copy (factors 6.0 and 1.5);
-# see profiles/hbm_traffic_moe_s_like.md.  Valid only for the kernel sources
+# HBM bytes per call (fetch + write; a GEMM stage's main and partial-tile
+# launches together) of the FFN and row kernels on the MoE-S-like workload,
+# from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs scaled by the readings
+# of a plain 1 GiB device copy in the same run (factors 4.0 and 1.0); see
+# profiles/hbm_traffic_moe_s_like.md.  Valid only for the kernel sources
 # whose SHA-256 prefix is TRAFFIC_SRC; null once they change.
-TRAFFIC_SRC = "41a03a652cb41189"
+TRAFFIC_SRC = "54564313b93d3aff"
 TRAFFIC_SOURCES = ("ggemm.hip", "common.h", "permute.hip", "combine.hip")
-TRAFFIC = {"gemm_up_gelu": 1174509062, "gemm_down": 830728245,
-           "gemm_dA_gelu": 1392432808, "gemm_dW1": 1610767075,
-           "gemm_dW2": 1610767075, "gemm_dX": 830736232, "perm_copy": 101567255,
-           "combine": 127494818, "combine_bwd": 203230211,
-           "unpermute_grad": 126719206}
+TRAFFIC = {"gemm_up_gelu": 918308302, "gemm_down": 738628869,
+           "gemm_dA_gelu": 1074262403, "gemm_dW1": 1073915555,
+           "gemm_dW2": 1073915555, "gemm_dX": 738578646, "perm_copy": 67711770,
+           "combine": 84996514, "combine_bwd": 135486990,
+           "unpermute_grad": 84478927}
 
 
 def traffic_for(kernel, workload):

@@ -83,6 +83,11 @@ bool SideStream::wait(int i) {
     return ok_ && i >= 1 && i <= 2 && hipStreamWaitEvent(main_, ev_[i], 0) == hipSuccess;
 }
 
+bool SideStream::follow() {
+    return ok_ && hipEventRecord(ev_[0], main_) == hipSuccess &&
+           hipStreamWaitEvent(side_, ev_[0], 0) == hipSuccess;
+}
+
 bool SideStream::join() {
     if (!ok_ || joined_) return ok_;
     joined_ = true;

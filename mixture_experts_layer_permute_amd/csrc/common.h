@@ -113,6 +113,8 @@ class SideStream {
     // record mark i (0..2) on the side stream / make the caller's stream wait for it
     bool mark(int i);
     bool wait(int i);
+    // the side stream waits for all work queued on the caller's stream so far
+    bool follow();
     bool join();
 
    private:

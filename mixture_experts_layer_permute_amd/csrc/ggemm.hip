@@ -1218,12 +1218,15 @@ using DefaultCfg = TileCfg<256, 256, 4, 2, 128, 4, 2, true, 64, 256, 1, 4, 128, 
 // partial; with nN column tiles per row tile the last round of workgroups
 // is often nearly empty (e.g. 72 x 4 tiles on 256 compute units: two rounds
 // for 1.125 rounds of work), and the partial tiles cost as much as full
-// ones.  Split: one launch multiplies the full row tiles of all experts,
+// ones.  Split (when the product is under kSplitRounds rounds of
+// workgroups): one launch multiplies the full row tiles of all experts,
 // a second one only the partial last tiles, cut into BMT-row slices (empty
 // slices exit at once) with BNT-wide columns, or BNN-wide ones when the
 // wide tail would leave most compute units idle, spread over all XCDs.
 // Every output element is still one fixed-order sum over k: identical
 // results.
+constexpr int kSplitRounds = 8;
+
 inline int xcd_run_for(long tiles) {
     int run = 1;
     while (run < 32 && (long)run * 2 * NXCD <= tiles) run *= 2;
@@ -1235,16 +1238,31 @@ struct Launch;
 
 template <class Cfg>
 struct Launch<bf16_t, Cfg> {
+    // Whether go() splits a product of this shape (given a tail name).
+    template <int MODE, bool DUAL>
+    static bool splits(int R, int E, int N) {
+        if constexpr (MODE == RAGGED_M && !DUAL && Cfg::BMT > 0) {
+            // Split only when the product is a few rounds of workgroups:
+            // with many rounds the one partially filled last round is a
+            // small share, and the narrow slices cost more than they save.
+            const long tiles = (long)(cdiv(R, Cfg::BM) + E / 2) * cdiv(N, Cfg::BN);
+            return tiles < (long)kSplitRounds * device_cus();
+        }
+        return false;
+    }
+    // Returns true when the product was split: full row tiles on s, the
+    // partial last tiles on ts.  Otherwise everything ran on s.
     template <int MODE, int ALAY, int BLAY, bool DUAL, bool KSPLIT, class Epi>
-    static void go(GemmArgs<bf16_t> p, Epi epi, int R, hipStream_t s, const char* name,
+    static bool go(GemmArgs<bf16_t> p, Epi epi, int R, hipStream_t s, const char* name,
                    const char* tail_name = nullptr, hipStream_t ts = nullptr) {
         if (!ts) ts = s;           // stream of the tail launch
         if constexpr (DUAL) {
             launch_bf16<Cfg::BM, Cfg::BND, Cfg::WMD, Cfg::WND, Cfg::DMA, MODE, ALAY, BLAY, DUAL,
                         KSPLIT>(p, epi, R, s, name);
+            return false;
         } else {
             if constexpr (MODE == RAGGED_M && Cfg::BMT > 0) {
-                if (tail_name) {
+                if (tail_name && splits<MODE, DUAL>(R, p.E, p.N)) {
                     GemmArgs<bf16_t> q = p;
                     q.part_mode = 1;
                     q.bm_plan = Cfg::BM;
@@ -1262,11 +1280,12 @@ struct Launch<bf16_t, Cfg> {
                         launch_bf16<Cfg::BMT, Cfg::BNT, Cfg::WMT, Cfg::WNT, Cfg::DMA, MODE,
                                     ALAY, BLAY, DUAL, KSPLIT>(q, epi, R, ts, tail_name);
                     }
-                    return;
+                    return true;
                 }
             }
             launch_bf16<Cfg::BM, Cfg::BN, Cfg::WM, Cfg::WN, Cfg::DMA, MODE, ALAY, BLAY, DUAL,
                         KSPLIT>(p, epi, R, s, name);
+            return false;
         }
     }
     static constexpr int BM = Cfg::BM;
@@ -1274,10 +1293,13 @@ struct Launch<bf16_t, Cfg> {
 
 template <class Cfg>
 struct Launch<float, Cfg> {
+    template <int MODE, bool DUAL>
+    static bool splits(int, int, int) { return false; }
     template <int MODE, int ALAY, int BLAY, bool DUAL, bool KSPLIT, class Epi>
-    static void go(GemmArgs<float> p, Epi epi, int R, hipStream_t s, const char* name,
+    static bool go(GemmArgs<float> p, Epi epi, int R, hipStream_t s, const char* name,
                    const char* = nullptr, hipStream_t = nullptr) {
         launch_f32<MODE, ALAY, BLAY, DUAL, KSPLIT>(p, epi, R, s, name);
+        return false;
     }
     static constexpr int BM = FB;
 };
@@ -1318,12 +1340,21 @@ moe_status ffn_fwd(const void* x_perm, const int32_t* offsets, int R, int E,
     }
     // The rows of the experts' full tiles (main launches, caller's stream)
     // and of their partial last tiles (tail launches, side stream) are
-    // independent all the way through both GEMMs.
+    // independent through both GEMMs; where only one of the two products is
+    // split, the stream of the partial rows' consumer waits for their producer.
     SideStream side(s);
     hipStream_t ts = side.ok() ? side.get() : s;
+    bool up_split = false;
     if (act == MOE_ACT_GELU)
-        Launch<T, Cfg>::template go<RAGGED_M, KMAJ, MNMAJ, false, false>(
+        up_split = Launch<T, Cfg>::template go<RAGGED_M, KMAJ, MNMAJ, false, false>(
             p, EpiGeluFwd<T>{H, A, f}, R, s, "gemm_up_gelu", "gemm_up_gelu_tail", ts);
+    const bool down_split = Launch<T, Cfg>::template splits<RAGGED_M, false>(R, E, d);
+    if (side.ok() && up_split != down_split) {
+        // up split, down whole: down (caller's stream) needs up's partial rows;
+        // up whole, down split: down's tail (side stream) needs rows made on s
+        const bool ok = up_split ? side.mark(1) && side.wait(1) : side.follow();
+        if (!ok) return MOE_ERR_HIP;
+    }
     Launch<T, Cfg>::template go<RAGGED_M, KMAJ, MNMAJ, false, false>(
         q, EpiStore<T>{static_cast<T*>(out_perm), d, 0}, R, s, "gemm_down", "gemm_down_tail",
         ts);
@@ -1354,9 +1385,12 @@ moe_status ffn_bwd(const void* d_out, const void* x_perm, const void* h_save,
     const T* dO = static_cast<const T*>(d_out);
     // Caller's stream: dA (full tiles) -> dX (full tiles) -> dW1, dW3.
     // Side stream:     dA (partial tiles) -> dW2 -> dX (partial tiles).
-    // dW2 depends on neither dA nor dX; dW1/dW3 need every row of dH.
+    // dW2 depends on neither dA nor dX; dW1/dW3 need every row of dH.  A
+    // product that is not split runs whole on the caller's stream, and the
+    // stream that consumes its rows waits for it.
     SideStream side(s);
     hipStream_t ts = side.ok() ? side.get() : s;
+    bool dA_split = false;
     // dA = dO W2[e]^T with the activation derivative in the epilogue -> dH
     {
         GemmArgs<T> p = base_args<T>(offsets, pl, E);
@@ -1364,14 +1398,14 @@ moe_status ffn_bwd(const void* d_out, const void* x_perm, const void* h_save,
         p.B = static_cast<const T*>(W2); p.ldb = d; p.bstride = (long)f * d;
         p.N = f; p.K = d;
         if (!sw)
-            Launch<T, Cfg>::template go<RAGGED_M, KMAJ, KMAJ, false, false>(
+            dA_split = Launch<T, Cfg>::template go<RAGGED_M, KMAJ, KMAJ, false, false>(
                 p, EpiGeluBwd<T>{static_cast<const T*>(h_save), dH, f}, R, s, "gemm_dA_gelu",
                 "gemm_dA_gelu_tail", ts);
         else
-            Launch<T, Cfg>::template go<RAGGED_M, KMAJ, KMAJ, false, false>(
-                p, EpiSwigluBwd<T>{static_cast<const T*>(h_save), dH, f}, R, s, "gemm_dA_swiglu",
-                "gemm_dA_swiglu_tail", ts);
-        if (side.ok() && !side.mark(1)) return MOE_ERR_HIP;  // dH of the partial tiles
+            dA_split = Launch<T, Cfg>::template go<RAGGED_M, KMAJ, KMAJ, false, false>(
+                p, EpiSwigluBwd<T>{static_cast<const T*>(h_save), dH, f}, R, s,
+                "gemm_dA_swiglu", "gemm_dA_swiglu_tail", ts);
+        if (side.ok() && dA_split && !side.mark(1)) return MOE_ERR_HIP;  // dH, partial tiles
     }
     // dW2[e] = A_e^T dO_e   [f, d]
     {
@@ -1382,6 +1416,13 @@ moe_status ffn_bwd(const void* d_out, const void* x_perm, const void* h_save,
             p, EpiStore<T>{static_cast<T*>(dW2), d, (long)f * d}, R, ts, "gemm_dW2");
     }
     // dX = dH1 W1[e]^T (+ dH3 W3[e]^T)   [R, d]
+    const bool dX_split = Launch<T, Cfg>::template splits<RAGGED_M, false>(R, E, d);
+    if (side.ok() && dA_split != dX_split) {
+        // dA split, dX whole: dX (caller's stream) needs the side's rows of dH;
+        // dA whole, dX split: dX's tail (side stream) needs dH made on s
+        const bool ok = dA_split ? side.wait(1) : side.follow();
+        if (!ok) return MOE_ERR_HIP;
+    }
     {
         GemmArgs<T> p = base_args<T>(offsets, pl, E);
         p.A = dH; p.lda = ldh;
@@ -1400,8 +1441,8 @@ moe_status ffn_bwd(const void* d_out, const void* x_perm, const void* h_save,
                                                                            "gemm_dX_tail", ts);
         }
     }
-    // dW1[e] = X_e^T dH1_e  [d, f]   (dW3 with dH3): needs the side's part of dH
-    if (side.ok() && !side.wait(1)) return MOE_ERR_HIP;
+    // dW1[e] = X_e^T dH1_e  [d, f]   (dW3 with dH3): needs every row of dH
+    if (side.ok() && dA_split && !side.wait(1)) return MOE_ERR_HIP;
     {
         GemmArgs<T> p = base_args<T>(offsets, pl, E);
         p.A = static_cast<const T*>(x_perm); p.lda = d; p.M = d;

@@ -63,13 +63,21 @@ def test_layer_full(name):
         assert np.all(host(layer.dWg) == 0)
 
 
-@pytest.mark.parametrize("name", ["moe_s_like", "small_swiglu"])
+OVERLAP_CASES = {
+    "moe_s_like": None,                       # every RAGGED_M product split
+    "small_swiglu": ("long_ctx_swiglu", dict(T=1500, d=256, f=512, E=8)),
+    # up and dA (N = f = 8192) run whole, down and dX (N = d = 512) split
+    "mixed_split": ("moe_s_like", dict(d=512, f=8192)),
+}
+
+
+@pytest.mark.parametrize("name", list(OVERLAP_CASES))
 def test_stream_overlap_bit_identical(name):
     """The side-stream schedule (partial tiles and dW2 beside the main
     launches) gives exactly the bits of the single-stream schedule."""
     from moe_inputs import small_variant
-    cfg = CONFIGS[name] if name in CONFIGS else small_variant(
-        "long_ctx_swiglu", T=1500, d=256, f=512, E=8)
+    spec = OVERLAP_CASES[name]
+    cfg = CONFIGS[name] if spec is None else small_variant(spec[0], **spec[1])
     banner("overlap", name, cfg.short())
     outs = []
     try:
