@@ -33,13 +33,13 @@ PEAK_HBM_GBS = 8000.0
 # of a plain 1 GiB device copy in the same run (factors 4.0 and 1.0); see
 # profiles/hbm_traffic_moe_s_like.md.  Valid only for the kernel sources
 # whose SHA-256 prefix is TRAFFIC_SRC; null once they change.
-TRAFFIC_SRC = "54564313b93d3aff"
+TRAFFIC_SRC = "c78e40a0e2abf1b3"
 TRAFFIC_SOURCES = ("ggemm.hip", "common.h", "permute.hip", "combine.hip")
-TRAFFIC = {"gemm_up_gelu": 918308302, "gemm_down": 738628869,
-           "gemm_dA_gelu": 1074262403, "gemm_dW1": 1073915555,
-           "gemm_dW2": 1073915555, "gemm_dX": 738578646, "perm_copy": 67711770,
-           "combine": 84996514, "combine_bwd": 135486990,
-           "unpermute_grad": 84478927}
+TRAFFIC = {"gemm_up_gelu": 916850469, "gemm_down": 738626498,
+           "gemm_dA_gelu": 1074931522, "gemm_dW1": 1073908219,
+           "gemm_dW2": 1073908219, "gemm_dX": 738584671, "perm_copy": 67711455,
+           "combine": 84996038, "combine_bwd": 135486675,
+           "unpermute_grad": 84478657}
 
 
 def traffic_for(kernel, workload):

@@ -117,8 +117,17 @@ __device__ __forceinline__ float sigmoid_f(float z) {
     else return sigmoid_exact(z);
 }
 
+// Epilogue functors.  vec8(e, row, col, v) finishes 8 consecutive outputs.
+// Functors that read memory split that into pre8() (issue the loads, return
+// the raw data) and vec8p(..., pre), so the bf16 kernel can put all loads of
+// a slab in flight before it consumes the first; kPre says which do.
+struct NoPre {};
+
 template <typename T>
 struct EpiStore {            // C[e*cstride + row*ldc + col] = v
+    static constexpr bool kPre = false;
+    typedef NoPre Pre;
+    __device__ __forceinline__ Pre pre8(int, long, int) const { return {}; }
     T* C;
     long ldc, cstride;
     __device__ __forceinline__ void operator()(int e, long row, int col, float v) const {
@@ -127,10 +136,17 @@ struct EpiStore {            // C[e*cstride + row*ldc + col] = v
     __device__ __forceinline__ void vec8(int e, long row, int col, const float* v) const {
         Vec16<T>::st(C + e * cstride + row * ldc + col, v);
     }
+    __device__ __forceinline__ void vec8p(int e, long row, int col, const float* v,
+                                          const Pre&) const {
+        vec8(e, row, col, v);
+    }
 };
 
 template <typename T>
 struct EpiGeluFwd {          // H = v, A = GeLU(v)
+    static constexpr bool kPre = false;
+    typedef NoPre Pre;
+    __device__ __forceinline__ Pre pre8(int, long, int) const { return {}; }
     T* H;
     T* A;
     long ld;
@@ -145,10 +161,17 @@ struct EpiGeluFwd {          // H = v, A = GeLU(v)
         Vec16<T>::st(H + row * ld + col, v);
         Vec16<T>::st(A + row * ld + col, a);
     }
+    __device__ __forceinline__ void vec8p(int e, long row, int col, const float* v,
+                                          const Pre&) const {
+        vec8(e, row, col, v);
+    }
 };
 
 template <typename T>
 struct EpiSwigluFwd {        // H1 = v1, H3 = v3 (row = [H1 | H3]), A = SiLU(v1) v3
+    static constexpr bool kPre = false;
+    typedef NoPre Pre;
+    __device__ __forceinline__ Pre pre8(int, long, int) const { return {}; }
     T* H;
     T* A;
     long f;
@@ -171,6 +194,14 @@ struct EpiSwigluFwd {        // H1 = v1, H3 = v3 (row = [H1 | H3]), A = SiLU(v1)
 
 template <typename T>
 struct EpiGeluBwd {          // dH = dA * GeLU'(H)
+    static constexpr bool kPre = true;
+    struct Pre {
+        uint4 h;                    // 8 bf16 of H, raw (bf16 kernels only)
+    };
+    __device__ __forceinline__ Pre pre8(int, long row, int col) const {
+        static_assert(sizeof(T) == 2, "prefetching epilogue is for bf16 tensors");
+        return {*reinterpret_cast<const uint4*>(H + row * ld + col)};
+    }
     const T* H;
     T* dH;
     long ld;
@@ -185,10 +216,32 @@ struct EpiGeluBwd {          // dH = dA * GeLU'(H)
         for (int q = 0; q < 8; ++q) o[q] = v[q] * gelu_grad_f<T>(h[q]);
         Vec16<T>::st(dH + row * ld + col, o);
     }
+    __device__ __forceinline__ void vec8p(int, long row, int col, const float* v,
+                                          const Pre& pr) const {
+        float h[8], o[8];
+        const uint32_t w[4] = {pr.h.x, pr.h.y, pr.h.z, pr.h.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            h[2 * q] = __uint_as_float(w[q] << 16);
+            h[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) o[q] = v[q] * gelu_grad_f<T>(h[q]);
+        Vec16<T>::st(dH + row * ld + col, o);
+    }
 };
 
 template <typename T>
 struct EpiSwigluBwd {        // dH1 = dA H3 SiLU'(H1), dH3 = dA SiLU(H1)
+    static constexpr bool kPre = true;
+    struct Pre {
+        uint4 h1, h3;               // 8 bf16 each of H1 and H3, raw (bf16 kernels only)
+    };
+    __device__ __forceinline__ Pre pre8(int, long row, int col) const {
+        static_assert(sizeof(T) == 2, "prefetching epilogue is for bf16 tensors");
+        return {*reinterpret_cast<const uint4*>(H + row * 2 * f + col),
+                *reinterpret_cast<const uint4*>(H + row * 2 * f + f + col)};
+    }
     const T* H;
     T* dH;
     long f;
@@ -203,6 +256,27 @@ struct EpiSwigluBwd {        // dH1 = dA H3 SiLU'(H1), dH3 = dA SiLU(H1)
         float h1[8], h3[8], o1[8], o3[8];
         Vec16<T>::ld(H + row * 2 * f + col, h1);
         Vec16<T>::ld(H + row * 2 * f + f + col, h3);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const float sg = sigmoid_f<T>(h1[q]);
+            o1[q] = v[q] * h3[q] * sg * (1.0f + h1[q] * (1.0f - sg));
+            o3[q] = v[q] * h1[q] * sg;
+        }
+        Vec16<T>::st(dH + row * 2 * f + col, o1);
+        Vec16<T>::st(dH + row * 2 * f + f + col, o3);
+    }
+    __device__ __forceinline__ void vec8p(int, long row, int col, const float* v,
+                                          const Pre& pr) const {
+        float h1[8], h3[8], o1[8], o3[8];
+        const uint32_t w1[4] = {pr.h1.x, pr.h1.y, pr.h1.z, pr.h1.w};
+        const uint32_t w3[4] = {pr.h3.x, pr.h3.y, pr.h3.z, pr.h3.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            h1[2 * q] = __uint_as_float(w1[q] << 16);
+            h1[2 * q + 1] = __uint_as_float(w1[q] & 0xffff0000u);
+            h3[2 * q] = __uint_as_float(w3[q] << 16);
+            h3[2 * q + 1] = __uint_as_float(w3[q] & 0xffff0000u);
+        }
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             const float sg = sigmoid_f<T>(h1[q]);
@@ -943,30 +1017,49 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ggemm_bf16_dma_kernel(GemmArg
                         slab[SLAB + r * LDW + j * 32 + (lane & 31)] = acc2[i][j][v];
                 }
             __syncthreads();
+            constexpr int NPS = 16 / RPP;                 // sub-passes of this slab
+            auto row_of = [&](int ps) { return wm * WTM + i * 32 + h * 16 + ps * RPP + lane / LPR; };
+            const int c0 = (lane % LPR) * 8;
+            const int col = ti.n0 + wn * WTN + c0;
+            auto ok_of = [&](int rl) {
+                return col < p.N && (MODE == RAGGED_M ? rl < ti.rows : ti.m0 + rl < p.M);
+            };
+            if constexpr (Epi::kPre && !DUAL && MODE == RAGGED_M) {
+                // every read of this slab in flight before the first is used
+                typename Epi::Pre pre[NPS];
+#pragma unroll
+                for (int ps = 0; ps < NPS; ++ps)
+                    if (ok_of(row_of(ps))) pre[ps] = epi.pre8(ti.e, ti.r0 + row_of(ps), col);
+#pragma unroll
+                for (int ps = 0; ps < NPS; ++ps) {
+                    const int rl = row_of(ps);
+                    const float* src = &slab[(ps * RPP + lane / LPR) * LDW + c0];
+                    float v[8];
+                    *reinterpret_cast<float4*>(v) = *reinterpret_cast<const float4*>(src);
+                    *reinterpret_cast<float4*>(v + 4) = *reinterpret_cast<const float4*>(src + 4);
+                    if (ok_of(rl)) epi.vec8p(ti.e, ti.r0 + rl, col, v, pre[ps]);
+                }
+            } else {
 #pragma unroll 1
-            for (int ps = 0; ps < 16 / RPP; ++ps) {
-                const int r = ps * RPP + lane / LPR;
-                const int c0 = (lane % LPR) * 8;
-                const int rl = wm * WTM + i * 32 + h * 16 + r;
-                const int col = ti.n0 + wn * WTN + c0;
-                const float* src = &slab[r * LDW + c0];
-                float v[8];
-                *reinterpret_cast<float4*>(v) = *reinterpret_cast<const float4*>(src);
-                *reinterpret_cast<float4*>(v + 4) = *reinterpret_cast<const float4*>(src + 4);
-                const bool ok =
-                    col < p.N && (MODE == RAGGED_M ? rl < ti.rows : ti.m0 + rl < p.M);
-                if (ok) {
-                    if constexpr (DUAL) {
-                        float v3[8];
-                        *reinterpret_cast<float4*>(v3) =
-                            *reinterpret_cast<const float4*>(src + SLAB);
-                        *reinterpret_cast<float4*>(v3 + 4) =
-                            *reinterpret_cast<const float4*>(src + SLAB + 4);
-                        epi.vec8(ti.e, ti.r0 + rl, col, v, v3);
-                    } else if (MODE == RAGGED_M) {
-                        epi.vec8(ti.e, ti.r0 + rl, col, v);
-                    } else {
-                        epi.vec8(ti.e, (long)ti.m0 + rl, col, v);
+                for (int ps = 0; ps < NPS; ++ps) {
+                    const int rl = row_of(ps);
+                    const float* src = &slab[(ps * RPP + lane / LPR) * LDW + c0];
+                    float v[8];
+                    *reinterpret_cast<float4*>(v) = *reinterpret_cast<const float4*>(src);
+                    *reinterpret_cast<float4*>(v + 4) = *reinterpret_cast<const float4*>(src + 4);
+                    if (ok_of(rl)) {
+                        if constexpr (DUAL) {
+                            float v3[8];
+                            *reinterpret_cast<float4*>(v3) =
+                                *reinterpret_cast<const float4*>(src + SLAB);
+                            *reinterpret_cast<float4*>(v3 + 4) =
+                                *reinterpret_cast<const float4*>(src + SLAB + 4);
+                            epi.vec8(ti.e, ti.r0 + rl, col, v, v3);
+                        } else if (MODE == RAGGED_M) {
+                            epi.vec8(ti.e, ti.r0 + rl, col, v);
+                        } else {
+                            epi.vec8(ti.e, (long)ti.m0 + rl, col, v);
+                        }
                     }
                 }
             }
