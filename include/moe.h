@@ -136,14 +136,18 @@ moe_status moe_permute(const int32_t *topk_idx, const void *x, int T, int d,
 /*
  * moe_expert_ffn_fwd -- every expert's FFN on its segment, one grouped GEMM
  * per product over the ragged segments (rows offsets[e]..offsets[e+1]).
- *   GeLU:   H = X_e W1[e], A = GeLU(H) (exact erf form), O = A W2[e]
+ *   GeLU:   H = X_e W1[e], A = GeLU(H) (erf form), O = A W2[e]
  *   SwiGLU: H1 = X_e W1[e], H3 = X_e W3[e], A = SiLU(H1)*H3, O = A W2[e]
+ * For bf16 the normal CDF inside GeLU is evaluated with the rational
+ * approximation of erf of Abramowitz & Stegun 7.1.26 (|error| <= 1.5e-7).
  * Source: FastMoE review, 제안 방법 (dedicated expert FFN, parallel expert
  * linear layers); ES-MoE review, 三 技术架构 (experts take their tokens in
  * sequence, no padding).
  *   x_perm [R,d] dt, offsets [E+1] int32 (device; R = offsets[E]),
  *   W1 [E,d,f], W3 [E,d,f] (SwiGLU only, else NULL), W2 [E,f,d] dt,
- *   h_save [R,f] (GeLU: H) or [R,2f] (SwiGLU: row r = H1[r,:] then H3[r,:]),
+ *   h_save: what the backward needs of the pre-activation, computed from the
+ *     fp32 accumulator: GeLU: [R,f] = GeLU'(H); SwiGLU: [R,2f], row r =
+ *     H3*SiLU'(H1) then SiLU(H1).  Only moe_expert_ffn_bwd reads it.
  *   a_save [R,f] (A), out_perm [R,d] dt.  Accumulation is fp32.
  *   ws: at least moe_ffn_workspace_bytes(R,E,d,f,act,dt,0).
  */

@@ -98,23 +98,29 @@ __device__ __forceinline__ float sigmoid_fast(float z) {
 }
 
 template <typename T>
-__device__ __forceinline__ float gelu_f(float z) {
-    if constexpr (sizeof(T) == 2) return z * norm_fast(z).cdf;
-    else return gelu_exact(z);
-}
-template <typename T>
-__device__ __forceinline__ float gelu_grad_f(float z) {
-    if constexpr (sizeof(T) == 2) {
-        const NormCP n = norm_fast(z);
-        return fmaf(z, n.pdf, n.cdf);
-    } else {
-        return gelu_grad_exact(z);
-    }
-}
-template <typename T>
 __device__ __forceinline__ float sigmoid_f(float z) {
     if constexpr (sizeof(T) == 2) return sigmoid_fast(z);
     else return sigmoid_exact(z);
+}
+
+// GeLU(z) and GeLU'(z) from one evaluation of the normal CDF and density.
+template <typename T>
+__device__ __forceinline__ void gelu_and_grad(float z, float& a, float& g) {
+    if constexpr (sizeof(T) == 2) {
+        const NormCP n = norm_fast(z);
+        a = z * n.cdf;
+        g = fmaf(z, n.pdf, n.cdf);
+    } else {
+        a = gelu_exact(z);
+        g = gelu_grad_exact(z);
+    }
+}
+// The SwiGLU factors the backward needs: s1 = H3 * SiLU'(H1), s3 = SiLU(H1).
+template <typename T>
+__device__ __forceinline__ void swiglu_saved(float h1, float h3, float& s1, float& s3) {
+    const float sg = sigmoid_f<T>(h1);
+    s3 = h1 * sg;
+    s1 = h3 * sg * (1.0f + h1 * (1.0f - sg));
 }
 
 // Epilogue functors.  vec8(e, row, col, v) finishes 8 consecutive outputs.
@@ -142,23 +148,29 @@ struct EpiStore {            // C[e*cstride + row*ldc + col] = v
     }
 };
 
+// The forward saves what the backward's activation derivative needs, not
+// the pre-activation: GeLU'(H) for GeLU, [H3 SiLU'(H1) | SiLU(H1)] for
+// SwiGLU, each computed from the fp32 accumulator, so the backward epilogue
+// is one (two) multiplications per element.
 template <typename T>
-struct EpiGeluFwd {          // H = v, A = GeLU(v)
+struct EpiGeluFwd {          // S = GeLU'(v) (saved for the backward), A = GeLU(v)
     static constexpr bool kPre = false;
     typedef NoPre Pre;
     __device__ __forceinline__ Pre pre8(int, long, int) const { return {}; }
-    T* H;
+    T* S;
     T* A;
     long ld;
     __device__ __forceinline__ void operator()(int, long row, int col, float v) const {
-        Elem<T>::st(H + row * ld + col, v);
-        Elem<T>::st(A + row * ld + col, gelu_f<T>(v));
+        float a, g;
+        gelu_and_grad<T>(v, a, g);
+        Elem<T>::st(S + row * ld + col, g);
+        Elem<T>::st(A + row * ld + col, a);
     }
     __device__ __forceinline__ void vec8(int, long row, int col, const float* v) const {
-        float a[8];
+        float a[8], g[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) a[q] = gelu_f<T>(v[q]);
-        Vec16<T>::st(H + row * ld + col, v);
+        for (int q = 0; q < 8; ++q) gelu_and_grad<T>(v[q], a[q], g[q]);
+        Vec16<T>::st(S + row * ld + col, g);
         Vec16<T>::st(A + row * ld + col, a);
     }
     __device__ __forceinline__ void vec8p(int e, long row, int col, const float* v,
@@ -168,121 +180,111 @@ struct EpiGeluFwd {          // H = v, A = GeLU(v)
 };
 
 template <typename T>
-struct EpiSwigluFwd {        // H1 = v1, H3 = v3 (row = [H1 | H3]), A = SiLU(v1) v3
+struct EpiSwigluFwd {        // S = [H3 SiLU'(H1) | SiLU(H1)] per row, A = SiLU(H1) H3
     static constexpr bool kPre = false;
     typedef NoPre Pre;
     __device__ __forceinline__ Pre pre8(int, long, int) const { return {}; }
-    T* H;
+    T* S;
     T* A;
     long f;
     __device__ __forceinline__ void operator()(int, long row, int col, float v1,
                                                float v3) const {
-        Elem<T>::st(H + row * 2 * f + col, v1);
-        Elem<T>::st(H + row * 2 * f + f + col, v3);
-        Elem<T>::st(A + row * f + col, v1 * sigmoid_f<T>(v1) * v3);
+        float s1, s3;
+        swiglu_saved<T>(v1, v3, s1, s3);
+        Elem<T>::st(S + row * 2 * f + col, s1);
+        Elem<T>::st(S + row * 2 * f + f + col, s3);
+        Elem<T>::st(A + row * f + col, s3 * v3);
     }
     __device__ __forceinline__ void vec8(int, long row, int col, const float* v1,
                                          const float* v3) const {
-        float a[8];
+        float s1[8], s3[8], a[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) a[q] = v1[q] * sigmoid_f<T>(v1[q]) * v3[q];
-        Vec16<T>::st(H + row * 2 * f + col, v1);
-        Vec16<T>::st(H + row * 2 * f + f + col, v3);
+        for (int q = 0; q < 8; ++q) {
+            swiglu_saved<T>(v1[q], v3[q], s1[q], s3[q]);
+            a[q] = s3[q] * v3[q];
+        }
+        Vec16<T>::st(S + row * 2 * f + col, s1);
+        Vec16<T>::st(S + row * 2 * f + f + col, s3);
         Vec16<T>::st(A + row * f + col, a);
     }
 };
 
+__device__ __forceinline__ void unpack_bf16x8(const uint4& r, float* o) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        o[2 * q] = __uint_as_float(w[q] << 16);
+        o[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+    }
+}
+
 template <typename T>
-struct EpiGeluBwd {          // dH = dA * GeLU'(H)
+struct EpiGeluBwd {          // dH = dA * S, S = GeLU'(H) saved by the forward
     static constexpr bool kPre = true;
     struct Pre {
-        uint4 h;                    // 8 bf16 of H, raw (bf16 kernels only)
+        uint4 s;                    // 8 bf16 of S, raw (bf16 kernels only)
     };
     __device__ __forceinline__ Pre pre8(int, long row, int col) const {
         static_assert(sizeof(T) == 2, "prefetching epilogue is for bf16 tensors");
-        return {*reinterpret_cast<const uint4*>(H + row * ld + col)};
+        return {*reinterpret_cast<const uint4*>(S + row * ld + col)};
     }
-    const T* H;
+    const T* S;
     T* dH;
     long ld;
     __device__ __forceinline__ void operator()(int, long row, int col, float v) const {
-        const float h = Elem<T>::ld(H + row * ld + col);
-        Elem<T>::st(dH + row * ld + col, v * gelu_grad_f<T>(h));
+        Elem<T>::st(dH + row * ld + col, v * Elem<T>::ld(S + row * ld + col));
     }
     __device__ __forceinline__ void vec8(int, long row, int col, const float* v) const {
-        float h[8], o[8];
-        Vec16<T>::ld(H + row * ld + col, h);
+        float g[8], o[8];
+        Vec16<T>::ld(S + row * ld + col, g);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) o[q] = v[q] * gelu_grad_f<T>(h[q]);
+        for (int q = 0; q < 8; ++q) o[q] = v[q] * g[q];
         Vec16<T>::st(dH + row * ld + col, o);
     }
     __device__ __forceinline__ void vec8p(int, long row, int col, const float* v,
                                           const Pre& pr) const {
-        float h[8], o[8];
-        const uint32_t w[4] = {pr.h.x, pr.h.y, pr.h.z, pr.h.w};
+        float g[8], o[8];
+        unpack_bf16x8(pr.s, g);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            h[2 * q] = __uint_as_float(w[q] << 16);
-            h[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
-        }
-#pragma unroll
-        for (int q = 0; q < 8; ++q) o[q] = v[q] * gelu_grad_f<T>(h[q]);
+        for (int q = 0; q < 8; ++q) o[q] = v[q] * g[q];
         Vec16<T>::st(dH + row * ld + col, o);
     }
 };
 
 template <typename T>
-struct EpiSwigluBwd {        // dH1 = dA H3 SiLU'(H1), dH3 = dA SiLU(H1)
+struct EpiSwigluBwd {        // dH1 = dA * S1, dH3 = dA * S3 (S saved by the forward)
     static constexpr bool kPre = true;
     struct Pre {
-        uint4 h1, h3;               // 8 bf16 each of H1 and H3, raw (bf16 kernels only)
+        uint4 s1, s3;               // 8 bf16 each of S1 and S3, raw (bf16 kernels only)
     };
     __device__ __forceinline__ Pre pre8(int, long row, int col) const {
         static_assert(sizeof(T) == 2, "prefetching epilogue is for bf16 tensors");
-        return {*reinterpret_cast<const uint4*>(H + row * 2 * f + col),
-                *reinterpret_cast<const uint4*>(H + row * 2 * f + f + col)};
+        return {*reinterpret_cast<const uint4*>(S + row * 2 * f + col),
+                *reinterpret_cast<const uint4*>(S + row * 2 * f + f + col)};
     }
-    const T* H;
+    const T* S;
     T* dH;
     long f;
     __device__ __forceinline__ void operator()(int, long row, int col, float v) const {
-        const float h1 = Elem<T>::ld(H + row * 2 * f + col);
-        const float h3 = Elem<T>::ld(H + row * 2 * f + f + col);
-        const float s = sigmoid_f<T>(h1);
-        Elem<T>::st(dH + row * 2 * f + col, v * h3 * s * (1.0f + h1 * (1.0f - s)));
-        Elem<T>::st(dH + row * 2 * f + f + col, v * h1 * s);
+        Elem<T>::st(dH + row * 2 * f + col, v * Elem<T>::ld(S + row * 2 * f + col));
+        Elem<T>::st(dH + row * 2 * f + f + col, v * Elem<T>::ld(S + row * 2 * f + f + col));
     }
     __device__ __forceinline__ void vec8(int, long row, int col, const float* v) const {
-        float h1[8], h3[8], o1[8], o3[8];
-        Vec16<T>::ld(H + row * 2 * f + col, h1);
-        Vec16<T>::ld(H + row * 2 * f + f + col, h3);
+        float s1[8], s3[8], o1[8], o3[8];
+        Vec16<T>::ld(S + row * 2 * f + col, s1);
+        Vec16<T>::ld(S + row * 2 * f + f + col, s3);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const float sg = sigmoid_f<T>(h1[q]);
-            o1[q] = v[q] * h3[q] * sg * (1.0f + h1[q] * (1.0f - sg));
-            o3[q] = v[q] * h1[q] * sg;
-        }
+        for (int q = 0; q < 8; ++q) o1[q] = v[q] * s1[q], o3[q] = v[q] * s3[q];
         Vec16<T>::st(dH + row * 2 * f + col, o1);
         Vec16<T>::st(dH + row * 2 * f + f + col, o3);
     }
     __device__ __forceinline__ void vec8p(int, long row, int col, const float* v,
                                           const Pre& pr) const {
-        float h1[8], h3[8], o1[8], o3[8];
-        const uint32_t w1[4] = {pr.h1.x, pr.h1.y, pr.h1.z, pr.h1.w};
-        const uint32_t w3[4] = {pr.h3.x, pr.h3.y, pr.h3.z, pr.h3.w};
+        float s1[8], s3[8], o1[8], o3[8];
+        unpack_bf16x8(pr.s1, s1);
+        unpack_bf16x8(pr.s3, s3);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            h1[2 * q] = __uint_as_float(w1[q] << 16);
-            h1[2 * q + 1] = __uint_as_float(w1[q] & 0xffff0000u);
-            h3[2 * q] = __uint_as_float(w3[q] << 16);
-            h3[2 * q + 1] = __uint_as_float(w3[q] & 0xffff0000u);
-        }
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const float sg = sigmoid_f<T>(h1[q]);
-            o1[q] = v[q] * h3[q] * sg * (1.0f + h1[q] * (1.0f - sg));
-            o3[q] = v[q] * h1[q] * sg;
-        }
+        for (int q = 0; q < 8; ++q) o1[q] = v[q] * s1[q], o3[q] = v[q] * s3[q];
         Vec16<T>::st(dH + row * 2 * f + col, o1);
         Vec16<T>::st(dH + row * 2 * f + f + col, o3);
     }

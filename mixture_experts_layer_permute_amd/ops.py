@@ -100,7 +100,8 @@ def moe_permute(topk_idx, x, E, out=None, ws=None):
 
 def moe_expert_ffn_fwd(x_perm, offsets, W1, W2, W3=None, act="gelu", out=None,
                        ws=None):
-    """-> (h_save [R,f] or [R,2f], a_save [R,f], out_perm [R,d])."""
+    """-> (h_save, a_save [R,f], out_perm [R,d]); h_save is the state the
+    backward needs: GeLU'(H) [R,f], or [H3 SiLU'(H1) | SiLU(H1)] [R,2f]."""
     _need_gpu(x_perm, offsets, W1, W2, W3)
     a = _act(act)
     R, d = x_perm.shape

@@ -62,3 +62,13 @@ def assert_equal_i(got, ref, name):
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
     bad = np.flatnonzero(got.reshape(-1) != ref.reshape(-1))
     assert bad.size == 0, "%s: %d mismatches, first at %d" % (name, bad.size, bad[0])
+
+
+def saved_state(act, H, H3=None):
+    """What the FFN forward saves for its backward, from the oracle's
+    pre-activations: GeLU'(H), or [H3 * SiLU'(H1) | SiLU(H1)] for SwiGLU."""
+    import oracle
+    if act == "gelu":
+        return oracle.gelu_grad(H)
+    return np.concatenate([np.asarray(H3, np.float64) * oracle.silu_grad(H),
+                           oracle.silu(H)], axis=1)

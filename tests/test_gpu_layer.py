@@ -9,7 +9,7 @@ import mixture_experts_layer_permute_amd as M
 import oracle
 from moe_inputs import CONFIGS, device, rng
 
-from _gpu import assert_close, assert_equal_i, banner, host, needs_gpu
+from _gpu import assert_close, assert_equal_i, banner, host, needs_gpu, saved_state
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
@@ -47,7 +47,8 @@ def test_layer_full(name):
         assert_equal_i(got, fw[n], n)
     assert_close(layer.topk_w, fw["w"], "f32", "topk_w")
     assert_close(layer.x_perm, fw["x_perm"], dt, "x_perm")
-    assert_close(layer.h_save, fw["H"], dt, "H")
+    assert_close(layer.h_save, saved_state(cfg.act, fw["H"], fw.get("H3")), dt,
+                 "saved GeLU'(H)")
     assert_close(layer.a_save, fw["A"], dt, "A")
     assert_close(layer.out_perm, fw["out_perm"], dt, "out_perm")
     assert_close(layer.y, fw["y"], dt, "y")
