@@ -21,13 +21,12 @@
 //            (三 技术架构 / 动态专家放置), here applied across compute units.
 //            An expert with no rows writes zeros.
 //
-// bf16 path: 256 threads (2x2 waves of 64), block tile BMxBNx64, gfx950
-// MFMA v_mfma_f32_32x32x16_bf16 with fp32 accumulators, both operands
-// staged in LDS as K-contiguous rows (16-byte chunks XOR-swizzled against
-// bank conflicts) and double-buffered, next tile prefetched into registers
-// while the current one is multiplied.  Operands stored with M/N contiguous
-// (the weight in x W, both sides of the dW products) are transposed in
-// registers, 8x8 bf16 at a time, on their way into LDS.
+// bf16 path: block tile 256x256, 8 waves of 64 (4x2, 64x128 each), gfx950
+// MFMA v_mfma_f32_32x32x16_bf16 with fp32 accumulators.  Operands go from
+// HBM straight into a 4-stage LDS ring; K-contiguous operands are read as
+// 16-byte fragments, M/N-contiguous ones with the transposing LDS read.
+// Products that are a few rounds of workgroups run as a full-tile launch
+// and a partial-tile launch; independent launches may run on a side stream.
 // fp32 path (tiny fp32 workload): a plain LDS-tiled FMA kernel with the same
 // tile scheduler and epilogues.
 #include "common.h"
@@ -382,349 +381,15 @@ __device__ __forceinline__ TileInfo decode_tile(const GemmArgs<T>& p) {
 // =====================================================================
 // bf16 MFMA kernel
 // =====================================================================
-
-constexpr int BK = 64;
-
-// byte offset of 16-byte chunk c (0..7) of LDS row r (rows of 64 bf16)
-__device__ __forceinline__ int swz(int r, int c) {
-    return r * 128 + ((c ^ ((r ^ (r >> 3)) & 7)) << 4);
-}
-
-// ------------------------------------------------------------- loads
-// Operand tiles are read with raw buffer loads: the descriptor's byte range
-// covers exactly the valid part of the tile, and the hardware returns zeros
-// for any lane whose offset falls outside it.  Ragged segment ends, the end
-// of the reduction, partial M/N tiles and the end of the allocation need no
-// branches.  A descriptor is rebuilt per k-tile from scalar registers.
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
-constexpr uint32_t OOB = 0x80000000u;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const bf16_t* base,
-                                                            long nbytes) {
-    const uint32_t n = nbytes <= 0 ? 0u : (uint32_t)nbytes;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(base), 0, n, 0x00020000);
-}
-
-__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-    return __builtin_bit_cast(uint4, v);
-}
-
-// One operand tile (ROWS x 64 along M or N by K) in flight between its
-// global load and its LDS store, spread over NT threads, 16 bytes a piece.
-//  KMAJ : elem(row, k) = P[row * ld + k],  rows < row_lim valid.  LDS holds
-//         K-contiguous rows of 64 (128 B), 16-byte chunks XOR-swizzled;
-//         MFMA fragments are plain 16-byte reads.
-//  MNMAJ: elem(row, k) = P[k * ld + row],  rows < row_lim, k < k_lim valid.
-//         LDS holds the tile as it lies in memory, 64 rows of ROWS elements
-//         (row pitch padded by 64 B); MFMA fragments come from two gfx950
-//         transposing reads (ds_read_b64_tr_b16) each.
-// P points at the tile origin (first row / first column, k = 0).
-template <int ROWS>
-struct MnLayout {
-    static constexpr int PITCH = ROWS * 2 + 64;        // bytes per k row
-    static constexpr int BYTES = 64 * PITCH;
-};
-
-template <int ROWS, int LAY>
-constexpr int op_lds_bytes() {
-    return LAY == KMAJ ? ROWS * BK * 2 : MnLayout<ROWS>::BYTES;
-}
-
-template <int ROWS, int LAY, int NT>
-struct Operand {
-    static constexpr int NB = ROWS / 8;                        // 16 B pieces per k row
-    static constexpr int NREG = ROWS * 8 / NT;                 // pieces per thread
-    static_assert(ROWS * 8 % NT == 0 && NT % NB == 0, "tile/thread mismatch");
-    const bf16_t* P;
-    long ld;
-    int row_lim;
-    long k_lim;
-    uint32_t off0;     // lane offset (bytes) of its first piece
-    uint4 r[NREG];
-
-    __device__ __forceinline__ void init(const bf16_t* P_, long ld_, int row_lim_,
-                                         long k_lim_) {
-        P = P_;
-        ld = ld_;
-        row_lim = row_lim_;
-        k_lim = k_lim_;
-        const int tid = threadIdx.x;
-        if (LAY == KMAJ) {
-            off0 = (uint32_t)((tid >> 3) * ld * 2 + (tid & 7) * 16);
-        } else {
-            const int cb = tid % NB, k = tid / NB;
-            off0 = cb * 8 < row_lim ? (uint32_t)(k * ld * 2 + cb * 16) : OOB;
-        }
-    }
-
-    __device__ __forceinline__ void load(long k0) {
-        if (LAY == KMAJ) {
-            const __amdgpu_buffer_rsrc_t rs =
-                make_rsrc(P + k0, (long)row_lim * ld * 2 - k0 * 2);
-            const uint32_t step = (uint32_t)((NT / 8) * ld * 2);
-#pragma unroll
-            for (int i = 0; i < NREG; ++i) r[i] = bload16(rs, off0 + i * step);
-        } else {
-            const long kv = min((long)BK, k_lim - k0);
-            const __amdgpu_buffer_rsrc_t rs = make_rsrc(P + k0 * ld, kv * ld * 2);
-            const uint32_t step = (uint32_t)((NT / NB) * ld * 2);
-#pragma unroll
-            for (int i = 0; i < NREG; ++i)
-                r[i] = bload16(rs, off0 == OOB ? OOB : off0 + i * step);
-        }
-    }
-
-    __device__ __forceinline__ void store(uint8_t* lds) const {
-        const int tid = threadIdx.x;
-        if (LAY == KMAJ) {
-#pragma unroll
-            for (int i = 0; i < NREG; ++i) {
-                const int row = (tid >> 3) + (NT / 8) * i, c = tid & 7;
-                *reinterpret_cast<uint4*>(lds + swz(row, c)) = r[i];
-            }
-        } else {
-            const int cb = tid % NB, k = tid / NB;
-#pragma unroll
-            for (int i = 0; i < NREG; ++i)
-                *reinterpret_cast<uint4*>(lds + (k + (NT / NB) * i) * MnLayout<ROWS>::PITCH +
-                                          cb * 16) = r[i];
-        }
-    }
-};
-
-// Fragment of a 32x32x16 MFMA operand for the wave's 32-row (or -column)
-// block starting at `row0`, reduction step ks: lane l holds rows
-// row0 + (l & 31), reduction indices ks*16 + (l >> 5)*8 + 0..7.
-__device__ __forceinline__ bf16x8 lds_frag(const uint8_t* lds, int row, int chunk) {
-    const uint4 v = *reinterpret_cast<const uint4*>(lds + swz(row, chunk));
-    return __builtin_bit_cast(bf16x8, v);
-}
-
-typedef short v4i16_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
-
-// The same fragment from an MN-major tile.  ds_read_b64_tr_b16 over a group
-// of 16 lanes: lane i receives element (i % 4) of the 8-byte pieces addressed
-// by lanes i/4 + 4q, q = 0..3.  Lane j of the group therefore points at
-// reduction row (base + j/4) and columns (col0 + 4*(j % 4)), which hands lane
-// i the four consecutive reduction indices of column col0 + i.
-template <int ROWS>
-__device__ __forceinline__ bf16x8 lds_frag_tr(const uint8_t* lds, int row0, int ks,
-                                              int lane) {
-    constexpr int PITCH = MnLayout<ROWS>::PITCH;
-    const int kr = ks * 16 + (lane >> 5) * 8 + ((lane & 15) >> 2);
-    const int col = row0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    const uint8_t* p0 = lds + kr * PITCH + col * 2;
-    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_v4i16_t*)(p0));
-    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_v4i16_t*)(p0 + 4 * PITCH));
-    typedef short v8i16_t __attribute__((ext_vector_type(8)));
-    const v8i16_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return __builtin_bit_cast(bf16x8, v);
-}
-
-template <int ROWS, int LAY>
-__device__ __forceinline__ bf16x8 op_frag(const uint8_t* lds, int row0, int ks, int lane) {
-    if constexpr (LAY == KMAJ)
-        return lds_frag(lds, row0 + (lane & 31), ks * 2 + (lane >> 5));
-    else
-        return lds_frag_tr<ROWS>(lds, row0, ks, lane);
-}
-
-// Block tile BM x BN x 64, WM x WN waves (64 threads each), wave tile
-// (BM/WM) x (BN/WN) of 32x32 MFMA tiles.
-template <int BM, int BN, int WM, int WN, int MODE, int ALAY, int BLAY, bool DUAL,
-          bool KSPLIT, class Epi>
-__global__ __launch_bounds__(64 * WM * WN, 1) void ggemm_bf16_kernel(GemmArgs<bf16_t> p,
-                                                                     Epi epi) {
-    constexpr int NT = 64 * WM * WN;
-    constexpr int WTM = BM / WM, WTN = BN / WN;
-    constexpr int FM = WTM / 32, FN = WTN / 32;
-    constexpr int NBT = DUAL ? 2 : 1;
-    constexpr int A_BYTES = op_lds_bytes<BM, ALAY>(), B_BYTES = op_lds_bytes<BN, BLAY>();
-    constexpr int STAGE = A_BYTES + NBT * B_BYTES;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
-
-    const TileInfo ti = decode_tile<MODE, BM, BN>(p);
-    if (!ti.live) return;
-
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int wm = wv / WN, wn = wv % WN;
-
-    Operand<BM, ALAY, NT> opA;
-    Operand<BN, BLAY, NT> opB;
-    Operand<BN, BLAY, NT> opB2;    // DUAL: the W3 tile
-    const bf16_t* bsplit[2];       // KSPLIT: B below / above the split of the reduction
-    if (MODE == RAGGED_M) {
-        opA.init(p.A + ti.r0 * p.lda, p.lda, ti.rows, p.K);
-        const long eoff = (long)ti.e * p.bstride;
-        const long nofs = BLAY == KMAJ ? (long)ti.n0 * p.ldb : (long)ti.n0;
-        opB.init(p.B + eoff + nofs, p.ldb, p.N - ti.n0, p.K);
-        if (DUAL) opB2.init(p.B2 + eoff + nofs, p.ldb, p.N - ti.n0, p.K);
-        if (KSPLIT) bsplit[0] = opB.P, bsplit[1] = p.B2 + eoff + nofs;
-    } else {
-        opA.init(p.A + ti.kbeg * p.lda + ti.m0, p.lda, p.M - ti.m0, ti.klen);
-        opB.init(p.B + ti.kbeg * p.ldb + ti.n0, p.ldb, p.N - ti.n0, ti.klen);
-    }
-
-    f32x16 acc[FM][FN];
-    f32x16 acc2[DUAL ? FM : 1][DUAL ? FN : 1];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-    if constexpr (DUAL) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) acc2[i][j][v] = 0.0f;
-    }
-
-    const int nk = (ti.klen + BK - 1) / BK;
-    // k-tile t+1 is fetched into registers while k-tile t is multiplied out
-    // of LDS stage (t & 1); it is written to the other stage afterwards.
-    auto load_stage = [&](int kt) {
-        const long k0 = (long)kt * BK;
-        opA.load(k0);
-        if constexpr (KSPLIT) {
-            const bool hi = k0 >= p.Ksplit;
-            opB.P = bsplit[hi];
-            opB.load(hi ? k0 - p.Ksplit : k0);
-        } else {
-            opB.load(k0);
-        }
-        if constexpr (DUAL) opB2.load(k0);
-    };
-    auto store_stage = [&](int buf) {
-        uint8_t* sm = smem + buf * STAGE;
-        opA.store(sm);
-        opB.store(sm + A_BYTES);
-        if constexpr (DUAL) opB2.store(sm + A_BYTES + B_BYTES);
-    };
-
-    if (nk > 0) {
-        load_stage(0);
-        store_stage(0);
-        __syncthreads();
-    }
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) load_stage(kt + 1);
-        const uint8_t* sA = smem + cur * STAGE;
-        const uint8_t* sB = sA + A_BYTES;
-        const uint8_t* sB2 = sB + B_BYTES;
-        // fragments of k-step ks+1 are read while the MFMAs of ks run
-        bf16x8 af[2][FM], bfr[2][FN], bf2[2][DUAL ? FN : 1];
-        auto read_frags = [&](int ks, int buf) {
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-                af[buf][i] = op_frag<BM, ALAY>(sA, wm * WTM + i * 32, ks, lane);
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-                bfr[buf][j] = op_frag<BN, BLAY>(sB, wn * WTN + j * 32, ks, lane);
-            if constexpr (DUAL) {
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    bf2[buf][j] = op_frag<BN, BLAY>(sB2, wn * WTN + j * 32, ks, lane);
-            }
-        };
-        read_frags(0, 0);
-#pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            const int cb = ks & 1;
-            if (ks + 1 < BK / 16) read_frags(ks + 1, cb ^ 1);
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        af[cb][i], bfr[cb][j], acc[i][j], 0, 0, 0);
-            if constexpr (DUAL) {
-#pragma unroll
-                for (int i = 0; i < FM; ++i)
-#pragma unroll
-                    for (int j = 0; j < FN; ++j)
-                        acc2[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            af[cb][i], bf2[cb][j], acc2[i][j], 0, 0, 0);
-            }
-        }
-        if (kt + 1 < nk) store_stage(cur ^ 1);
-        __syncthreads();
-    }
-
-    // ---- epilogue through LDS: one 16-row half of a 32-row slab of the wave
-    // tile at a time, then every lane owns 8 consecutive columns of a row
-    // (16-byte stores).  acc layout: lane holds column (lane & 31) and rows
-    // (v/4)*8 + (lane/32)*4 + v%4 of its 32x32 tile; registers v = 8h..8h+7
-    // cover rows 16h..16h+15.
-    constexpr int LDW = WTN + 4;                     // padded fp32 row
-    constexpr int SLAB = 16 * LDW;                   // floats per wave half-slab
-    float* slab = reinterpret_cast<float*>(smem) + wv * SLAB * NBT;
-    constexpr int LPR = WTN / 8;                     // lanes per row
-    constexpr int RPP = 64 / LPR;                    // rows per pass
-    static_assert(NT / 64 * SLAB * NBT * 4 <= 2 * STAGE, "epilogue slab too big");
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-                for (int vv = 0; vv < 8; ++vv) {
-                    const int v = h * 8 + vv;
-                    const int r = (vv >> 2) * 8 + (lane >> 5) * 4 + (vv & 3);
-                    slab[r * LDW + j * 32 + (lane & 31)] = acc[i][j][v];
-                    if constexpr (DUAL)
-                        slab[SLAB + r * LDW + j * 32 + (lane & 31)] = acc2[i][j][v];
-                }
-            __syncthreads();
-#pragma unroll 1
-            for (int ps = 0; ps < 16 / RPP; ++ps) {
-                const int r = ps * RPP + lane / LPR;
-                const int c0 = (lane % LPR) * 8;
-                const int rl = wm * WTM + i * 32 + h * 16 + r;
-                const int col = ti.n0 + wn * WTN + c0;
-                const float* src = &slab[r * LDW + c0];
-                float v[8];
-                *reinterpret_cast<float4*>(v) = *reinterpret_cast<const float4*>(src);
-                *reinterpret_cast<float4*>(v + 4) = *reinterpret_cast<const float4*>(src + 4);
-                const bool ok =
-                    col < p.N && (MODE == RAGGED_M ? rl < ti.rows : ti.m0 + rl < p.M);
-                if (ok) {
-                    if constexpr (DUAL) {
-                        float v3[8];
-                        *reinterpret_cast<float4*>(v3) =
-                            *reinterpret_cast<const float4*>(src + SLAB);
-                        *reinterpret_cast<float4*>(v3 + 4) =
-                            *reinterpret_cast<const float4*>(src + SLAB + 4);
-                        epi.vec8(ti.e, ti.r0 + rl, col, v, v3);
-                    } else if (MODE == RAGGED_M) {
-                        epi.vec8(ti.e, ti.r0 + rl, col, v);
-                    } else {
-                        epi.vec8(ti.e, (long)ti.m0 + rl, col, v);
-                    }
-                }
-            }
-            __syncthreads();
-        }
-    }
-}
-
-// =====================================================================
-// bf16 MFMA kernel, direct-to-LDS variant
-// =====================================================================
 // Operand tiles go from HBM straight into LDS with buffer_load_dwordx4 ...
 // lds (each wave instruction fills 1 KB: lane l's 16 bytes land at base +
-// 16*l), through a ring of NSTG stages of BKD reduction steps.  No register
-// staging; a stage is loaded NSTG-1 stages ahead of its use.  The stages are
-// separate LDS objects so the compiler can tell that a load into one stage
-// does not alias reads of another.
+// 16*l), through a ring of NSTG stages of BKD reduction steps, with no
+// register staging.  The descriptor's byte range covers exactly the valid
+// part of the tile, so lanes past a ragged segment end, the end of the
+// reduction, a partial tile or the allocation read zeros, with no branch.
+constexpr uint32_t OOB = 0x80000000u;    // an offset past any descriptor range
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 constexpr int BKD = 32;
 constexpr int NSTG = 4;
 
@@ -745,8 +410,9 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
 // The four words of a raw buffer resource: base address, stride 0,
-// num_records = nbytes (clamped at 0), and the same format word as
-// make_rsrc().  Reads at offsets >= nbytes return zero.
+// num_records = nbytes (clamped at 0), and word 3 = 0x00020000 (data format
+// 32 bits, no swizzle), the usual raw-access setting on gfx9 parts.  Reads at
+// offsets >= nbytes return zero.
 __device__ __forceinline__ i32x4_t rsrc_words(const bf16_t* base, long nbytes) {
     const uint64_t a = (uint64_t)base;
     const uint32_t n = nbytes <= 0 ? 0u : (uint32_t)nbytes;
@@ -1230,7 +896,7 @@ FfnWs ffn_layout(int R, int E, int f, moe_act act, moe_dtype dt, int backward) {
     return w;
 }
 
-template <int BM, int BN, int WM, int WN, bool DMA, int MODE, int ALAY, int BLAY, bool DUAL,
+template <int BM, int BN, int WM, int WN, int MODE, int ALAY, int BLAY, bool DUAL,
           bool KSPLIT, class Epi>
 void launch_bf16(GemmArgs<bf16_t> p, Epi epi, int R, hipStream_t s, const char* name) {
     p.nN = (p.N + BN - 1) / BN;
@@ -1249,14 +915,9 @@ void launch_bf16(GemmArgs<bf16_t> p, Epi epi, int R, hipStream_t s, const char* 
     if (p.xcd_run <= 0) p.xcd_run = MODE == RAGGED_M ? 32 : 8;
     const int pad = NXCD * p.xcd_run;                      // whole XCD runs
     blocks = (blocks + pad - 1) / pad * pad;
-    if constexpr (DMA)
-        MOE_LAUNCH(name, s,
-                   ggemm_bf16_dma_kernel<BM, BN, WM, WN, MODE, ALAY, BLAY, DUAL, KSPLIT, Epi>
-                   <<<blocks, 64 * WM * WN, 0, s>>>(p, epi));
-    else
-        MOE_LAUNCH(name, s,
-                   ggemm_bf16_kernel<BM, BN, WM, WN, MODE, ALAY, BLAY, DUAL, KSPLIT, Epi>
-                   <<<blocks, 64 * WM * WN, 0, s>>>(p, epi));
+    MOE_LAUNCH(name, s,
+               ggemm_bf16_dma_kernel<BM, BN, WM, WN, MODE, ALAY, BLAY, DUAL, KSPLIT, Epi>
+               <<<blocks, 64 * WM * WN, 0, s>>>(p, epi));
 }
 
 template <int MODE, int ALAY, int BLAY, bool DUAL, bool KSPLIT, class Epi>
@@ -1297,16 +958,15 @@ GemmArgs<T> base_args(const int32_t* offsets, const Plan& pl, int E) {
 // single-product GEMMs, for the dual-weight (SwiGLU up) product, and for the
 // tail launch of a split RAGGED_M product (BMT = 0: never split), in a wide
 // (BNT) and a narrow (BNN) column variant.
-template <int BM_, int BN_, int WM_, int WN_, int BND_, int WMD_, int WND_, bool DMA_ = false,
-          int BMT_ = 0, int BNT_ = 0, int WMT_ = 0, int WNT_ = 0, int BNN_ = 0, int WNN_ = 0>
+template <int BM_, int BN_, int WM_, int WN_, int BND_, int WMD_, int WND_, int BMT_ = 0,
+          int BNT_ = 0, int WMT_ = 0, int WNT_ = 0, int BNN_ = 0, int WNN_ = 0>
 struct TileCfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
     static constexpr int BND = BND_, WMD = WMD_, WND = WND_;
-    static constexpr bool DMA = DMA_;     // direct-to-LDS ring instead of register staging
     static constexpr int BMT = BMT_, BNT = BNT_, WMT = WMT_, WNT = WNT_;
     static constexpr int BNN = BNN_, WNN = WNN_;
 };
-using DefaultCfg = TileCfg<256, 256, 4, 2, 128, 4, 2, true, 64, 256, 1, 4, 128, 4>;
+using DefaultCfg = TileCfg<256, 256, 4, 2, 128, 4, 2, 64, 256, 1, 4, 128, 4>;
 
 // Wave quantisation.  A RAGGED_M product has between ceil(R/BM) and
 // ceil(R/BM) + E - 1 row tiles, since each expert's last tile is usually
@@ -1352,7 +1012,7 @@ struct Launch<bf16_t, Cfg> {
                    const char* tail_name = nullptr, hipStream_t ts = nullptr) {
         if (!ts) ts = s;           // stream of the tail launch
         if constexpr (DUAL) {
-            launch_bf16<Cfg::BM, Cfg::BND, Cfg::WMD, Cfg::WND, Cfg::DMA, MODE, ALAY, BLAY, DUAL,
+            launch_bf16<Cfg::BM, Cfg::BND, Cfg::WMD, Cfg::WND, MODE, ALAY, BLAY, DUAL,
                         KSPLIT>(p, epi, R, s, name);
             return false;
         } else {
@@ -1361,24 +1021,24 @@ struct Launch<bf16_t, Cfg> {
                     GemmArgs<bf16_t> q = p;
                     q.part_mode = 1;
                     q.bm_plan = Cfg::BM;
-                    launch_bf16<Cfg::BM, Cfg::BN, Cfg::WM, Cfg::WN, Cfg::DMA, MODE, ALAY, BLAY,
+                    launch_bf16<Cfg::BM, Cfg::BN, Cfg::WM, Cfg::WN, MODE, ALAY, BLAY,
                                 DUAL, KSPLIT>(q, epi, R, s, name);
                     q.part_mode = 2;
                     // expected live slices: about half of the slots of the partial tiles
                     const long slices = (long)min(p.E, R) * (Cfg::BM / Cfg::BMT) / 2;
                     if (Cfg::BNN > 0 && slices * cdiv(p.N, Cfg::BNT) < device_cus()) {
                         q.xcd_run = xcd_run_for(slices * cdiv(p.N, Cfg::BNN));
-                        launch_bf16<Cfg::BMT, Cfg::BNN, Cfg::WMT, Cfg::WNN, Cfg::DMA, MODE,
+                        launch_bf16<Cfg::BMT, Cfg::BNN, Cfg::WMT, Cfg::WNN, MODE,
                                     ALAY, BLAY, DUAL, KSPLIT>(q, epi, R, ts, tail_name);
                     } else {
                         q.xcd_run = xcd_run_for(slices * cdiv(p.N, Cfg::BNT));
-                        launch_bf16<Cfg::BMT, Cfg::BNT, Cfg::WMT, Cfg::WNT, Cfg::DMA, MODE,
+                        launch_bf16<Cfg::BMT, Cfg::BNT, Cfg::WMT, Cfg::WNT, MODE,
                                     ALAY, BLAY, DUAL, KSPLIT>(q, epi, R, ts, tail_name);
                     }
                     return true;
                 }
             }
-            launch_bf16<Cfg::BM, Cfg::BN, Cfg::WM, Cfg::WN, Cfg::DMA, MODE, ALAY, BLAY, DUAL,
+            launch_bf16<Cfg::BM, Cfg::BN, Cfg::WM, Cfg::WN, MODE, ALAY, BLAY, DUAL,
                         KSPLIT>(p, epi, R, s, name);
             return false;
         }
