@@ -383,22 +383,25 @@ __device__ __forceinline__ TileInfo decode_tile(const GemmArgs<T>& p) {
 // =====================================================================
 // Operand tiles go from HBM straight into LDS with buffer_load_dwordx4 ...
 // lds (each wave instruction fills 1 KB: lane l's 16 bytes land at base +
-// 16*l), through a ring of NSTG stages of BKD reduction steps, with no
+// 16*l), through a ring of NSTG stages of BK reduction steps, with no
 // register staging.  The descriptor's byte range covers exactly the valid
 // part of the tile, so lanes past a ragged segment end, the end of the
 // reduction, a partial tile or the allocation read zeros, with no branch.
 constexpr uint32_t OOB = 0x80000000u;    // an offset past any descriptor range
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
-constexpr int BKD = 32;
-constexpr int NSTG = 4;
 
-// K-major stage tile: rows of 32 bf16 (64 B), 16-byte chunks XOR-swizzled
-// by (row ^ row/4) mod 4 so that 16 consecutive rows hit distinct banks.
-__device__ __forceinline__ int swz32(int r, int c) {
-    return r * 64 + ((c ^ ((r ^ (r >> 2)) & 3)) << 4);
+
+// K-major stage tile: rows of BK bf16 (CH = BK/8 chunks of 16 B), chunk c of
+// row r stored at chunk c ^ ((r ^ r/CH) mod CH), so that the rows one
+// fragment read touches spread over distinct banks.
+template <int CH>
+__device__ __forceinline__ int swzk(int r, int c) {
+    constexpr int L = CH == 4 ? 2 : 3;
+    static_assert(CH == 4 || CH == 8, "32 or 64 reduction steps per stage");
+    return r * (CH * 16) + ((c ^ ((r ^ (r >> L)) & (CH - 1))) << 4);
 }
-// M/N-major stage tile: BKD rows of ROWS elements; chunk c of row k is
+// M/N-major stage tile: BK rows of ROWS elements; chunk c of row k is
 // stored at chunk c ^ 4*(k mod 4), which spreads the four rows a transposing
 // read touches over distinct banks.
 template <int ROWS>
@@ -434,10 +437,11 @@ __device__ __forceinline__ void lds_dma16(i32x4_t rs, uint32_t voff, uint32_t ld
         : "memory", "m0");
 }
 
-template <int ROWS, int LAY, int NT>
+template <int ROWS, int LAY, int NT, int BK>
 struct DmaOperand {
     static constexpr int NW = NT / 64;
-    static constexpr int TILE = ROWS * BKD * 2;           // bytes per stage
+    static constexpr int CH = BK / 8;                     // K-major: chunks per row
+    static constexpr int TILE = ROWS * BK * 2;            // bytes per stage
     static constexpr int NLOAD = TILE / 1024 / NW;        // 1 KB loads per wave
     static_assert(TILE % (1024 * NW) == 0, "tile/wave mismatch");
     static_assert(LAY == KMAJ || ROWS >= 128, "M/N-major swizzle needs 16 chunks per row");
@@ -459,8 +463,9 @@ struct DmaOperand {
         for (int i = 0; i < NLOAD; ++i) {
             const int blk = w + NW * i;                    // 1 KB block of the stage
             if (LAY == KMAJ) {
-                const int row = blk * 16 + (lane >> 2);
-                const int c = (lane & 3) ^ ((row ^ (row >> 2)) & 3);
+                constexpr int L = CH == 4 ? 2 : 3;
+                const int row = blk * (64 / CH) + lane / CH;
+                const int c = (lane % CH) ^ ((row ^ (row >> L)) & (CH - 1));
                 off[i] = (uint32_t)(row * ld * 2 + c * 16);
             } else {
                 constexpr int NC = ROWS / 8;               // chunks per row
@@ -480,7 +485,7 @@ struct DmaOperand {
             nbytes = (long)row_lim * ld * 2 - k0 * 2;
         } else {
             base = P + k0 * ld;
-            nbytes = min((long)BKD, k_lim - k0) * ld * 2;
+            nbytes = min((long)BK, k_lim - k0) * ld * 2;
         }
         const i32x4_t rs = rsrc_words(base, nbytes);
         const uint32_t lds0 = lds_addr(stage) + (uint32_t)((threadIdx.x >> 6) * 1024);
@@ -489,11 +494,11 @@ struct DmaOperand {
     }
 };
 
-template <int ROWS, int LAY>
+template <int ROWS, int LAY, int BK>
 __device__ __forceinline__ bf16x8 dma_frag(const uint8_t* lds, int row0, int ks, int lane) {
     if constexpr (LAY == KMAJ) {
         const uint4 v = *reinterpret_cast<const uint4*>(
-            lds + swz32(row0 + (lane & 31), ks * 2 + (lane >> 5)));
+            lds + swzk<BK / 8>(row0 + (lane & 31), ks * 2 + (lane >> 5)));
         return __builtin_bit_cast(bf16x8, v);
     } else {
         const int k = ks * 16 + (lane >> 5) * 8 + ((lane & 15) >> 2);
@@ -514,21 +519,30 @@ template <int N>
 __device__ __forceinline__ void stage_barrier() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
+// stage_barrier with `ahead` (0..MAXA, wave-uniform) later stages of NL loads
+// each allowed to stay in flight
+template <int NL, int MAXA>
+__device__ __forceinline__ void stage_barrier_ahead(int ahead) {
+    if constexpr (MAXA <= 0) {
+        stage_barrier<0>();
+    } else {
+        if (ahead >= MAXA) stage_barrier<NL * MAXA>();
+        else stage_barrier_ahead<NL, MAXA - 1>(ahead);
+    }
+}
 
-template <int BM, int BN, int WM, int WN, int MODE, int ALAY, int BLAY, bool DUAL,
-          bool KSPLIT, class Epi>
+template <int BM, int BN, int WM, int WN, int NSTG, int BK, int MODE, int ALAY, int BLAY,
+          bool DUAL, bool KSPLIT, class Epi>
 __global__ __launch_bounds__(64 * WM * WN, 1) void ggemm_bf16_dma_kernel(GemmArgs<bf16_t> p,
                                                                          Epi epi) {
     constexpr int NT = 64 * WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
     constexpr int NBT = DUAL ? 2 : 1;
-    constexpr int A_BYTES = BM * BKD * 2, B_BYTES = BN * BKD * 2;
+    constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
     constexpr int STAGE = A_BYTES + NBT * B_BYTES;
-    __shared__ __attribute__((aligned(1024))) uint8_t st0[STAGE];
-    __shared__ __attribute__((aligned(1024))) uint8_t st1[STAGE];
-    __shared__ __attribute__((aligned(1024))) uint8_t st2[STAGE];
-    __shared__ __attribute__((aligned(1024))) uint8_t st3[STAGE];
+    static_assert(NSTG >= 3 && STAGE % 1024 == 0 && NSTG * STAGE <= 160 * 1024, "ring size");
+    __shared__ __attribute__((aligned(1024))) uint8_t ringbuf[NSTG * STAGE];
 
     const TileInfo ti = decode_tile<MODE, BM, BN>(p);
     if (!ti.live) return;
@@ -536,9 +550,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ggemm_bf16_dma_kernel(GemmArg
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int wm = wv / WN, wn = wv % WN;
 
-    DmaOperand<BM, ALAY, NT> opA;
-    DmaOperand<BN, BLAY, NT> opB;
-    DmaOperand<BN, BLAY, NT> opB2;
+    DmaOperand<BM, ALAY, NT, BK> opA;
+    DmaOperand<BN, BLAY, NT, BK> opB;
+    DmaOperand<BN, BLAY, NT, BK> opB2;
     const bf16_t* bsplit[2];
     if (MODE == RAGGED_M) {
         opA.init(p.A + ti.r0 * p.lda, p.lda, ti.rows, p.K);
@@ -551,7 +565,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ggemm_bf16_dma_kernel(GemmArg
         opA.init(p.A + ti.kbeg * p.lda + ti.m0, p.lda, p.M - ti.m0, ti.klen);
         opB.init(p.B + ti.kbeg * p.ldb + ti.n0, p.ldb, p.N - ti.n0, ti.klen);
     }
-    constexpr int NL = DmaOperand<BM, ALAY, NT>::NLOAD + NBT * DmaOperand<BN, BLAY, NT>::NLOAD;
+    constexpr int NL = DmaOperand<BM, ALAY, NT, BK>::NLOAD + NBT * DmaOperand<BN, BLAY, NT, BK>::NLOAD;
+    static_assert(NL * (NSTG - 2) <= 63, "vmcnt counts at most 63 loads");
 
     f32x16 acc[FM][FN];
     f32x16 acc2[DUAL ? FM : 1][DUAL ? FN : 1];
@@ -571,7 +586,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ggemm_bf16_dma_kernel(GemmArg
     }
 
     auto issue = [&](uint8_t* stg, int j) {
-        const long k0 = (long)j * BKD;
+        const long k0 = (long)j * BK;
         opA.dma(k0, stg);
         if constexpr (KSPLIT) {
             const bool hi = k0 >= p.Ksplit;
@@ -585,7 +600,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ggemm_bf16_dma_kernel(GemmArg
     // Fragments are double-buffered across k-steps and across stages: the
     // first fragments of stage j+1 are read while the last MFMAs of stage j
     // run, so the matrix pipe never waits for a stage boundary.
-    constexpr int KS = BKD / 16;                       // MFMA k-steps per stage
+    constexpr int KS = BK / 16;                       // MFMA k-steps per stage
     static_assert(KS % 2 == 0, "fragment buffer parity assumes an even count");
     bf16x8 af[2][FM], bfr[2][FN], bf2[2][DUAL ? FN : 1];
     auto read_frags = [&](const uint8_t* stg, int ks, int buf) {
@@ -593,14 +608,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ggemm_bf16_dma_kernel(GemmArg
         const uint8_t* sB = stg + A_BYTES;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
-            af[buf][i] = dma_frag<BM, ALAY>(sA, wm * WTM + i * 32, ks, lane);
+            af[buf][i] = dma_frag<BM, ALAY, BK>(sA, wm * WTM + i * 32, ks, lane);
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-            bfr[buf][j] = dma_frag<BN, BLAY>(sB, wn * WTN + j * 32, ks, lane);
+            bfr[buf][j] = dma_frag<BN, BLAY, BK>(sB, wn * WTN + j * 32, ks, lane);
         if constexpr (DUAL) {
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                bf2[buf][j] = dma_frag<BN, BLAY>(sB + B_BYTES, wn * WTN + j * 32, ks, lane);
+                bf2[buf][j] = dma_frag<BN, BLAY, BK>(sB + B_BYTES, wn * WTN + j * 32, ks, lane);
         }
     };
     auto mfmas = [&](int buf) {
@@ -619,39 +634,38 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ggemm_bf16_dma_kernel(GemmArg
                         af[buf][i], bf2[buf][j], acc2[i][j], 0, 0, 0);
         }
     };
-    auto ring = [&](int q) -> uint8_t* {
-        return q == 0 ? st0 : q == 1 ? st1 : q == 2 ? st2 : st3;
-    };
-    // Ring of NSTG = 4 stages: while stage j is multiplied, stage j+1 has
-    // landed, j+2 is in flight and j+3 is issued once every wave is past the
-    // reads of stage j-1 (whose buffer it reuses).
-    const int nj = (ti.klen + BKD - 1) / BKD;
-    if (nj > 0) issue(st0, 0);
-    if (nj > 1) issue(st1, 1);
-    if (nj > 2) issue(st2, 2);
-    if (nj > 2) stage_barrier<2 * NL>();               // stage 0 landed
-    else if (nj > 1) stage_barrier<NL>();
-    else stage_barrier<0>();
-    if (nj > 0) read_frags(st0, 0, 0);
+    auto ring = [&](int q) -> uint8_t* { return ringbuf + q * STAGE; };
+    // Ring of NSTG stages: while stage j is multiplied, stage j+1 has
+    // landed, j+2 .. j+NSTG-2 are in flight, and j+NSTG-1 is issued once
+    // every wave is past the reads of stage j-1 (whose buffer it reuses).
+    const int nj = (ti.klen + BK - 1) / BK;
+#pragma unroll
+    for (int q = 0; q < NSTG - 1; ++q)
+        if (q < nj) issue(ring(q), q);
+    stage_barrier_ahead<NL, NSTG - 2>(min(nj - 1, NSTG - 2));   // stage 0 landed
+    if (nj > 0) read_frags(ring(0), 0, 0);
     // all stages but the last; the last one is peeled off so that the loop
     // body has one path and the compiler's LDS waits before its final MFMAs
     // do not cover the reads of the next stage
+    int qc = 0;                                        // ring slot of stage j
 #pragma unroll 1
     for (int j = 0; j + 1 < nj; ++j) {
-        const uint8_t* cur = ring(j & 3);
+        const uint8_t* cur = ring(qc);
+        const int qn = qc + 1 == NSTG ? 0 : qc + 1;    // slot of stage j+1
+        const int qf = qc == 0 ? NSTG - 1 : qc - 1;    // slot of stage j-1 = j+NSTG-1
 #pragma unroll
         for (int ks = 0; ks + 1 < KS; ++ks) {
             read_frags(cur, ks + 1, (ks + 1) & 1);
             mfmas(ks & 1);
         }
-        if (j + 2 < nj) stage_barrier<NL>();            // stage j+1 landed
-        else stage_barrier<0>();
-        if (j + 3 < nj) issue(ring((j + 3) & 3), j + 3);
-        read_frags(ring((j + 1) & 3), 0, 0);
+        stage_barrier_ahead<NL, NSTG - 3>(min(nj - 2 - j, NSTG - 3));  // stage j+1 landed
+        if (j + NSTG - 1 < nj) issue(ring(qf), j + NSTG - 1);
+        read_frags(ring(qn), 0, 0);
         mfmas((KS - 1) & 1);
+        qc = qn;
     }
     if (nj > 0) {
-        const uint8_t* cur = ring((nj - 1) & 3);
+        const uint8_t* cur = ring(qc);
 #pragma unroll
         for (int ks = 0; ks + 1 < KS; ++ks) {
             read_frags(cur, ks + 1, (ks + 1) & 1);
@@ -666,7 +680,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ggemm_bf16_dma_kernel(GemmArg
     constexpr int SLAB = 16 * LDW;                   // floats per wave half-slab
     constexpr int WPS = STAGE / (SLAB * NBT * 4);    // wave slabs per stage array
     static_assert(WPS * NSTG >= NT / 64, "epilogue slabs do not fit");
-    uint8_t* home = wv / WPS == 0 ? st0 : wv / WPS == 1 ? st1 : wv / WPS == 2 ? st2 : st3;
+    uint8_t* home = ring(wv / WPS);
     float* slab = reinterpret_cast<float*>(home) + (wv % WPS) * SLAB * NBT;
     constexpr int LPR = WTN / 8;
     constexpr int RPP = 64 / LPR;
@@ -896,8 +910,8 @@ FfnWs ffn_layout(int R, int E, int f, moe_act act, moe_dtype dt, int backward) {
     return w;
 }
 
-template <int BM, int BN, int WM, int WN, int MODE, int ALAY, int BLAY, bool DUAL,
-          bool KSPLIT, class Epi>
+template <int BM, int BN, int WM, int WN, int NSTG, int BK, int MODE, int ALAY, int BLAY,
+          bool DUAL, bool KSPLIT, class Epi>
 void launch_bf16(GemmArgs<bf16_t> p, Epi epi, int R, hipStream_t s, const char* name) {
     p.nN = (p.N + BN - 1) / BN;
     int blocks;
@@ -916,7 +930,8 @@ void launch_bf16(GemmArgs<bf16_t> p, Epi epi, int R, hipStream_t s, const char* 
     const int pad = NXCD * p.xcd_run;                      // whole XCD runs
     blocks = (blocks + pad - 1) / pad * pad;
     MOE_LAUNCH(name, s,
-               ggemm_bf16_dma_kernel<BM, BN, WM, WN, MODE, ALAY, BLAY, DUAL, KSPLIT, Epi>
+               ggemm_bf16_dma_kernel<BM, BN, WM, WN, NSTG, BK, MODE, ALAY, BLAY, DUAL, KSPLIT,
+                                     Epi>
                <<<blocks, 64 * WM * WN, 0, s>>>(p, epi));
 }
 
@@ -958,15 +973,28 @@ GemmArgs<T> base_args(const int32_t* offsets, const Plan& pl, int E) {
 // single-product GEMMs, for the dual-weight (SwiGLU up) product, and for the
 // tail launch of a split RAGGED_M product (BMT = 0: never split), in a wide
 // (BNT) and a narrow (BNN) column variant.
+// Ring<NS, BK>: an LDS ring of NS stages of BK reduction steps.
+template <int NS_, int BK_>
+struct Ring {
+    static constexpr int NS = NS_, BK = BK_;
+};
+// RM, RT, RN are the rings of the main, wide-tail and narrow-tail kernels.
 template <int BM_, int BN_, int WM_, int WN_, int BND_, int WMD_, int WND_, int BMT_ = 0,
-          int BNT_ = 0, int WMT_ = 0, int WNT_ = 0, int BNN_ = 0, int WNN_ = 0>
+          int BNT_ = 0, int WMT_ = 0, int WNT_ = 0, int BNN_ = 0, int WNN_ = 0,
+          class RM_ = Ring<4, 32>, class RT_ = Ring<4, 32>, class RN_ = Ring<4, 32>>
 struct TileCfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
     static constexpr int BND = BND_, WMD = WMD_, WND = WND_;
     static constexpr int BMT = BMT_, BNT = BNT_, WMT = WMT_, WNT = WNT_;
     static constexpr int BNN = BNN_, WNN = WNN_;
+    typedef RM_ RM;
+    typedef RT_ RT;
+    typedef RN_ RN;
 };
-using DefaultCfg = TileCfg<256, 256, 4, 2, 128, 4, 2, 64, 256, 1, 4, 128, 4>;
+// The narrow tail (64x128 slices, few MFMAs per stage) takes 64-deep stages
+// in a 5-stage ring: half the barriers of 32-deep ones, and 3 stages in flight.
+using DefaultCfg = TileCfg<256, 256, 4, 2, 128, 4, 2, 64, 256, 1, 4, 128, 4, Ring<4, 32>,
+                           Ring<4, 32>, Ring<5, 64>>;
 
 // Wave quantisation.  A RAGGED_M product has between ceil(R/BM) and
 // ceil(R/BM) + E - 1 row tiles, since each expert's last tile is usually
@@ -1012,7 +1040,7 @@ struct Launch<bf16_t, Cfg> {
                    const char* tail_name = nullptr, hipStream_t ts = nullptr) {
         if (!ts) ts = s;           // stream of the tail launch
         if constexpr (DUAL) {
-            launch_bf16<Cfg::BM, Cfg::BND, Cfg::WMD, Cfg::WND, MODE, ALAY, BLAY, DUAL,
+            launch_bf16<Cfg::BM, Cfg::BND, Cfg::WMD, Cfg::WND, Cfg::RM::NS, Cfg::RM::BK, MODE, ALAY, BLAY, DUAL,
                         KSPLIT>(p, epi, R, s, name);
             return false;
         } else {
@@ -1021,24 +1049,24 @@ struct Launch<bf16_t, Cfg> {
                     GemmArgs<bf16_t> q = p;
                     q.part_mode = 1;
                     q.bm_plan = Cfg::BM;
-                    launch_bf16<Cfg::BM, Cfg::BN, Cfg::WM, Cfg::WN, MODE, ALAY, BLAY,
+                    launch_bf16<Cfg::BM, Cfg::BN, Cfg::WM, Cfg::WN, Cfg::RM::NS, Cfg::RM::BK, MODE, ALAY, BLAY,
                                 DUAL, KSPLIT>(q, epi, R, s, name);
                     q.part_mode = 2;
                     // expected live slices: about half of the slots of the partial tiles
                     const long slices = (long)min(p.E, R) * (Cfg::BM / Cfg::BMT) / 2;
                     if (Cfg::BNN > 0 && slices * cdiv(p.N, Cfg::BNT) < device_cus()) {
                         q.xcd_run = xcd_run_for(slices * cdiv(p.N, Cfg::BNN));
-                        launch_bf16<Cfg::BMT, Cfg::BNN, Cfg::WMT, Cfg::WNN, MODE,
+                        launch_bf16<Cfg::BMT, Cfg::BNN, Cfg::WMT, Cfg::WNN, Cfg::RN::NS, Cfg::RN::BK, MODE,
                                     ALAY, BLAY, DUAL, KSPLIT>(q, epi, R, ts, tail_name);
                     } else {
                         q.xcd_run = xcd_run_for(slices * cdiv(p.N, Cfg::BNT));
-                        launch_bf16<Cfg::BMT, Cfg::BNT, Cfg::WMT, Cfg::WNT, MODE,
+                        launch_bf16<Cfg::BMT, Cfg::BNT, Cfg::WMT, Cfg::WNT, Cfg::RT::NS, Cfg::RT::BK, MODE,
                                     ALAY, BLAY, DUAL, KSPLIT>(q, epi, R, ts, tail_name);
                     }
                     return true;
                 }
             }
-            launch_bf16<Cfg::BM, Cfg::BN, Cfg::WM, Cfg::WN, MODE, ALAY, BLAY, DUAL,
+            launch_bf16<Cfg::BM, Cfg::BN, Cfg::WM, Cfg::WN, Cfg::RM::NS, Cfg::RM::BK, MODE, ALAY, BLAY, DUAL,
                         KSPLIT>(p, epi, R, s, name);
             return false;
         }
