@@ -76,11 +76,11 @@ int moe_abi_version(void);
 moe_status moe_init(int device);
 
 /*
- * moe_set_overlap -- whether the expert FFN calls may run launches that do
- * not depend on each other (the experts' partial last tiles, dW2) on a
- * library-owned side stream of the current device, concurrently with the
- * rest of the call on `stream` (enable != 0, the default), or run every
- * kernel in order on `stream` (enable = 0).  Either way a call is ordered on
+ * moe_set_overlap -- whether the expert FFN and gate backward calls may run
+ * launches that do not depend on each other (the experts' partial last
+ * tiles, dW2, dWg) on a library-owned side stream of the current device,
+ * concurrently with the rest of the call on `stream` (enable != 0, the
+ * default), or run every kernel in order on `stream` (enable = 0).  Either way a call is ordered on
  * `stream` as a whole (the side stream forks from it and joins back through
  * events) and the results are bit-identical.  Process-wide setting.
  * While kernel timing is enabled (moe_profile_enable) the library runs as

@@ -552,19 +552,24 @@ moe_status launch_gate_bwd(const void* x, const void* Wg, const float* logits,
         MOE_LAUNCH("gate_dlogits", s,
             gate_dlogits_kernel<<<cdiv(Tn, 4), 256, sizeof(int) * 4 * (size_t)E, s>>>(
                 logits, idx, w, dw, Tn, E, k, renorm, dl));
+    // dWg = x^T dl (side stream) and dx += dl Wg^T (caller's stream) only
+    // share dl: they run side by side and join before the call returns
+    SideStream side(s);
+    hipStream_t ss = side.ok() ? side.get() : s;
     const DwgSplit z = dwg_split(Tn, d, E);
     dim3 g(cdiv(z.nft, 4), z.net, z.nchunk);
-    MOE_LAUNCH("gate_dwg_partial", s,
-        gate_dwg_partial_kernel<T><<<g, 256, 0, s>>>(xp, dl, Tn, d, E, z.tc, z.nft, partial));
+    MOE_LAUNCH("gate_dwg_partial", ss,
+        gate_dwg_partial_kernel<T><<<g, 256, 0, ss>>>(xp, dl, Tn, d, E, z.tc, z.nft, partial));
     const long n = (long)d * E;
-    MOE_LAUNCH("gate_dwg_reduce", s,
-        gate_dwg_reduce_kernel<T><<<cdiv(n / 4, 256 / DW_RG), 256, 0, s>>>(
+    MOE_LAUNCH("gate_dwg_reduce", ss,
+        gate_dwg_reduce_kernel<T><<<cdiv(n / 4, 256 / DW_RG), 256, 0, ss>>>(
             partial, z.nchunk, n, static_cast<T*>(dWg)));
     const size_t lds_dx = renorm ? sizeof(float) * 2 * (size_t)k : sizeof(float) * (size_t)E;
     if (Tn > 0)     // no tokens: dWg is zero (one empty chunk), dx is empty
         MOE_LAUNCH("gate_dx", s,
             gate_dx_kernel<T><<<Tn, 256, lds_dx + 16, s>>>(wgt, dl, idx, w, dw, d, E, k,
                                                             renorm, static_cast<T*>(dx)));
+    if (side.ok() && !side.join()) return MOE_ERR_HIP;
     return launch_status();
 }
 
