@@ -33,13 +33,13 @@ PEAK_HBM_GBS = 8000.0
 # of a plain 1 GiB device copy in the same run (factors 4.0 and 1.0); see
 # profiles/hbm_traffic_moe_s_like.md.  Valid only for the kernel sources
 # whose SHA-256 prefix is TRAFFIC_SRC; null once they change.
-TRAFFIC_SRC = "c78e40a0e2abf1b3"
+TRAFFIC_SRC = "49ef3edcf3484ea6"
 TRAFFIC_SOURCES = ("ggemm.hip", "common.h", "permute.hip", "combine.hip")
-TRAFFIC = {"gemm_up_gelu": 916850469, "gemm_down": 738626498,
-           "gemm_dA_gelu": 1074931522, "gemm_dW1": 1073908219,
-           "gemm_dW2": 1073908219, "gemm_dX": 738584671, "perm_copy": 67711455,
-           "combine": 84996038, "combine_bwd": 135486675,
-           "unpermute_grad": 84478657}
+TRAFFIC = {"gemm_up_gelu": 916631790, "gemm_down": 738623759,
+           "gemm_dA_gelu": 1074256118, "gemm_dW1": 1073913371,
+           "gemm_dW2": 1073913371, "gemm_dX": 738611932, "perm_copy": 67712928,
+           "combine": 84996629, "combine_bwd": 135487186,
+           "unpermute_grad": 84479193}
 
 
 def traffic_for(kernel, workload):
