@@ -91,7 +91,54 @@ def parse():
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB before the "
                          "steps (a known-size reference for HBM byte counters)")
+    ap.add_argument("--flush-mall", action="store_true",
+                    help="add a per-kernel pass that reads a 512 MiB buffer before "
+                         "every entry point, so memory kernels read from HBM")
     return ap.parse_args()
+
+
+def stream_copy_gbs(torch, mib=1024, reps=5):
+    """Measured device copy bandwidth (read + write bytes / time), the
+    reference for the memory kernels' GB/s."""
+    n = (mib << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2.0 * (mib << 20) / (ms * 1e-3) / 1e9
+
+
+def parity(cfg, layer, fw, gr):
+    """max|gpu - oracle| / max|oracle| per output of the step, against the
+    oracle run of the CPU baseline (same inputs), with the test tolerance."""
+    import numpy as np
+    tol = 2e-2 if cfg.dtype == "bf16" else 1e-5
+    pairs = {"y": (layer.y, fw["y"]), "dx": (layer.dx, gr["dx"]),
+             "dW1": (layer.dW1, gr["dW1"]), "dW2": (layer.dW2, gr["dW2"]),
+             "dWg": (layer.dWg, gr["dWg"])}
+    out, ok = {}, True
+    for n, (g, r) in pairs.items():
+        g = g.float().cpu().numpy().astype(np.float64).reshape(np.shape(r))
+        r = np.asarray(r, dtype=np.float64)
+        den = float(np.abs(r).max())
+        e = float(np.abs(g - r).max()) / den if den > 0 else float(np.abs(g).max())
+        out[n] = round(e, 6)
+        ok = ok and e <= tol
+    idx_ok = bool(np.array_equal(layer.topk_idx.cpu().numpy(), fw["idx"]))
+    out["topk_idx_exact"] = idx_ok
+    out["tolerance"] = tol
+    out["pass"] = bool(ok and idx_ok)
+    return out
 
 
 def cpu_baseline(cfg, budget_s):
@@ -116,8 +163,8 @@ def cpu_baseline(cfg, budget_s):
         t0 = time.perf_counter()
         fw = oracle.layer_forward(x, Wg, W1, W2, W3, k=cfg.k, act=cfg.act,
                                   bias=bias, renorm=cfg.renorm)
-        oracle.layer_backward(fw, dy, x, Wg, W1, W2, W3, act=cfg.act,
-                              renorm=cfg.renorm)
+        gr = oracle.layer_backward(fw, dy, x, Wg, W1, W2, W3, act=cfg.act,
+                                   renorm=cfg.renorm)
         t_tot += time.perf_counter() - t0
         reps += 1
         if t_tot >= budget_s or reps >= 5:
@@ -127,7 +174,16 @@ def cpu_baseline(cfg, budget_s):
     return {"value": reps * Ts / t_tot, "unit": "tokens/s", "cores": cores,
             "kind": "oracle",
             "sample": "NumPy float64 oracle, full layer fwd+bwd of all %d tokens "
-                      "(%d rep%s, %.1f s)" % (Ts, reps, "s" if reps > 1 else "", t_tot)}
+                      "(%d rep%s, %.1f s)" % (Ts, reps, "s" if reps > 1 else "", t_tot)}, fw, gr
+
+
+def load_stats(counts, cfg):
+    """Per-expert row counts of the routing the step ran on."""
+    c = sorted(int(v) for v in counts.cpu().tolist())
+    return {"max_over_mean": round(c[-1] * cfg.E / cfg.R, 3),
+            "empty_experts": sum(1 for v in c if v == 0),
+            "rows_min": c[0], "rows_median": c[len(c) // 2], "rows_max": c[-1],
+            "zipf_s": cfg.zipf_s}
 
 
 def main():
@@ -180,6 +236,19 @@ def main():
     wall = time.perf_counter() - w0
     ms = ev0.elapsed_time(ev1) / args.steps
 
+    # ---- step-time distribution: an event pair around every step
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a, b in evs:
+        a.record(stream)
+        layer.step(s)
+        b.record(stream)
+    torch.cuda.synchronize()
+    step_ms = sorted(a.elapsed_time(b) for a, b in evs)
+
+    def pct(q):
+        return step_ms[min(len(step_ms) - 1, int(q * (len(step_ms) - 1) + 0.5))]
+
     # ---- per-kernel pass: HIP events around every launch, same K steps
     L = _lib.load()
     _lib.check(L.moe_profile_enable(args.steps * 40), "moe_profile_enable")
@@ -191,6 +260,27 @@ def main():
     per = {}
     for name, kms in recs:
         per.setdefault(name, []).append(kms)
+
+    # ---- optional pass with the MALL flushed before every entry point
+    flushed = {}
+    if args.flush_mall:
+        # reading 512 MiB evicts the 256 MB MALL with clean lines (a write
+        # would leave dirty lines to be written back during the next kernel)
+        junk = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+        calls = layer.stage_calls()
+        nsteps = max(1, min(args.steps, 10))
+        _lib.check(L.moe_profile_enable(nsteps * 40), "moe_profile_enable")
+        for _ in range(nsteps):
+            for _, call in calls:
+                junk.sum()
+                call()
+        torch.cuda.synchronize()
+        for name, kms in _lib.profile_records():
+            flushed.setdefault(name, []).append(kms)
+        L.moe_profile_disable()
+        del junk
+        torch.cuda.empty_cache()
+    copy_gbs = stream_copy_gbs(torch)
     work = kernel_work(cfg)
     kernels = {}
     for name, v in per.items():
@@ -226,6 +316,12 @@ def main():
         else:
             ent["gbs"] = round(amt / (per_call * 1e-3) / 1e9, 1)
             ent["frac_of_peak"] = round(ent["gbs"] / PEAK_HBM_GBS, 4)
+            ent["frac_of_copy"] = round(ent["gbs"] / copy_gbs, 4)
+            # working set under the 256 MB MALL: the rate is cache-assisted
+            ent["cache_resident"] = amt < 256e6
+            if base in flushed:
+                fms = sum(flushed[base]) / len(flushed[base])
+                ent["gbs_mall_flushed"] = round(amt / (fms * 1e-3) / 1e9, 1)
     gemm_flops = cfg.gemm_flops_fwd_bwd()
     dom = max(stage_ms, key=lambda n: stage_ms[n] * kernels.get(n, {}).get(
         "launches_per_step", 1.0))
@@ -267,13 +363,18 @@ def main():
         "gemm_frac_of_bf16_peak": round(gemm_flops / (gemm_ms * 1e-3) / 1e12
                                         / PEAK_BF16_TFLOPS, 4) if gemm_ms else None,
         "wall_s_timed_region": round(wall, 4),
+        "step_ms": {"p10": round(pct(0.1), 5), "p50": round(pct(0.5), 5),
+                    "p90": round(pct(0.9), 5)},
+        "value_at_median_step": round(cfg.T / (pct(0.5) * 1e-3), 1),
+        "stream_copy_gbs": round(copy_gbs, 1),
         "roofline": roof,
         "kernels": kernels,
-        "load": {"max_over_mean": round(float(layer.counts.max()) * cfg.E / cfg.R, 3),
-                 "empty_experts": int((layer.counts == 0).sum())},
+        "load": load_stats(layer.counts, cfg),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+        base, fw, gr = cpu_baseline(cfg, args.cpu_seconds)
+        base["parity"] = parity(cfg, layer, fw, gr)
+        out["cpu_baseline"] = base
     print(json.dumps(out), flush=True)
 
 
