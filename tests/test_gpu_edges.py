@@ -1,0 +1,176 @@
+"""Edge cases of the whole layer, bit-for-bit determinism, and randomized
+gate/permute cases, all against the oracle on the host copy of the inputs.
+
+* E = 1: the layer reduces to one MLP applied to every token.
+* Every token routed to one expert (a large logit bias on it).
+* k = E: every token visits every expert.
+* T = 1 and a token count that is no multiple of any tile.
+* Two runs of the same step give identical bits (no float atomics, fixed
+  reduction orders), with side-stream overlap on.
+* Randomized (T, d, E, k, skew) for the gate and the permute, bit-exact
+  routing (a fixed number of seeded draws).
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_permute_amd as M
+import oracle
+from moe_inputs import CONFIGS, device, rng, small_variant, stage
+
+from _gpu import (assert_close, assert_equal_i, banner, dev, dev_i32, host,
+                  needs_gpu, saved_state)
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+
+def layer_case(cfg, bias=None):
+    """Run the layer on the workload's seeded inputs (bias overrides the
+    workload's own) and the oracle on their host copy; compare everything."""
+    t = device.gen_all(cfg)
+    if bias is not None:
+        t["bias"] = torch.from_numpy(bias).cuda()
+    layer = M.MoELayer(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.act,
+                       device.torch_dtype(cfg), cfg.renorm)
+    layer.bind(t["x"], t["Wg"], t["W1"], t["W2"], t["W3"], t["bias"], t["dy"])
+    layer.step()
+    torch.cuda.synchronize()
+    x, Wg, dy = (rng.gen(cfg, n) for n in ("x", "Wg", "dy"))
+    W1, W2 = rng.gen_experts(cfg, "W1"), rng.gen_experts(cfg, "W2")
+    W3 = rng.gen_experts(cfg, "W3") if cfg.swiglu else None
+    b = bias if bias is not None else rng.logit_bias(cfg)
+    fw = oracle.layer_forward(x, Wg, W1, W2, W3, k=cfg.k, act=cfg.act, bias=b,
+                              renorm=cfg.renorm)
+    gr = oracle.layer_backward(fw, dy, x, Wg, W1, W2, W3, act=cfg.act, renorm=cfg.renorm)
+    dt = cfg.dtype
+    assert_equal_i(layer.logits.cpu().numpy().view(np.uint32),
+                   fw["logits"].view(np.uint32), "logits")
+    assert_equal_i(layer.topk_idx, fw["idx"], "topk_idx")
+    for n in ("counts", "offsets", "dest", "src"):
+        assert_equal_i(getattr(layer, n), fw[n], n)
+    assert_close(layer.topk_w, fw["w"], "f32", "topk_w")
+    assert_close(layer.h_save, saved_state(cfg.act, fw["H"], fw.get("H3")), dt, "saved")
+    assert_close(layer.a_save, fw["A"], dt, "A")
+    assert_close(layer.y, fw["y"], dt, "y")
+    assert_close(layer.dx_perm, gr["dx_perm"], dt, "dx_perm")
+    assert_close(layer.dW1, gr["dW1"], dt, "dW1")
+    assert_close(layer.dW2, gr["dW2"], dt, "dW2")
+    if cfg.swiglu:
+        assert_close(layer.dW3, gr["dW3"], dt, "dW3")
+    assert_close(layer.dx, gr["dx"], dt, "dx")
+    if np.abs(gr["dWg"]).max() > 0:
+        assert_close(layer.dWg, gr["dWg"], dt, "dWg")
+    else:       # top-1 with renormalised weights: the gate gets no gradient
+        assert float(layer.dWg.abs().max()) == 0.0
+    return layer, fw
+
+
+def small(name="moe_s_like", **kw):
+    base = dict(T=300, d=128, f=256, E=8, k=2, zipf_s=None, alpha=0.0)
+    base.update(kw)
+    return small_variant(name, **base)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_one_expert_is_an_mlp(dt):
+    cfg = small(E=1, k=1, dtype=dt)
+    banner("edge E=1", dt)
+    layer, fw = layer_case(cfg)
+    assert int(layer.counts[0]) == cfg.T
+    # with one expert the layer is y = GeLU(x W1) W2 for every token
+    x = rng.gen(cfg, "x")
+    W1, W2 = rng.gen(cfg, "W1", 0), rng.gen(cfg, "W2", 0)
+    mlp = oracle.gelu(x.astype(np.float64) @ W1) @ W2
+    assert_close(layer.y, mlp, dt, "y = MLP(x)")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_all_tokens_to_one_expert(dt):
+    cfg = small(E=8, k=1, T=517, dtype=dt)
+    bias = np.zeros(cfg.E, np.float32)
+    bias[5] = 1000.0                    # every token's top-1 is expert 5
+    banner("edge all to one", dt)
+    layer, _ = layer_case(cfg, bias)
+    counts = layer.counts.cpu().numpy()
+    assert counts[5] == cfg.T and counts.sum() == cfg.T
+    for e in range(cfg.E):              # the other experts get exact zero gradients
+        if e != 5:
+            assert float(layer.dW1[e].abs().max()) == 0.0
+            assert float(layer.dW2[e].abs().max()) == 0.0
+
+
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
+def test_k_equals_e(act):
+    cfg = small("long_ctx_swiglu" if act == "swiglu" else "moe_s_like", E=4, k=4, T=203,
+                act=act, dtype="bf16")
+    banner("edge k=E", act)
+    layer, _ = layer_case(cfg)
+    assert np.all(layer.counts.cpu().numpy() == cfg.T)
+
+
+@pytest.mark.parametrize("T", [1, 17, 1031])
+def test_token_counts(T):
+    cfg = small(T=T, E=6, k=2, dtype="bf16")
+    banner("edge T", T)
+    layer_case(cfg)
+
+
+def test_step_is_deterministic():
+    """Two runs of the same step, side-stream overlap on, give identical bits."""
+    cfg = CONFIGS["many_expert_zipf1.0"]
+    cfg = small_variant(cfg.name, T=4096)
+    banner("determinism", cfg.short())
+    t = device.gen_all(cfg)
+    outs = []
+    for _ in range(2):
+        layer = M.MoELayer(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.act,
+                           device.torch_dtype(cfg), cfg.renorm)
+        layer.bind(t["x"], t["Wg"], t["W1"], t["W2"], t["W3"], t["bias"], t["dy"])
+        layer.step()
+        layer.step()
+        torch.cuda.synchronize()
+        outs.append({n: getattr(layer, n).clone() for n in
+                     ("logits", "topk_w", "x_perm", "h_save", "a_save", "out_perm", "y",
+                      "d_out_perm", "d_topk_w", "dx_perm", "dW1", "dW2", "dx", "dWg")})
+        del layer
+    for n in outs[0]:
+        assert torch.equal(outs[0][n], outs[1][n]), n
+
+
+# ------------------------------------------------------- randomized cases
+
+def _draws(n, seed):
+    g = np.random.default_rng(seed)
+    for _ in range(n):
+        E = int(g.integers(1, 80))
+        k = int(g.integers(1, min(E, 8) + 1))
+        T = int(g.integers(1, 400))
+        d = int(g.choice([8, 16, 64, 136]))
+        skew = float(g.choice([0.0, 0.5, 0.95]))
+        yield T, d, E, k, skew, int(g.integers(0, 2**31))
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_random_gate_and_permute(dt):
+    for T, d, E, k, skew, seed in _draws(24, 4242 if dt == "bf16" else 4343):
+        banner("random", T, d, E, k, skew, dt)
+        x = stage.normal(seed, (T, d), 1.0, dt)
+        Wg = stage.normal(seed + 1, (d, E), 1.0 / np.sqrt(d), dt)
+        bias = np.zeros(E, np.float32)
+        if skew > 0:                       # one hot expert takes most first choices
+            bias[seed % E] = 4.0 * skew
+        lg, idx, w = M.moe_gate_topk(dev(x, dt), dev(Wg, dt), k, dev(bias), 1)
+        ref_l = oracle.gate_logits(x, Wg, bias)
+        ref_i = oracle.topk_select(ref_l, k)
+        assert_equal_i(lg.cpu().numpy().view(np.uint32), ref_l.view(np.uint32), "logits")
+        assert_equal_i(idx, ref_i, "topk_idx")
+        assert_close(w, oracle.gate_weights(ref_l, ref_i, 1), "f32", "topk_w")
+        counts, offsets, dest, src, xp = M.moe_permute(idx, dev(x, dt), E)
+        torch.cuda.synchronize()
+        rc, ro, rd, rs = oracle.permute(ref_i, E)
+        assert_equal_i(counts, rc, "counts")
+        assert_equal_i(offsets, ro, "offsets")
+        assert_equal_i(dest, rd, "dest")
+        assert_equal_i(src, rs, "src")
+        got = host(xp)
+        assert np.array_equal(got, oracle.dispatch_rows(x, rs)), "x_perm"
