@@ -82,14 +82,16 @@ struct NormCP {
     float cdf, pdf;
 };
 __device__ __forceinline__ NormCP norm_fast(float z) {
-    constexpr float P = 0.3275911f;
-    constexpr float A1 = 0.254829592f, A2 = -0.284496736f, A3 = 1.421413741f,
-                    A4 = -1.453152027f, A5 = 1.061405429f;
-    const float x = fabsf(z) * 0.70710678118654752f;
-    const float t = __builtin_amdgcn_rcpf(fmaf(P, x, 1.0f));
-    const float poly = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, A5, A4), A3), A2), A1);
+    // p/sqrt(2) takes |z| straight to 1 + p x; the coefficients are halved
+    // (exactly, a power of two) so that the sum is Q(|z|) = erfc(x) / 2.
+    constexpr float PS = 0.3275911f * 0.70710678118654752f;
+    constexpr float H1 = 0.5f * 0.254829592f, H2 = 0.5f * -0.284496736f,
+                    H3 = 0.5f * 1.421413741f, H4 = 0.5f * -1.453152027f,
+                    H5 = 0.5f * 1.061405429f;
+    const float t = __builtin_amdgcn_rcpf(fmaf(fabsf(z), PS, 1.0f));
+    const float q = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, H5, H4), H3), H2), H1);
     const float g = __builtin_amdgcn_exp2f(z * z * -0.72134752044448170f);  // e^(-z^2/2)
-    const float tail = 0.5f * poly * g;                                       // Q(|z|)
+    const float tail = q * g;                                                 // Q(|z|)
     return {z >= 0.0f ? 1.0f - tail : tail, 0.3989422804014327f * g};
 }
 __device__ __forceinline__ float sigmoid_fast(float z) {
@@ -533,7 +535,7 @@ __device__ __forceinline__ void stage_barrier_ahead(int ahead) {
 
 template <int BM, int BN, int WM, int WN, int NSTG, int BK, int MODE, int ALAY, int BLAY,
           bool DUAL, bool KSPLIT, class Epi>
-__global__ __launch_bounds__(64 * WM * WN, 1) void ggemm_bf16_dma_kernel(GemmArgs<bf16_t> p,
+__global__ __launch_bounds__(64 * WM * WN, 2) void ggemm_bf16_dma_kernel(GemmArgs<bf16_t> p,
                                                                          Epi epi) {
     constexpr int NT = 64 * WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -635,9 +637,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ggemm_bf16_dma_kernel(GemmArg
         }
     };
     auto ring = [&](int q) -> uint8_t* { return ringbuf + q * STAGE; };
-    // Ring of NSTG stages: while stage j is multiplied, stage j+1 has
-    // landed, j+2 .. j+NSTG-2 are in flight, and j+NSTG-1 is issued once
-    // every wave is past the reads of stage j-1 (whose buffer it reuses).
+    // Ring of NSTG stages.  Every read of stage j-1 has returned once the
+    // waves meet at the barrier of stage j-1 (fragments go to registers),
+    // so stage j+NSTG-1 is issued into that slot at the top of stage j,
+    // away from the barrier and behind the MFMAs still in the pipe: while
+    // stage j is multiplied, j+1 .. j+NSTG-1 are landing.
     const int nj = (ti.klen + BK - 1) / BK;
 #pragma unroll
     for (int q = 0; q < NSTG - 1; ++q)
@@ -653,13 +657,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ggemm_bf16_dma_kernel(GemmArg
         const uint8_t* cur = ring(qc);
         const int qn = qc + 1 == NSTG ? 0 : qc + 1;    // slot of stage j+1
         const int qf = qc == 0 ? NSTG - 1 : qc - 1;    // slot of stage j-1 = j+NSTG-1
+        if (j + NSTG - 1 < nj) issue(ring(qf), j + NSTG - 1);
 #pragma unroll
         for (int ks = 0; ks + 1 < KS; ++ks) {
             read_frags(cur, ks + 1, (ks + 1) & 1);
             mfmas(ks & 1);
         }
-        stage_barrier_ahead<NL, NSTG - 3>(min(nj - 2 - j, NSTG - 3));  // stage j+1 landed
-        if (j + NSTG - 1 < nj) issue(ring(qf), j + NSTG - 1);
+        stage_barrier_ahead<NL, NSTG - 2>(min(nj - 2 - j, NSTG - 2));  // stage j+1 landed
         read_frags(ring(qn), 0, 0);
         mfmas((KS - 1) & 1);
         qc = qn;
