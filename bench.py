@@ -30,16 +30,16 @@ PEAK_HBM_GBS = 8000.0
 # HBM bytes per call (fetch + write; a GEMM stage's main and partial-tile
 # launches together) of the FFN and row kernels on the MoE-S-like workload,
 # from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs scaled by the readings
-# of a plain 1 GiB device copy in the same run (factors 4.0 and 1.0); see
+# of a plain 1 GiB device copy in the same run (factors 6.0 and 1.0); see
 # profiles/hbm_traffic_moe_s_like.md.  Valid only for the kernel sources
 # whose SHA-256 prefix is TRAFFIC_SRC; null once they change.
-TRAFFIC_SRC = "49ef3edcf3484ea6"
+TRAFFIC_SRC = "4a5f1442bdce1af8"
 TRAFFIC_SOURCES = ("ggemm.hip", "common.h", "permute.hip", "combine.hip")
-TRAFFIC = {"gemm_up_gelu": 916631790, "gemm_down": 738623759,
-           "gemm_dA_gelu": 1074256118, "gemm_dW1": 1073913371,
-           "gemm_dW2": 1073913371, "gemm_dX": 738611932, "perm_copy": 67712928,
-           "combine": 84996629, "combine_bwd": 135487186,
-           "unpermute_grad": 84479193}
+TRAFFIC = {"gemm_up_gelu": 1243298119, "gemm_down": 1091191270,
+           "gemm_dA_gelu": 1544264804, "gemm_dW1": 1577256126,
+           "gemm_dW2": 1577256126, "gemm_dX": 1091132523, "perm_copy": 84789385,
+           "combine": 119104451, "combine_bwd": 186418194,
+           "unpermute_grad": 118328733}
 
 
 def traffic_for(kernel, workload):
@@ -91,6 +91,13 @@ def parse():
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB before the "
                          "steps (a known-size reference for HBM byte counters)")
+    ap.add_argument("--fuse-gather", action="store_true",
+                    help="headline layer reads x through src inside the expert "
+                         "GEMMs (no x_perm, no row-copy kernel); by default that "
+                         "variant is timed after the headline as fused_gather")
+    ap.add_argument("--no-fused-pass", action="store_true",
+                    help="skip the fused_gather timing (profiler runs: one kernel "
+                         "variant per name)")
     ap.add_argument("--flush-mall", action="store_true",
                     help="add a per-kernel pass that reads a 512 MiB buffer before "
                          "every entry point, so memory kernels read from HBM")
@@ -204,7 +211,7 @@ def main():
     M.moe_set_overlap(not args.serial)
     t = device.gen_all(cfg)
     layer = M.MoELayer(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.act,
-                       device.torch_dtype(cfg), cfg.renorm)
+                       device.torch_dtype(cfg), cfg.renorm, fuse_gather=args.fuse_gather)
     layer.bind(t["x"], t["Wg"], t["W1"], t["W2"], t["W3"], t["bias"], t["dy"])
     stream = torch.cuda.current_stream()
     s = stream.cuda_stream
@@ -356,7 +363,8 @@ def main():
         "data": "synthetic (seeded counter-based generator, inputs resident in HBM)",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "f": cfg.f,
                    "E": cfg.E, "k": cfg.k, "act": cfg.act, "renorm": cfg.renorm,
-                   "routing_skew_zipf_s": cfg.zipf_s, "stream_overlap": not args.serial},
+                   "routing_skew_zipf_s": cfg.zipf_s, "stream_overlap": not args.serial,
+                   "fused_gather": args.fuse_gather},
         "gemm_tflops_layer": round(gemm_flops / (ms * 1e-3) / 1e12, 2),
         "gemm_tflops_kernels": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 2)
         if gemm_ms else None,
@@ -375,6 +383,30 @@ def main():
         base, fw, gr = cpu_baseline(cfg, args.cpu_seconds)
         base["parity"] = parity(cfg, layer, fw, gr)
         out["cpu_baseline"] = base
+    if not args.fuse_gather and not args.no_fused_pass:
+        # the same step with the row copy fused into the expert GEMMs (its
+        # results are bit-identical: tests/test_gpu_gather.py); timed after
+        # the headline layer is freed, so that both never share HBM
+        y0 = layer.y.clone()
+        del layer
+        torch.cuda.empty_cache()
+        fl = M.MoELayer(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.act,
+                        device.torch_dtype(cfg), cfg.renorm, fuse_gather=True)
+        fl.bind(t["x"], t["Wg"], t["W1"], t["W2"], t["W3"], t["bias"], t["dy"])
+        for _ in range(args.warmup):
+            fl.step(s)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            fl.step(s)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        fms = ev0.elapsed_time(ev1) / args.steps
+        out["fused_gather"] = {"ms_per_step": round(fms, 5),
+                               "value": round(cfg.T / (fms * 1e-3), 1),
+                               "y_bit_identical": bool(torch.equal(y0, fl.y)),
+                               "x_perm_bytes_not_allocated": cfg.T * cfg.k * cfg.d
+                               * (2 if cfg.dtype == "bf16" else 4)}
     print(json.dumps(out), flush=True)
 
 

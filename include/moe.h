@@ -122,6 +122,8 @@ moe_status moe_gate_topk(const void *x, const void *Wg, const float *logit_bias,
  * layout by expert).
  *   topk_idx [T,k] int32 (each row: k distinct experts in [0,E)), x [T,d] dt,
  *   counts [E], offsets [E+1], dest [T,k], src [T*k] int32, x_perm [T*k,d] dt.
+ *   x_perm == NULL skips the row copy (x may then be NULL too): routing only,
+ *   for the *_gather FFN entry points, which read x through src.
  *   ws: device workspace of at least moe_permute_workspace_bytes(T,E,k).
  * Entries of topk_idx outside [0,E) give MOE_ERR_INVALID_ARG only if detected
  * on the host; the kernels skip them (their dest entries are then undefined).
@@ -179,6 +181,39 @@ moe_status moe_expert_ffn_bwd(const void *d_out_perm, const void *x_perm,
                               const void *W3, const void *W2, void *dx_perm,
                               void *dW1, void *dW3, void *dW2, void *ws,
                               size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_expert_ffn_fwd_gather / moe_expert_ffn_bwd_gather -- the products of
+ * moe_expert_ffn_fwd / moe_expert_ffn_bwd with the permute's row copy fused
+ * into the operand loads: permuted row r is read as x[src[r],:] straight from
+ * the token-order input, so no x_perm buffer is written or read.  GEMM1 and
+ * dW1 (dW3) gather their rows while loading tiles; every result is bit-
+ * identical to moe_permute's copy followed by the plain entry points.
+ * Sources: ES-MoE review, 三 技术架构 / 专家级卸载与处理 (token permutation
+ * overlapped with the expert work; no dispatch buffer); FastMoE review,
+ * 제안 방법 (scatter/gather layout to reduce data movement).
+ *   x [T,d] dt (16-byte aligned), src [R] int32 from moe_permute, every entry
+ *   in [0,T) (a precondition: not checked on the device).  Other arguments
+ *   as in the plain entry points; same workspace sizes.
+ *   bf16 needs T*d*2 < 2^31 bytes (32-bit buffer offsets): MOE_ERR_UNSUPPORTED
+ *   otherwise.
+ */
+moe_status moe_expert_ffn_fwd_gather(const void *x, const int32_t *src,
+                                     const int32_t *offsets, int T, int R, int E,
+                                     int d, int f, moe_act act, moe_dtype dt,
+                                     const void *W1, const void *W3,
+                                     const void *W2, void *h_save, void *a_save,
+                                     void *out_perm, void *ws, size_t ws_bytes,
+                                     hipStream_t stream);
+moe_status moe_expert_ffn_bwd_gather(const void *d_out_perm, const void *x,
+                                     const int32_t *src, const void *h_save,
+                                     const void *a_save, const int32_t *offsets,
+                                     int T, int R, int E, int d, int f,
+                                     moe_act act, moe_dtype dt, const void *W1,
+                                     const void *W3, const void *W2,
+                                     void *dx_perm, void *dW1, void *dW3,
+                                     void *dW2, void *ws, size_t ws_bytes,
+                                     hipStream_t stream);
 
 /*
  * moe_combine -- y[t,:] = sum_{j=0..k-1} topk_w[t,j] * out_perm[dest[t,j],:],

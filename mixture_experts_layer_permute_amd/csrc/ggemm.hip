@@ -56,6 +56,11 @@ struct GemmArgs {
                          // 2 partial tiles cut into BM-row slices
     int bm_plan;         // row tile of the plan (part_mode 2)
     int xcd_run;         // logical tiles per XCD run (block -> tile remap)
+    // Row gather of the A operand (NULL: none).  RAGGED_M: row r of the
+    // expert-ordered A is A[gather[r]]; RAGGED_K: reduction row r (the
+    // segment's rows) is A[gather[r]].  A then has gather_rows rows.
+    const int32_t* gather;
+    long gather_rows;
 };
 
 // ------------------------------------------------------------ epilogues
@@ -421,7 +426,11 @@ typedef int i32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ i32x4_t rsrc_words(const bf16_t* base, long nbytes) {
     const uint64_t a = (uint64_t)base;
     const uint32_t n = nbytes <= 0 ? 0u : (uint32_t)nbytes;
-    return i32x4_t{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xFFFFu), (int)n, 0x00020000};
+    // the words are wave-uniform; readfirstlane states it where the
+    // compiler cannot see it (operand fields set on two paths)
+    return i32x4_t{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                   __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu)),
+                   __builtin_amdgcn_readfirstlane((int)n), 0x00020000};
 }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const lds_void_t*)p;
@@ -452,6 +461,7 @@ struct DmaOperand {
     long ld;
     int row_lim;
     long k_lim;
+    long span;               // K-major: bytes from P that hold valid rows
     uint32_t off[NLOAD];
 
     __device__ __forceinline__ void init(const bf16_t* P_, long ld_, int row_lim_,
@@ -460,6 +470,7 @@ struct DmaOperand {
         ld = ld_;
         row_lim = row_lim_;
         k_lim = k_lim_;
+        span = (long)row_lim_ * ld_ * 2;
         const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
         for (int i = 0; i < NLOAD; ++i) {
@@ -479,12 +490,80 @@ struct DmaOperand {
         }
     }
 
+    // K-major operand whose tile row r (< row_lim) is source row map[r] of a
+    // source of src_rows rows at P; the byte range then covers the whole
+    // source (under 2^31 bytes, checked on the host) and rows past row_lim
+    // get an offset past it.
+    __device__ __forceinline__ void init_gather(const bf16_t* P_, long ld_, int row_lim_,
+                                                const int32_t* map, long src_rows) {
+        static_assert(LAY == KMAJ, "row gather of a K-major operand");
+        P = P_;
+        ld = ld_;
+        row_lim = row_lim_;
+        k_lim = 0;
+        span = src_rows * ld_ * 2;
+        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+        constexpr int L = CH == 4 ? 2 : 3;
+#pragma unroll
+        for (int i = 0; i < NLOAD; ++i) {
+            const int row = (w + NW * i) * (64 / CH) + lane / CH;
+            const int c = (lane % CH) ^ ((row ^ (row >> L)) & (CH - 1));
+            off[i] = row < row_lim ? (uint32_t)((long)map[row] * ld * 2 + c * 16) : OOB;
+        }
+    }
+
+    // M/N-major operand whose reduction row k (< k_lim) is a gathered row of
+    // a source with src_rows rows; P points at the tile's first column (of
+    // row_lim valid ones).  off[] holds each load's chunk offset in a row.
+    __device__ __forceinline__ void init_kgather(const bf16_t* P_, long ld_, int row_lim_,
+                                                 long k_lim_, long src_rows, int m0) {
+        static_assert(LAY != KMAJ, "reduction-row gather of an M/N-major operand");
+        P = P_;
+        ld = ld_;
+        row_lim = row_lim_;
+        k_lim = k_lim_;
+        span = src_rows * ld_ * 2 - (long)m0 * 2;
+        constexpr int NC = ROWS / 8;
+        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+        for (int i = 0; i < NLOAD; ++i) {
+            const int k = (w + NW * i) * (1024 / (ROWS * 2)) + lane / NC;
+            const int c = (lane % NC) ^ ((k & 3) << 2);
+            off[i] = c * 8 < row_lim ? (uint32_t)(c * 16) : OOB;
+        }
+    }
+    // Source rows of the loads of the stage of reduction rows k0 .. k0+BK-1:
+    // row k is source row lmap[k - kmap] (lmap in LDS); -1 where the load
+    // is past the segment or the tile's columns.
+    __device__ __forceinline__ void rows_of(long k0, const int32_t* lmap, long kmap,
+                                            int32_t* rows) const {
+        constexpr int NC = ROWS / 8;
+        constexpr int RB = 1024 / (ROWS * 2);
+        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+        for (int i = 0; i < NLOAD; ++i) {
+            const long k = k0 + (w + NW * i) * RB + lane / NC;
+            rows[i] = off[i] != OOB && k < k_lim ? lmap[k - kmap] : -1;
+        }
+    }
+    // Issue that stage, given rows_of's result.
+    __device__ __forceinline__ void dma_rows(uint8_t* stage, const int32_t* rows) const {
+        const int w = threadIdx.x >> 6;
+        const i32x4_t rs = rsrc_words(P, span);
+        const uint32_t lds0 = lds_addr(stage) + (uint32_t)(w * 1024);
+#pragma unroll
+        for (int i = 0; i < NLOAD; ++i) {
+            const uint32_t o = rows[i] >= 0 ? (uint32_t)((long)rows[i] * ld * 2) + off[i] : OOB;
+            lds_dma16(rs, o, lds0 + NW * i * 1024);
+        }
+    }
+
     __device__ __forceinline__ void dma(long k0, uint8_t* stage) const {
         const bf16_t* base;
         long nbytes;
         if (LAY == KMAJ) {
             base = P + k0;
-            nbytes = (long)row_lim * ld * 2 - k0 * 2;
+            nbytes = span - k0 * 2;
         } else {
             base = P + k0 * ld;
             nbytes = min((long)BK, k_lim - k0) * ld * 2;
@@ -533,8 +612,11 @@ __device__ __forceinline__ void stage_barrier_ahead(int ahead) {
     }
 }
 
+// Rows of the reduction-row gather map held in LDS at a time (RAGGED_K).
+constexpr int KG_CHUNK = 4096;
+
 template <int BM, int BN, int WM, int WN, int NSTG, int BK, int MODE, int ALAY, int BLAY,
-          bool DUAL, bool KSPLIT, class Epi>
+          bool DUAL, bool KSPLIT, bool GATHER, class Epi>
 __global__ __launch_bounds__(64 * WM * WN, 2) void ggemm_bf16_dma_kernel(GemmArgs<bf16_t> p,
                                                                          Epi epi) {
     constexpr int NT = 64 * WM * WN;
@@ -543,8 +625,14 @@ __global__ __launch_bounds__(64 * WM * WN, 2) void ggemm_bf16_dma_kernel(GemmArg
     constexpr int NBT = DUAL ? 2 : 1;
     constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
     constexpr int STAGE = A_BYTES + NBT * B_BYTES;
-    static_assert(NSTG >= 3 && STAGE % 1024 == 0 && NSTG * STAGE <= 160 * 1024, "ring size");
+    constexpr bool KGATHER = GATHER && MODE == RAGGED_K;
+    static_assert(!GATHER || (ALAY == KMAJ) == (MODE == RAGGED_M), "gather form");
+    static_assert(KG_CHUNK % BK == 0, "map chunks hold whole stages");
+    constexpr int KGM = KGATHER ? KG_CHUNK : 1;
+    static_assert(NSTG >= 3 && STAGE % 1024 == 0 && NSTG * STAGE + KGM * 4 <= 160 * 1024,
+                  "ring size");
     __shared__ __attribute__((aligned(1024))) uint8_t ringbuf[NSTG * STAGE];
+    __shared__ int32_t kmap[KGM];        // source rows of reduction rows kmap0 ..
 
     const TileInfo ti = decode_tile<MODE, BM, BN>(p);
     if (!ti.live) return;
@@ -556,17 +644,34 @@ __global__ __launch_bounds__(64 * WM * WN, 2) void ggemm_bf16_dma_kernel(GemmArg
     DmaOperand<BN, BLAY, NT, BK> opB;
     DmaOperand<BN, BLAY, NT, BK> opB2;
     const bf16_t* bsplit[2];
-    if (MODE == RAGGED_M) {
-        opA.init(p.A + ti.r0 * p.lda, p.lda, ti.rows, p.K);
+    if constexpr (MODE == RAGGED_M) {
+        if constexpr (GATHER)
+            opA.init_gather(p.A, p.lda, ti.rows, p.gather + ti.r0, p.gather_rows);
+        else
+            opA.init(p.A + ti.r0 * p.lda, p.lda, ti.rows, p.K);
         const long eoff = (long)ti.e * p.bstride;
         const long nofs = BLAY == KMAJ ? (long)ti.n0 * p.ldb : (long)ti.n0;
         opB.init(p.B + eoff + nofs, p.ldb, p.N - ti.n0, p.K);
         if (DUAL) opB2.init(p.B2 + eoff + nofs, p.ldb, p.N - ti.n0, p.K);
         if (KSPLIT) bsplit[0] = opB.P, bsplit[1] = p.B2 + eoff + nofs;
     } else {
-        opA.init(p.A + ti.kbeg * p.lda + ti.m0, p.lda, p.M - ti.m0, ti.klen);
+        if constexpr (KGATHER)
+            opA.init_kgather(p.A + ti.m0, p.lda, p.M - ti.m0, ti.klen, p.gather_rows, ti.m0);
+        else
+            opA.init(p.A + ti.kbeg * p.lda + ti.m0, p.lda, p.M - ti.m0, ti.klen);
         opB.init(p.B + ti.kbeg * p.ldb + ti.n0, p.ldb, p.N - ti.n0, ti.klen);
     }
+    // KGATHER: the source rows of reduction rows kmap0 .. kmap0+KG_CHUNK-1
+    // of the segment, reloaded between stages when the issue crosses a
+    // chunk (the barriers make every wave finish with the old chunk first)
+    auto load_kmap = [&](long kmap0) {
+        if constexpr (KGATHER) {
+            __syncthreads();
+            for (int q = threadIdx.x; q < KG_CHUNK; q += NT)
+                kmap[q] = kmap0 + q < ti.klen ? p.gather[ti.kbeg + kmap0 + q] : 0;
+            __syncthreads();
+        }
+    };
     constexpr int NL = DmaOperand<BM, ALAY, NT, BK>::NLOAD + NBT * DmaOperand<BN, BLAY, NT, BK>::NLOAD;
     static_assert(NL * (NSTG - 2) <= 63, "vmcnt counts at most 63 loads");
 
@@ -587,9 +692,22 @@ __global__ __launch_bounds__(64 * WM * WN, 2) void ggemm_bf16_dma_kernel(GemmArg
                 for (int v = 0; v < 16; ++v) acc2[i][j][v] = 0.0f;
     }
 
+    // KGATHER: source rows of the next stage to issue, read from the map one
+    // stage ahead so that the issue does not wait on LDS
+    int32_t krow[KGATHER ? DmaOperand<BM, ALAY, NT, BK>::NLOAD : 1];
     auto issue = [&](uint8_t* stg, int j) {
         const long k0 = (long)j * BK;
-        opA.dma(k0, stg);
+        if constexpr (KGATHER) {
+            const long c0 = k0 / KG_CHUNK * KG_CHUNK;
+            if (k0 == c0 && k0 > 0) {            // next map chunk
+                load_kmap(c0);
+                opA.rows_of(k0, kmap, c0, krow);
+            }
+            opA.dma_rows(stg, krow);
+            if ((k0 + BK) % KG_CHUNK != 0) opA.rows_of(k0 + BK, kmap, c0, krow);
+        } else {
+            opA.dma(k0, stg);
+        }
         if constexpr (KSPLIT) {
             const bool hi = k0 >= p.Ksplit;
             opB.P = bsplit[hi];
@@ -643,6 +761,8 @@ __global__ __launch_bounds__(64 * WM * WN, 2) void ggemm_bf16_dma_kernel(GemmArg
     // away from the barrier and behind the MFMAs still in the pipe: while
     // stage j is multiplied, j+1 .. j+NSTG-1 are landing.
     const int nj = (ti.klen + BK - 1) / BK;
+    load_kmap(0);
+    if constexpr (KGATHER) opA.rows_of(0, kmap, 0, krow);
 #pragma unroll
     for (int q = 0; q < NSTG - 1; ++q)
         if (q < nj) issue(ring(q), q);
@@ -781,10 +901,15 @@ __global__ __launch_bounds__(256) void ggemm_f32_kernel(GemmArgs<float> p, Epi e
             if (ALAY == KMAJ) { m = q / FK; kk = q % FK; } else { m = q % FB; kk = q / FB; }
             const long k = k0 + kk;
             if (MODE == RAGGED_M) {
-                if (m < ti.rows) v = p.A[(ti.r0 + m) * p.lda + k];
+                if (m < ti.rows) {
+                    const long r = ti.r0 + m;
+                    v = p.A[(p.gather ? (long)p.gather[r] : r) * p.lda + k];
+                }
             } else {
-                if (k < ti.klen && ti.m0 + m < p.M)
-                    v = p.A[(ti.kbeg + k) * p.lda + ti.m0 + m];
+                if (k < ti.klen && ti.m0 + m < p.M) {
+                    const long r = ti.kbeg + k;
+                    v = p.A[(p.gather ? (long)p.gather[r] : r) * p.lda + ti.m0 + m];
+                }
             }
             sA[kk][m] = v;
         }
@@ -914,8 +1039,9 @@ FfnWs ffn_layout(int R, int E, int f, moe_act act, moe_dtype dt, int backward) {
     return w;
 }
 
+// G: the product may gather its A rows (p.gather != NULL selects that kernel)
 template <int BM, int BN, int WM, int WN, int NSTG, int BK, int MODE, int ALAY, int BLAY,
-          bool DUAL, bool KSPLIT, class Epi>
+          bool DUAL, bool KSPLIT, bool G, class Epi>
 void launch_bf16(GemmArgs<bf16_t> p, Epi epi, int R, hipStream_t s, const char* name) {
     p.nN = (p.N + BN - 1) / BN;
     int blocks;
@@ -933,9 +1059,18 @@ void launch_bf16(GemmArgs<bf16_t> p, Epi epi, int R, hipStream_t s, const char* 
     if (p.xcd_run <= 0) p.xcd_run = MODE == RAGGED_M ? 32 : 8;
     const int pad = NXCD * p.xcd_run;                      // whole XCD runs
     blocks = (blocks + pad - 1) / pad * pad;
+    if constexpr (G) {
+        if (p.gather) {
+            MOE_LAUNCH(name, s,
+                       ggemm_bf16_dma_kernel<BM, BN, WM, WN, NSTG, BK, MODE, ALAY, BLAY, DUAL,
+                                             KSPLIT, true, Epi>
+                       <<<blocks, 64 * WM * WN, 0, s>>>(p, epi));
+            return;
+        }
+    }
     MOE_LAUNCH(name, s,
                ggemm_bf16_dma_kernel<BM, BN, WM, WN, NSTG, BK, MODE, ALAY, BLAY, DUAL, KSPLIT,
-                                     Epi>
+                                     false, Epi>
                <<<blocks, 64 * WM * WN, 0, s>>>(p, epi));
 }
 
@@ -970,6 +1105,8 @@ GemmArgs<T> base_args(const int32_t* offsets, const Plan& pl, int E) {
     p.part_mode = 0;
     p.bm_plan = 0;
     p.xcd_run = 0;
+    p.gather = nullptr;
+    p.gather_rows = 0;
     return p;
 }
 
@@ -1039,13 +1176,13 @@ struct Launch<bf16_t, Cfg> {
     }
     // Returns true when the product was split: full row tiles on s, the
     // partial last tiles on ts.  Otherwise everything ran on s.
-    template <int MODE, int ALAY, int BLAY, bool DUAL, bool KSPLIT, class Epi>
+    template <int MODE, int ALAY, int BLAY, bool DUAL, bool KSPLIT, bool G = false, class Epi>
     static bool go(GemmArgs<bf16_t> p, Epi epi, int R, hipStream_t s, const char* name,
                    const char* tail_name = nullptr, hipStream_t ts = nullptr) {
         if (!ts) ts = s;           // stream of the tail launch
         if constexpr (DUAL) {
             launch_bf16<Cfg::BM, Cfg::BND, Cfg::WMD, Cfg::WND, Cfg::RM::NS, Cfg::RM::BK, MODE, ALAY, BLAY, DUAL,
-                        KSPLIT>(p, epi, R, s, name);
+                        KSPLIT, G>(p, epi, R, s, name);
             return false;
         } else {
             if constexpr (MODE == RAGGED_M && Cfg::BMT > 0) {
@@ -1054,24 +1191,24 @@ struct Launch<bf16_t, Cfg> {
                     q.part_mode = 1;
                     q.bm_plan = Cfg::BM;
                     launch_bf16<Cfg::BM, Cfg::BN, Cfg::WM, Cfg::WN, Cfg::RM::NS, Cfg::RM::BK, MODE, ALAY, BLAY,
-                                DUAL, KSPLIT>(q, epi, R, s, name);
+                                DUAL, KSPLIT, G>(q, epi, R, s, name);
                     q.part_mode = 2;
                     // expected live slices: about half of the slots of the partial tiles
                     const long slices = (long)min(p.E, R) * (Cfg::BM / Cfg::BMT) / 2;
                     if (Cfg::BNN > 0 && slices * cdiv(p.N, Cfg::BNT) < device_cus()) {
                         q.xcd_run = xcd_run_for(slices * cdiv(p.N, Cfg::BNN));
                         launch_bf16<Cfg::BMT, Cfg::BNN, Cfg::WMT, Cfg::WNN, Cfg::RN::NS, Cfg::RN::BK, MODE,
-                                    ALAY, BLAY, DUAL, KSPLIT>(q, epi, R, ts, tail_name);
+                                    ALAY, BLAY, DUAL, KSPLIT, G>(q, epi, R, ts, tail_name);
                     } else {
                         q.xcd_run = xcd_run_for(slices * cdiv(p.N, Cfg::BNT));
                         launch_bf16<Cfg::BMT, Cfg::BNT, Cfg::WMT, Cfg::WNT, Cfg::RT::NS, Cfg::RT::BK, MODE,
-                                    ALAY, BLAY, DUAL, KSPLIT>(q, epi, R, ts, tail_name);
+                                    ALAY, BLAY, DUAL, KSPLIT, G>(q, epi, R, ts, tail_name);
                     }
                     return true;
                 }
             }
             launch_bf16<Cfg::BM, Cfg::BN, Cfg::WM, Cfg::WN, Cfg::RM::NS, Cfg::RM::BK, MODE, ALAY, BLAY, DUAL,
-                        KSPLIT>(p, epi, R, s, name);
+                        KSPLIT, G>(p, epi, R, s, name);
             return false;
         }
     }
@@ -1082,7 +1219,7 @@ template <class Cfg>
 struct Launch<float, Cfg> {
     template <int MODE, bool DUAL>
     static bool splits(int, int, int) { return false; }
-    template <int MODE, int ALAY, int BLAY, bool DUAL, bool KSPLIT, class Epi>
+    template <int MODE, int ALAY, int BLAY, bool DUAL, bool KSPLIT, bool G = false, class Epi>
     static bool go(GemmArgs<float> p, Epi epi, int R, hipStream_t s, const char* name,
                    const char* = nullptr, hipStream_t = nullptr) {
         launch_f32<MODE, ALAY, BLAY, DUAL, KSPLIT>(p, epi, R, s, name);
@@ -1095,7 +1232,9 @@ template <typename T, class Cfg = DefaultCfg>
 moe_status ffn_fwd(const void* x_perm, const int32_t* offsets, int R, int E,
                    int d, int f, moe_act act, const void* W1, const void* W3,
                    const void* W2, void* h_save, void* a_save, void* out_perm,
-                   void* ws, hipStream_t s) {
+                   void* ws, hipStream_t s, const int32_t* gather = nullptr, long T_src = 0) {
+    // gather != NULL: x_perm is the token-order input [T_src,d] and permuted row
+    // r is its row gather[r] (the permute's row copy fused into GEMM1)
     const FfnWs L = ffn_layout(R, E, f, act, MOE_F32, 0);
     char* base = static_cast<char*>(ws);
     int32_t* prefix = reinterpret_cast<int32_t*>(base + L.prefix);
@@ -1113,6 +1252,7 @@ moe_status ffn_fwd(const void* x_perm, const int32_t* offsets, int R, int E,
     // GEMM1 (+ activation): [R,d] x W1[e] [d,f]
     GemmArgs<T> p = base_args<T>(offsets, pl, E);
     p.A = xp; p.lda = d;
+    p.gather = gather; p.gather_rows = T_src;
     p.B = static_cast<const T*>(W1); p.ldb = f; p.bstride = (long)d * f;
     p.N = f; p.K = d;
     // GEMM2: A [R,f] x W2[e] [f,d]
@@ -1122,7 +1262,7 @@ moe_status ffn_fwd(const void* x_perm, const int32_t* offsets, int R, int E,
     q.N = d; q.K = f;
     if (act == MOE_ACT_SWIGLU) {       // one launch over all rows, before the fork
         p.B2 = static_cast<const T*>(W3);
-        Launch<T, Cfg>::template go<RAGGED_M, KMAJ, MNMAJ, true, false>(
+        Launch<T, Cfg>::template go<RAGGED_M, KMAJ, MNMAJ, true, false, true>(
             p, EpiSwigluFwd<T>{H, A, f}, R, s, "gemm_up_swiglu");
     }
     // The rows of the experts' full tiles (main launches, caller's stream)
@@ -1133,7 +1273,7 @@ moe_status ffn_fwd(const void* x_perm, const int32_t* offsets, int R, int E,
     hipStream_t ts = side.ok() ? side.get() : s;
     bool up_split = false;
     if (act == MOE_ACT_GELU)
-        up_split = Launch<T, Cfg>::template go<RAGGED_M, KMAJ, MNMAJ, false, false>(
+        up_split = Launch<T, Cfg>::template go<RAGGED_M, KMAJ, MNMAJ, false, false, true>(
             p, EpiGeluFwd<T>{H, A, f}, R, s, "gemm_up_gelu", "gemm_up_gelu_tail", ts);
     const bool down_split = Launch<T, Cfg>::template splits<RAGGED_M, false>(R, E, d);
     if (side.ok() && up_split != down_split) {
@@ -1154,7 +1294,10 @@ moe_status ffn_bwd(const void* d_out, const void* x_perm, const void* h_save,
                    const void* a_save, const int32_t* offsets, int R, int E,
                    int d, int f, moe_act act, const void* W1, const void* W3,
                    const void* W2, void* dx_perm, void* dW1, void* dW3,
-                   void* dW2, void* ws, hipStream_t s) {
+                   void* dW2, void* ws, hipStream_t s, const int32_t* gather = nullptr,
+                   long T_src = 0) {
+    // gather != NULL: x_perm is the token-order input [T_src,d]; dW1/dW3 read
+    // permuted row r as its row gather[r]
     const FfnWs L = ffn_layout(R, E, f, act, MOE_F32, 1);
     char* base = static_cast<char*>(ws);
     int32_t* prefix = reinterpret_cast<int32_t*>(base + L.prefix);
@@ -1233,12 +1376,13 @@ moe_status ffn_bwd(const void* d_out, const void* x_perm, const void* h_save,
     {
         GemmArgs<T> p = base_args<T>(offsets, pl, E);
         p.A = static_cast<const T*>(x_perm); p.lda = d; p.M = d;
+        p.gather = gather; p.gather_rows = T_src;
         p.B = dH; p.ldb = ldh; p.N = f;
-        Launch<T, Cfg>::template go<RAGGED_K, MNMAJ, MNMAJ, false, false>(
+        Launch<T, Cfg>::template go<RAGGED_K, MNMAJ, MNMAJ, false, false, true>(
             p, EpiStore<T>{static_cast<T*>(dW1), f, (long)d * f}, R, s, "gemm_dW1");
         if (sw) {
             p.B = dH + f;
-            Launch<T, Cfg>::template go<RAGGED_K, MNMAJ, MNMAJ, false, false>(
+            Launch<T, Cfg>::template go<RAGGED_K, MNMAJ, MNMAJ, false, false, true>(
                 p, EpiStore<T>{static_cast<T*>(dW3), f, (long)d * f}, R, s, "gemm_dW3");
         }
     }
@@ -1312,6 +1456,63 @@ moe_status moe_expert_ffn_bwd(const void* d_out_perm, const void* x_perm,
                                act, W1, W3, W2, dx_perm, dW1, dW3, dW2, ws, stream);
     return ffn_bwd<float>(d_out_perm, x_perm, h_save, a_save, offsets, R, E, d, f, act,
                           W1, W3, W2, dx_perm, dW1, dW3, dW2, ws, stream);
+}
+
+// The permute's row copy fused into the expert GEMMs: x is read in token
+// order through src.  The 32-bit buffer offsets of the bf16 path bound the
+// source at 2^31 bytes.
+static moe_status gather_check(const void* x, const int32_t* src, int T, int R, int d,
+                               moe_dtype dt) {
+    MOE_CHECK_ARG(T >= 0 && (R == 0 || (T > 0 && x && src && aligned16(x))));
+    if (dt == MOE_BF16 && (long long)T * d * 2 >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+moe_status moe_expert_ffn_fwd_gather(const void* x, const int32_t* src,
+                                     const int32_t* offsets, int T, int R, int E, int d,
+                                     int f, moe_act act, moe_dtype dt, const void* W1,
+                                     const void* W3, const void* W2, void* h_save,
+                                     void* a_save, void* out_perm, void* ws,
+                                     size_t ws_bytes, hipStream_t stream) {
+    moe_status st = ffn_check(R, E, d, f, act, dt);
+    if (st != MOE_OK) return st;
+    if ((st = gather_check(x, src, T, R, d, dt)) != MOE_OK) return st;
+    if (R == 0) return MOE_OK;
+    MOE_CHECK_ARG(offsets && W1 && W2 && h_save && a_save && out_perm);
+    MOE_CHECK_ARG(act != MOE_ACT_SWIGLU || W3);
+    MOE_CHECK_ARG(aligned16(W1) && aligned16(W2) && aligned16(h_save) &&
+                  aligned16(a_save) && aligned16(out_perm) && (W3 == nullptr || aligned16(W3)));
+    if (!ws || ws_bytes < moe_ffn_workspace_bytes(R, E, d, f, act, dt, 0))
+        return MOE_ERR_WORKSPACE;
+    MOE_CHECK_DEVICE();
+    if (dt == MOE_BF16)
+        return ffn_fwd<bf16_t>(x, offsets, R, E, d, f, act, W1, W3, W2, h_save, a_save,
+                               out_perm, ws, stream, src, T);
+    return ffn_fwd<float>(x, offsets, R, E, d, f, act, W1, W3, W2, h_save, a_save, out_perm,
+                          ws, stream, src, T);
+}
+
+moe_status moe_expert_ffn_bwd_gather(const void* d_out_perm, const void* x,
+                                     const int32_t* src, const void* h_save,
+                                     const void* a_save, const int32_t* offsets, int T,
+                                     int R, int E, int d, int f, moe_act act, moe_dtype dt,
+                                     const void* W1, const void* W3, const void* W2,
+                                     void* dx_perm, void* dW1, void* dW3, void* dW2,
+                                     void* ws, size_t ws_bytes, hipStream_t stream) {
+    moe_status st = ffn_check(R, E, d, f, act, dt);
+    if (st != MOE_OK) return st;
+    if ((st = gather_check(x, src, T, R, d, dt)) != MOE_OK) return st;
+    MOE_CHECK_ARG(offsets && W1 && W2 && dW1 && dW2);
+    MOE_CHECK_ARG(act != MOE_ACT_SWIGLU || (W3 && dW3));
+    MOE_CHECK_ARG(R == 0 || (d_out_perm && h_save && a_save && dx_perm));
+    if (!ws || ws_bytes < moe_ffn_workspace_bytes(R, E, d, f, act, dt, 1))
+        return MOE_ERR_WORKSPACE;
+    MOE_CHECK_DEVICE();
+    if (dt == MOE_BF16)
+        return ffn_bwd<bf16_t>(d_out_perm, x, h_save, a_save, offsets, R, E, d, f, act, W1,
+                               W3, W2, dx_perm, dW1, dW3, dW2, ws, stream, src, T);
+    return ffn_bwd<float>(d_out_perm, x, h_save, a_save, offsets, R, E, d, f, act, W1, W3,
+                          W2, dx_perm, dW1, dW3, dW2, ws, stream, src, T);
 }
 
 }  // extern "C"

@@ -229,8 +229,9 @@ moe_status moe_permute(const int32_t* topk_idx, const void* x, int T, int d,
     const int vec = dt == MOE_BF16 ? 8 : 4;
     MOE_CHECK_ARG(d % vec == 0);
     MOE_CHECK_ARG(counts && offsets);
-    MOE_CHECK_ARG(T == 0 || (topk_idx && x && dest && src && x_perm));
-    MOE_CHECK_ARG(T == 0 || (aligned16(x) && aligned16(x_perm)));
+    // x_perm == NULL: routing only (the expert GEMMs gather rows of x by src)
+    MOE_CHECK_ARG(T == 0 || (topk_idx && dest && src && (!x_perm || x)));
+    MOE_CHECK_ARG(T == 0 || !x_perm || (aligned16(x) && aligned16(x_perm)));
     if (ws_bytes < moe_permute_workspace_bytes(T, E, k) || (!ws && T > 0))
         return MOE_ERR_WORKSPACE;
     MOE_CHECK_DEVICE();
@@ -261,6 +262,7 @@ moe_status moe_permute(const int32_t* topk_idx, const void* x, int T, int d,
     MOE_LAUNCH("perm_scatter", stream,
         perm_scatter_kernel<<<nblk, 256, sizeof(int) * (5 * (size_t)E + 1), stream>>>(
             topk_idx, counts, bbase, T, E, k, tpb, nblk, nbits, offsets, dest, src));
+    if (!x_perm) return launch_status();
     if (dt == MOE_BF16)
         MOE_LAUNCH("perm_copy", stream,
             perm_copy_kernel<bf16_t><<<cdiv(T, 4), 256, 0, stream>>>(

@@ -13,8 +13,11 @@ from .ops import _stream
 
 class MoELayer:
     def __init__(self, T, d, f, E, k, act="gelu", dtype=torch.bfloat16,
-                 renorm=1, device="cuda"):
+                 renorm=1, device="cuda", fuse_gather=False):
+        """fuse_gather: no x_perm buffer; the permute only routes and the FFN
+        calls read rows of x through src (moe_expert_ffn_*_gather)."""
         self.T, self.d, self.f, self.E, self.k = T, d, f, E, k
+        self.fuse_gather = bool(fuse_gather)
         self.act = MOE_ACT_SWIGLU if act == "swiglu" else MOE_ACT_GELU
         self.dtype = dtype
         self.dt = MOE_BF16 if dtype == torch.bfloat16 else MOE_F32
@@ -34,7 +37,7 @@ class MoELayer:
         self.offsets = e(E + 1, dt=i32)
         self.dest = e(T, k, dt=i32)
         self.src = e(R, dt=i32)
-        self.x_perm = e(R, d)
+        self.x_perm = None if self.fuse_gather else e(R, d)
         self.h_save = e(R, hw)
         self.a_save = e(R, f)
         self.out_perm = e(R, d)
@@ -71,6 +74,11 @@ class MoELayer:
             ("moe_permute", (p(self.topk_idx), p(x), T, d, E, k, dt, p(self.counts),
                              p(self.offsets), p(self.dest), p(self.src),
                              p(self.x_perm), p(self.ws_perm), self.ws_perm.numel())),
+            ("moe_expert_ffn_fwd_gather", (p(x), p(self.src), p(self.offsets), T, R, E, d,
+                                           f, a, dt, p(W1), p(W3), p(W2), p(self.h_save),
+                                           p(self.a_save), p(self.out_perm),
+                                           p(self.ws_ffn_f), self.ws_ffn_f.numel()))
+            if self.fuse_gather else
             ("moe_expert_ffn_fwd", (p(self.x_perm), p(self.offsets), R, E, d, f, a, dt,
                                     p(W1), p(W3), p(W2), p(self.h_save),
                                     p(self.a_save), p(self.out_perm),
@@ -81,6 +89,13 @@ class MoELayer:
         self._bwd = [
             ("moe_combine_bwd", (p(dy), p(self.out_perm), p(self.dest), p(self.topk_w),
                                  T, k, d, dt, p(self.d_out_perm), p(self.d_topk_w))),
+            ("moe_expert_ffn_bwd_gather", (p(self.d_out_perm), p(x), p(self.src),
+                                           p(self.h_save), p(self.a_save), p(self.offsets),
+                                           T, R, E, d, f, a, dt, p(W1), p(W3), p(W2),
+                                           p(self.dx_perm), p(self.dW1), p(self.dW3),
+                                           p(self.dW2), p(self.ws_ffn_b),
+                                           self.ws_ffn_b.numel()))
+            if self.fuse_gather else
             ("moe_expert_ffn_bwd", (p(self.d_out_perm), p(self.x_perm), p(self.h_save),
                                     p(self.a_save), p(self.offsets), R, E, d, f, a, dt,
                                     p(W1), p(W3), p(W2), p(self.dx_perm),

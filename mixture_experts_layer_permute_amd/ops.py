@@ -75,8 +75,9 @@ def moe_gate_topk(x, Wg, k, logit_bias=None, renorm=1, logits=None,
     return logits, topk_idx, topk_w
 
 
-def moe_permute(topk_idx, x, E, out=None, ws=None):
-    """-> (counts [E], offsets [E+1], dest [T,k], src [T*k], x_perm [T*k,d])."""
+def moe_permute(topk_idx, x, E, out=None, ws=None, copy=True):
+    """-> (counts [E], offsets [E+1], dest [T,k], src [T*k], x_perm [T*k,d]);
+    copy=False: routing only, x_perm is None (for the *_gather FFN calls)."""
     _need_gpu(topk_idx, x)
     T, k = topk_idx.shape
     d = x.shape[1]
@@ -87,7 +88,7 @@ def moe_permute(topk_idx, x, E, out=None, ws=None):
                torch.empty(E + 1, dtype=torch.int32, device=dev),
                torch.empty(T, k, dtype=torch.int32, device=dev),
                torch.empty(T * k, dtype=torch.int32, device=dev),
-               torch.empty(T * k, d, dtype=x.dtype, device=dev))
+               torch.empty(T * k, d, dtype=x.dtype, device=dev) if copy else None)
     counts, offsets, dest, src, x_perm = out
     nb = L.moe_permute_workspace_bytes(T, E, k)
     if ws is None:
@@ -145,6 +146,59 @@ def moe_expert_ffn_bwd(d_out_perm, x_perm, h_save, a_save, offsets, W1, W2,
                                _dt(x_perm), _p(W1), _p(W3), _p(W2), _p(dx_perm),
                                _p(dW1), _p(dW3), _p(dW2), _p(ws), ws.numel(),
                                _stream(dev)), "moe_expert_ffn_bwd")
+    return dx_perm, dW1, dW3, dW2
+
+
+def moe_expert_ffn_fwd_gather(x, src, offsets, W1, W2, W3=None, act="gelu",
+                              out=None, ws=None):
+    """moe_expert_ffn_fwd reading permuted row r as x[src[r]] (no x_perm).
+    -> (h_save, a_save [R,f], out_perm [R,d]), R = src.numel()."""
+    _need_gpu(x, src, offsets, W1, W2, W3)
+    a = _act(act)
+    T, d = x.shape
+    R = src.numel()
+    E, _, f = W1.shape
+    dev = x.device
+    L = load()
+    if out is None:
+        hw = 2 * f if a == MOE_ACT_SWIGLU else f
+        out = (torch.empty(R, hw, dtype=x.dtype, device=dev),
+               torch.empty(R, f, dtype=x.dtype, device=dev),
+               torch.empty(R, d, dtype=x.dtype, device=dev))
+    h_save, a_save, out_perm = out
+    if ws is None:
+        ws = _ws(L.moe_ffn_workspace_bytes(R, E, d, f, a, _dt(x), 0), dev)
+    check(L.moe_expert_ffn_fwd_gather(_p(x), _p(src), _p(offsets), T, R, E, d, f, a,
+                                      _dt(x), _p(W1), _p(W3), _p(W2), _p(h_save),
+                                      _p(a_save), _p(out_perm), _p(ws), ws.numel(),
+                                      _stream(dev)), "moe_expert_ffn_fwd_gather")
+    return h_save, a_save, out_perm
+
+
+def moe_expert_ffn_bwd_gather(d_out_perm, x, src, h_save, a_save, offsets, W1, W2,
+                              W3=None, act="gelu", out=None, ws=None):
+    """moe_expert_ffn_bwd reading permuted row r as x[src[r]] (no x_perm).
+    -> (dx_perm [R,d], dW1 [E,d,f], dW3 or None, dW2 [E,f,d])."""
+    _need_gpu(d_out_perm, x, src, h_save, a_save, offsets, W1, W2, W3)
+    a = _act(act)
+    T, d = x.shape
+    R = src.numel()
+    E, _, f = W1.shape
+    dev = x.device
+    L = load()
+    if out is None:
+        out = (torch.empty(R, d, dtype=x.dtype, device=dev),
+               torch.empty_like(W1),
+               torch.empty_like(W3) if a == MOE_ACT_SWIGLU else None,
+               torch.empty_like(W2))
+    dx_perm, dW1, dW3, dW2 = out
+    if ws is None:
+        ws = _ws(L.moe_ffn_workspace_bytes(R, E, d, f, a, _dt(x), 1), dev)
+    check(L.moe_expert_ffn_bwd_gather(_p(d_out_perm), _p(x), _p(src), _p(h_save),
+                                      _p(a_save), _p(offsets), T, R, E, d, f, a, _dt(x),
+                                      _p(W1), _p(W3), _p(W2), _p(dx_perm), _p(dW1),
+                                      _p(dW3), _p(dW2), _p(ws), ws.numel(),
+                                      _stream(dev)), "moe_expert_ffn_bwd_gather")
     return dx_perm, dW1, dW3, dW2
 
 

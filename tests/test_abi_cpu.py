@@ -44,12 +44,13 @@ def test_every_declared_symbol_is_exported(lib):
 def test_binding_names_match_c_names():
     for n in ("moe_gate_topk", "moe_permute", "moe_expert_ffn_fwd",
               "moe_expert_ffn_bwd", "moe_combine", "moe_unpermute_grad",
-              "moe_combine_bwd", "moe_gate_topk_bwd", "moe_init"):
+              "moe_combine_bwd", "moe_gate_topk_bwd", "moe_init",
+              "moe_expert_ffn_fwd_gather", "moe_expert_ffn_bwd_gather"):
         assert callable(getattr(M, n))
 
 
 def test_status_strings_and_version(lib):
-    assert lib.moe_abi_version() == 2
+    assert lib.moe_abi_version() == 3
     for s in (0, -1, -2, -3, -4):
         assert lib.moe_status_string(s)
 
@@ -90,6 +91,29 @@ def test_invalid_arguments_rejected_before_launch(lib):
     p = ctypes.addressof(buf)
     assert lib.moe_permute(p, p, 100, 64, 4, 2, 0, p, p, p, p, p, p, 0, N) == \
         _lib.MOE_ERR_WORKSPACE
+
+
+def test_gather_entry_points_validate_on_host(lib):
+    N = None
+    buf = ctypes.create_string_buffer(4096)
+    p = ctypes.addressof(buf) + (-ctypes.addressof(buf)) % 16
+    # the bf16 source must stay under 2^31 bytes (32-bit buffer offsets)
+    assert lib.moe_expert_ffn_fwd_gather(p, p, p, 1 << 20, 16, 2, 1024, 64, 0, 1, p, N, p,
+                                         p, p, p, p, 1 << 20, N) == _lib.MOE_ERR_UNSUPPORTED
+    assert lib.moe_expert_ffn_bwd_gather(p, p, p, p, p, p, 1 << 20, 16, 2, 1024, 64, 0, 1,
+                                         p, N, p, p, p, N, p, p, 1 << 20, N) == \
+        _lib.MOE_ERR_UNSUPPORTED
+    # rows to gather but no source or no map
+    assert lib.moe_expert_ffn_fwd_gather(N, p, p, 100, 16, 2, 64, 64, 0, 1, p, N, p, p, p,
+                                         p, p, 1 << 20, N) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_ffn_fwd_gather(p, N, p, 100, 16, 2, 64, 64, 0, 1, p, N, p, p, p,
+                                         p, p, 1 << 20, N) == _lib.MOE_ERR_INVALID_ARG
+    # rows but an empty source
+    assert lib.moe_expert_ffn_fwd_gather(p, p, p, 0, 16, 2, 64, 64, 0, 1, p, N, p, p, p,
+                                         p, p, 1 << 20, N) == _lib.MOE_ERR_INVALID_ARG
+    # routing-only permute still needs dest and src
+    assert lib.moe_permute(p, N, 10, 64, 4, 2, 1, p, p, N, p, N, p, 1 << 20, N) == \
+        _lib.MOE_ERR_INVALID_ARG
 
 
 def test_no_gpu_means_error_not_fallback(lib):
