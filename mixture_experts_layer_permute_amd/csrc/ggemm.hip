@@ -23,12 +23,15 @@
 //
 // bf16 path: block tile 256x256, 8 waves of 64 (4x2, 64x128 each), gfx950
 // MFMA v_mfma_f32_32x32x16_bf16 with fp32 accumulators.  Operands go from
-// HBM straight into a 4-stage LDS ring; K-contiguous operands are read as
+// HBM straight into an LDS ring (two 64-deep stages for RAGGED_M, four
+// 32-deep ones for RAGGED_K); K-contiguous operands are read as
 // 16-byte fragments, M/N-contiguous ones with the transposing LDS read.
 // Products that are a few rounds of workgroups run as a full-tile launch
 // and a partial-tile launch; independent launches may run on a side stream.
 // fp32 path (tiny fp32 workload): a plain LDS-tiled FMA kernel with the same
 // tile scheduler and epilogues.
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
@@ -629,7 +632,7 @@ __global__ __launch_bounds__(64 * WM * WN, 2) void ggemm_bf16_dma_kernel(GemmArg
     static_assert(!GATHER || (ALAY == KMAJ) == (MODE == RAGGED_M), "gather form");
     static_assert(KG_CHUNK % BK == 0, "map chunks hold whole stages");
     constexpr int KGM = KGATHER ? KG_CHUNK : 1;
-    static_assert(NSTG >= 3 && STAGE % 1024 == 0 && NSTG * STAGE + KGM * 4 <= 160 * 1024,
+    static_assert(NSTG >= 2 && STAGE % 1024 == 0 && NSTG * STAGE + KGM * 4 <= 160 * 1024,
                   "ring size");
     __shared__ __attribute__((aligned(1024))) uint8_t ringbuf[NSTG * STAGE];
     __shared__ int32_t kmap[KGM];        // source rows of reduction rows kmap0 ..
@@ -1119,10 +1122,12 @@ template <int NS_, int BK_>
 struct Ring {
     static constexpr int NS = NS_, BK = BK_;
 };
-// RM, RT, RN are the rings of the main, wide-tail and narrow-tail kernels.
+// RM, RT, RN are the rings of the main, wide-tail and narrow-tail kernels
+// of RAGGED_M products, RK the ring of RAGGED_K (dW) products.
 template <int BM_, int BN_, int WM_, int WN_, int BND_, int WMD_, int WND_, int BMT_ = 0,
           int BNT_ = 0, int WMT_ = 0, int WNT_ = 0, int BNN_ = 0, int WNN_ = 0,
-          class RM_ = Ring<4, 32>, class RT_ = Ring<4, 32>, class RN_ = Ring<4, 32>>
+          class RM_ = Ring<4, 32>, class RT_ = Ring<4, 32>, class RN_ = Ring<4, 32>,
+          class RK_ = RM_>
 struct TileCfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
     static constexpr int BND = BND_, WMD = WMD_, WND = WND_;
@@ -1131,11 +1136,15 @@ struct TileCfg {
     typedef RM_ RM;
     typedef RT_ RT;
     typedef RN_ RN;
+    typedef RK_ RK;
 };
-// The narrow tail (64x128 slices, few MFMAs per stage) takes 64-deep stages
-// in a 5-stage ring: half the barriers of 32-deep ones, and 3 stages in flight.
-using DefaultCfg = TileCfg<256, 256, 4, 2, 128, 4, 2, 64, 256, 1, 4, 128, 4, Ring<4, 32>,
-                           Ring<4, 32>, Ring<5, 64>>;
+// RAGGED_M main tiles: two 64-deep stages (half the barriers of 32-deep
+// ones; the next stage is issued at the top of the current one).  dW
+// products, whose reduction is a segment that may be short, keep four
+// 32-deep stages.  The narrow tail (64x128 slices, few MFMAs per stage)
+// takes 64-deep stages in a 5-stage ring, three in flight.
+using DefaultCfg = TileCfg<256, 256, 4, 2, 128, 4, 2, 64, 256, 1, 4, 128, 4, Ring<2, 64>,
+                           Ring<4, 32>, Ring<5, 64>, Ring<4, 32>>;
 
 // Wave quantisation.  A RAGGED_M product has between ceil(R/BM) and
 // ceil(R/BM) + E - 1 row tiles, since each expert's last tile is usually
@@ -1179,9 +1188,10 @@ struct Launch<bf16_t, Cfg> {
     template <int MODE, int ALAY, int BLAY, bool DUAL, bool KSPLIT, bool G = false, class Epi>
     static bool go(GemmArgs<bf16_t> p, Epi epi, int R, hipStream_t s, const char* name,
                    const char* tail_name = nullptr, hipStream_t ts = nullptr) {
+        using RR = std::conditional_t<MODE == RAGGED_K, typename Cfg::RK, typename Cfg::RM>;
         if (!ts) ts = s;           // stream of the tail launch
         if constexpr (DUAL) {
-            launch_bf16<Cfg::BM, Cfg::BND, Cfg::WMD, Cfg::WND, Cfg::RM::NS, Cfg::RM::BK, MODE, ALAY, BLAY, DUAL,
+            launch_bf16<Cfg::BM, Cfg::BND, Cfg::WMD, Cfg::WND, RR::NS, RR::BK, MODE, ALAY, BLAY, DUAL,
                         KSPLIT, G>(p, epi, R, s, name);
             return false;
         } else {
@@ -1190,7 +1200,7 @@ struct Launch<bf16_t, Cfg> {
                     GemmArgs<bf16_t> q = p;
                     q.part_mode = 1;
                     q.bm_plan = Cfg::BM;
-                    launch_bf16<Cfg::BM, Cfg::BN, Cfg::WM, Cfg::WN, Cfg::RM::NS, Cfg::RM::BK, MODE, ALAY, BLAY,
+                    launch_bf16<Cfg::BM, Cfg::BN, Cfg::WM, Cfg::WN, RR::NS, RR::BK, MODE, ALAY, BLAY,
                                 DUAL, KSPLIT, G>(q, epi, R, s, name);
                     q.part_mode = 2;
                     // expected live slices: about half of the slots of the partial tiles
@@ -1207,7 +1217,7 @@ struct Launch<bf16_t, Cfg> {
                     return true;
                 }
             }
-            launch_bf16<Cfg::BM, Cfg::BN, Cfg::WM, Cfg::WN, Cfg::RM::NS, Cfg::RM::BK, MODE, ALAY, BLAY, DUAL,
+            launch_bf16<Cfg::BM, Cfg::BN, Cfg::WM, Cfg::WN, RR::NS, RR::BK, MODE, ALAY, BLAY, DUAL,
                         KSPLIT, G>(p, epi, R, s, name);
             return false;
         }
