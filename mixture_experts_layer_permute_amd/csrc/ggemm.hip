@@ -597,6 +597,15 @@ __device__ __forceinline__ bf16x8 dma_frag(const uint8_t* lds, int row0, int ks,
     }
 }
 
+// Order a wave's LDS writes before its later LDS reads (and reads before
+// later writes) of data other lanes of the same wave touch: one wave's LDS
+// instructions execute in order, so only the compiler must not move them.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+}
+
 // Wait until at most N direct-to-LDS loads of this wave are in flight and
 // its LDS reads have returned, then meet the other waves of the block.
 template <int N>
@@ -802,7 +811,9 @@ __global__ __launch_bounds__(64 * WM * WN, 2) void ggemm_bf16_dma_kernel(GemmArg
     }
     __syncthreads();
 
-    // ---- epilogue through LDS (same scheme as the register kernel)
+    // ---- epilogue through LDS.  Each wave stages its own 16-row slabs, so
+    // after the barrier above (every wave is done with the ring) the waves
+    // only order their own LDS writes and reads: no block barriers.
     constexpr int LDW = WTN + 4;
     constexpr int SLAB = 16 * LDW;                   // floats per wave half-slab
     constexpr int WPS = STAGE / (SLAB * NBT * 4);    // wave slabs per stage array
@@ -825,7 +836,7 @@ __global__ __launch_bounds__(64 * WM * WN, 2) void ggemm_bf16_dma_kernel(GemmArg
                     if constexpr (DUAL)
                         slab[SLAB + r * LDW + j * 32 + (lane & 31)] = acc2[i][j][v];
                 }
-            __syncthreads();
+            wave_lds_sync();
             constexpr int NPS = 16 / RPP;                 // sub-passes of this slab
             auto row_of = [&](int ps) { return wm * WTM + i * 32 + h * 16 + ps * RPP + lane / LPR; };
             const int c0 = (lane % LPR) * 8;
@@ -872,7 +883,7 @@ __global__ __launch_bounds__(64 * WM * WN, 2) void ggemm_bf16_dma_kernel(GemmArg
                     }
                 }
             }
-            __syncthreads();
+            wave_lds_sync();
         }
     }
 }
@@ -1138,13 +1149,13 @@ struct TileCfg {
     typedef RN_ RN;
     typedef RK_ RK;
 };
-// RAGGED_M main tiles: two 64-deep stages (half the barriers of 32-deep
-// ones; the next stage is issued at the top of the current one).  dW
+// RAGGED_M main and wide-tail tiles: two 64-deep stages (half the barriers
+// of 32-deep ones; the next stage is issued at the top of the current one).  dW
 // products, whose reduction is a segment that may be short, keep four
 // 32-deep stages.  The narrow tail (64x128 slices, few MFMAs per stage)
 // takes 64-deep stages in a 5-stage ring, three in flight.
 using DefaultCfg = TileCfg<256, 256, 4, 2, 128, 4, 2, 64, 256, 1, 4, 128, 4, Ring<2, 64>,
-                           Ring<4, 32>, Ring<5, 64>, Ring<4, 32>>;
+                           Ring<2, 64>, Ring<5, 64>, Ring<4, 32>>;
 
 // Wave quantisation.  A RAGGED_M product has between ceil(R/BM) and
 // ceil(R/BM) + E - 1 row tiles, since each expert's last tile is usually
