@@ -685,7 +685,7 @@ __global__ __launch_bounds__(64 * WM * WN, 2) void ggemm_bf16_dma_kernel(GemmArg
         }
     };
     constexpr int NL = DmaOperand<BM, ALAY, NT, BK>::NLOAD + NBT * DmaOperand<BN, BLAY, NT, BK>::NLOAD;
-    static_assert(NL * (NSTG - 2) <= 63, "vmcnt counts at most 63 loads");
+    static_assert(NL * (NSTG - 1) <= 63, "vmcnt counts at most 63 loads");
 
     f32x16 acc[FM][FN];
     f32x16 acc2[DUAL ? FM : 1][DUAL ? FN : 1];
@@ -775,10 +775,15 @@ __global__ __launch_bounds__(64 * WM * WN, 2) void ggemm_bf16_dma_kernel(GemmArg
     const int nj = (ti.klen + BK - 1) / BK;
     load_kmap(0);
     if constexpr (KGATHER) opA.rows_of(0, kmap, 0, krow);
+    // Prologue: the first NP stages.  With both operands K-contiguous the
+    // slot of stage NSTG-1 is filled here too (one stage more in flight
+    // from the start: dA, dX 2-3% faster); with a transposed operand the
+    // extra loads compete with the transposing LDS reads and cost as much.
+    constexpr int NP = ALAY == KMAJ && BLAY == KMAJ ? NSTG : NSTG - 1;
 #pragma unroll
-    for (int q = 0; q < NSTG - 1; ++q)
+    for (int q = 0; q < NP; ++q)
         if (q < nj) issue(ring(q), q);
-    stage_barrier_ahead<NL, NSTG - 2>(min(nj - 1, NSTG - 2));   // stage 0 landed
+    stage_barrier_ahead<NL, NP - 1>(min(nj - 1, NP - 1));   // stage 0 landed
     if (nj > 0) read_frags(ring(0), 0, 0);
     // all stages but the last; the last one is peeled off so that the loop
     // body has one path and the compiler's LDS waits before its final MFMAs
@@ -789,7 +794,7 @@ __global__ __launch_bounds__(64 * WM * WN, 2) void ggemm_bf16_dma_kernel(GemmArg
         const uint8_t* cur = ring(qc);
         const int qn = qc + 1 == NSTG ? 0 : qc + 1;    // slot of stage j+1
         const int qf = qc == 0 ? NSTG - 1 : qc - 1;    // slot of stage j-1 = j+NSTG-1
-        if (j + NSTG - 1 < nj) issue(ring(qf), j + NSTG - 1);
+        if ((NP < NSTG || j > 0) && j + NSTG - 1 < nj) issue(ring(qf), j + NSTG - 1);
 #pragma unroll
         for (int ks = 0; ks + 1 < KS; ++ks) {
             read_frags(cur, ks + 1, (ks + 1) & 1);
