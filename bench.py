@@ -95,6 +95,9 @@ def parse():
                     help="headline layer reads x through src inside the expert "
                          "GEMMs (no x_perm, no row-copy kernel); by default that "
                          "variant is timed after the headline as fused_gather")
+    ap.add_argument("--chunk-tokens", type=int, default=0,
+                    help="run the step over chunks of this many tokens with one "
+                         "chunk's activation buffers (ChunkedMoELayer)")
     ap.add_argument("--no-fused-pass", action="store_true",
                     help="skip the fused_gather timing (profiler runs: one kernel "
                          "variant per name)")
@@ -186,6 +189,8 @@ def cpu_baseline(cfg, budget_s):
 
 def load_stats(counts, cfg):
     """Per-expert row counts of the routing the step ran on."""
+    if counts.dim() == 2:             # per chunk
+        counts = counts.sum(0)
     c = sorted(int(v) for v in counts.cpu().tolist())
     return {"max_over_mean": round(c[-1] * cfg.E / cfg.R, 3),
             "empty_experts": sum(1 for v in c if v == 0),
@@ -210,8 +215,16 @@ def main():
     M.moe_init(0)
     M.moe_set_overlap(not args.serial)
     t = device.gen_all(cfg)
-    layer = M.MoELayer(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.act,
-                       device.torch_dtype(cfg), cfg.renorm, fuse_gather=args.fuse_gather)
+    inputs_bytes = sum(v.numel() * v.element_size() for v in t.values() if v is not None)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    if args.chunk_tokens:
+        layer = M.ChunkedMoELayer(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.act,
+                                  device.torch_dtype(cfg), cfg.renorm,
+                                  chunk_tokens=args.chunk_tokens)
+    else:
+        layer = M.MoELayer(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.act,
+                           device.torch_dtype(cfg), cfg.renorm, fuse_gather=args.fuse_gather)
     layer.bind(t["x"], t["Wg"], t["W1"], t["W2"], t["W3"], t["bias"], t["dy"])
     stream = torch.cuda.current_stream()
     s = stream.cuda_stream
@@ -242,6 +255,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms = ev0.elapsed_time(ev1) / args.steps
+    hbm_peak = torch.cuda.max_memory_allocated()
 
     # ---- step-time distribution: an event pair around every step
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -270,7 +284,7 @@ def main():
 
     # ---- optional pass with the MALL flushed before every entry point
     flushed = {}
-    if args.flush_mall:
+    if args.flush_mall and hasattr(layer, "stage_calls"):
         # reading 512 MiB evicts the 256 MB MALL with clean lines (a write
         # would leave dirty lines to be written back during the next kernel)
         junk = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
@@ -307,6 +321,10 @@ def main():
         if base not in work:
             continue
         calls = kernels[base]["launches_per_step"] if base in kernels else 1.0
+        if args.chunk_tokens:
+            # one launch per chunk (plus GEMM1's recomputation): rates are the
+            # step's algorithmic work over the stage's time per step
+            calls = 1.0
         per_call = sum(kernels[n]["ms_per_step"] for n in names) / calls
         stage_ms[base] = per_call
         amt, unit = work[base]
@@ -364,7 +382,10 @@ def main():
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "f": cfg.f,
                    "E": cfg.E, "k": cfg.k, "act": cfg.act, "renorm": cfg.renorm,
                    "routing_skew_zipf_s": cfg.zipf_s, "stream_overlap": not args.serial,
-                   "fused_gather": args.fuse_gather},
+                   "fused_gather": args.fuse_gather,
+                   "chunk_tokens": args.chunk_tokens or None},
+        "hbm_peak_bytes": hbm_peak,
+        "hbm_inputs_bytes": inputs_bytes,
         "gemm_tflops_layer": round(gemm_flops / (ms * 1e-3) / 1e12, 2),
         "gemm_tflops_kernels": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 2)
         if gemm_ms else None,
@@ -383,7 +404,7 @@ def main():
         base, fw, gr = cpu_baseline(cfg, args.cpu_seconds)
         base["parity"] = parity(cfg, layer, fw, gr)
         out["cpu_baseline"] = base
-    if not args.fuse_gather and not args.no_fused_pass:
+    if not args.fuse_gather and not args.no_fused_pass and not args.chunk_tokens:
         # the same step with the row copy fused into the expert GEMMs (its
         # results are bit-identical: tests/test_gpu_gather.py); timed after
         # the headline layer is freed, so that both never share HBM

@@ -151,6 +151,8 @@ moe_status moe_permute(const int32_t *topk_idx, const void *x, int T, int d,
  *     fp32 accumulator: GeLU: [R,f] = GeLU'(H); SwiGLU: [R,2f], row r =
  *     H3*SiLU'(H1) then SiLU(H1).  Only moe_expert_ffn_bwd reads it.
  *   a_save [R,f] (A), out_perm [R,d] dt.  Accumulation is fp32.
+ *   out_perm == NULL: GEMM1 only (h_save and a_save; W2 may be NULL) -- the
+ *   recomputation of the saved state for a chunk's backward.
  *   ws: at least moe_ffn_workspace_bytes(R,E,d,f,act,dt,0).
  */
 size_t moe_ffn_workspace_bytes(int R, int E, int d, int f, moe_act act,
@@ -181,6 +183,30 @@ moe_status moe_expert_ffn_bwd(const void *d_out_perm, const void *x_perm,
                               const void *W3, const void *W2, void *dx_perm,
                               void *dW1, void *dW3, void *dW2, void *ws,
                               size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_expert_ffn_bwd_accumulate -- moe_expert_ffn_bwd with the weight
+ * gradients added to what dW1, dW2 (dW3) hold: dW += X_e^T dH_e etc., the
+ * old value and the new product summed in fp32 and rounded once.  For a
+ * batch processed in chunks of tokens: the first chunk calls
+ * moe_expert_ffn_bwd, the later ones this entry point.  In exact arithmetic
+ * the chunked sum equals the whole one; in bf16 storage each chunk adds one
+ * rounding of the running sum.  Sources: MPipeMoE (icslab.whu.edu.cn),
+ * 研究方法 (buffers reused across micro-batches, recomputation); "Flattening
+ * Every Memory Peak in Long-Context MoE Training", English abstract (a cap on
+ * the tokens of each dispatch chunk; only order and granularity change).
+ *   Arguments as moe_expert_ffn_bwd; R == 0 leaves dW unchanged.
+ */
+moe_status moe_expert_ffn_bwd_accumulate(const void *d_out_perm,
+                                         const void *x_perm, const void *h_save,
+                                         const void *a_save,
+                                         const int32_t *offsets, int R, int E,
+                                         int d, int f, moe_act act, moe_dtype dt,
+                                         const void *W1, const void *W3,
+                                         const void *W2, void *dx_perm,
+                                         void *dW1, void *dW3, void *dW2,
+                                         void *ws, size_t ws_bytes,
+                                         hipStream_t stream);
 
 /*
  * moe_expert_ffn_fwd_gather / moe_expert_ffn_bwd_gather -- the products of

@@ -30,6 +30,8 @@ SIGNATURES = {
                                 _P, _P, _Z, _P]),
     "moe_expert_ffn_bwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P,
                                 _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "moe_expert_ffn_bwd_accumulate": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
+                                           _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "moe_expert_ffn_fwd_gather": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P,
                                        _P, _P, _P, _P, _P, _Z, _P]),
     "moe_expert_ffn_bwd_gather": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,

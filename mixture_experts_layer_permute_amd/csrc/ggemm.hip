@@ -228,6 +228,40 @@ __device__ __forceinline__ void unpack_bf16x8(const uint4& r, float* o) {
 }
 
 template <typename T>
+struct EpiAcc {              // C[e*cstride + row*ldc + col] += v: one fp32 sum, one rounding
+    static constexpr bool kPre = sizeof(T) == 2;
+    struct Pre {
+        uint4 c;                    // 8 bf16 of C, raw (bf16 kernels only)
+    };
+    __device__ __forceinline__ Pre pre8(int e, long row, int col) const {
+        static_assert(sizeof(T) == 2, "prefetching epilogue is for bf16 tensors");
+        return {*reinterpret_cast<const uint4*>(C + e * cstride + row * ldc + col)};
+    }
+    T* C;
+    long ldc, cstride;
+    __device__ __forceinline__ void operator()(int e, long row, int col, float v) const {
+        T* q = C + e * cstride + row * ldc + col;
+        Elem<T>::st(q, Elem<T>::ld(q) + v);
+    }
+    __device__ __forceinline__ void vec8(int e, long row, int col, const float* v) const {
+        float c[8];
+        T* q = C + e * cstride + row * ldc + col;
+        Vec16<T>::ld(q, c);
+#pragma unroll
+        for (int i = 0; i < Vec16<T>::N; ++i) c[i] += v[i];
+        Vec16<T>::st(q, c);
+    }
+    __device__ __forceinline__ void vec8p(int e, long row, int col, const float* v,
+                                          const Pre& pr) const {
+        float c[8];
+        unpack_bf16x8(pr.c, c);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c[i] += v[i];
+        Vec16<T>::st(C + e * cstride + row * ldc + col, c);
+    }
+};
+
+template <typename T>
 struct EpiGeluBwd {          // dH = dA * S, S = GeLU'(H) saved by the forward
     static constexpr bool kPre = true;
     struct Pre {
@@ -849,12 +883,15 @@ __global__ __launch_bounds__(64 * WM * WN, 2) void ggemm_bf16_dma_kernel(GemmArg
             auto ok_of = [&](int rl) {
                 return col < p.N && (MODE == RAGGED_M ? rl < ti.rows : ti.m0 + rl < p.M);
             };
-            if constexpr (Epi::kPre && !DUAL && MODE == RAGGED_M) {
+            if constexpr (Epi::kPre && !DUAL) {
                 // every read of this slab in flight before the first is used
+                auto grow = [&](int rl) {
+                    return MODE == RAGGED_M ? ti.r0 + rl : (long)ti.m0 + rl;
+                };
                 typename Epi::Pre pre[NPS];
 #pragma unroll
                 for (int ps = 0; ps < NPS; ++ps)
-                    if (ok_of(row_of(ps))) pre[ps] = epi.pre8(ti.e, ti.r0 + row_of(ps), col);
+                    if (ok_of(row_of(ps))) pre[ps] = epi.pre8(ti.e, grow(row_of(ps)), col);
 #pragma unroll
                 for (int ps = 0; ps < NPS; ++ps) {
                     const int rl = row_of(ps);
@@ -862,7 +899,7 @@ __global__ __launch_bounds__(64 * WM * WN, 2) void ggemm_bf16_dma_kernel(GemmArg
                     float v[8];
                     *reinterpret_cast<float4*>(v) = *reinterpret_cast<const float4*>(src);
                     *reinterpret_cast<float4*>(v + 4) = *reinterpret_cast<const float4*>(src + 4);
-                    if (ok_of(rl)) epi.vec8p(ti.e, ti.r0 + rl, col, v, pre[ps]);
+                    if (ok_of(rl)) epi.vec8p(ti.e, grow(rl), col, v, pre[ps]);
                 }
             } else {
 #pragma unroll 1
@@ -1301,6 +1338,10 @@ moe_status ffn_fwd(const void* x_perm, const int32_t* offsets, int R, int E,
     if (act == MOE_ACT_GELU)
         up_split = Launch<T, Cfg>::template go<RAGGED_M, KMAJ, MNMAJ, false, false, true>(
             p, EpiGeluFwd<T>{H, A, f}, R, s, "gemm_up_gelu", "gemm_up_gelu_tail", ts);
+    if (!out_perm) {                   // GEMM1 only (recomputation of the saved state)
+        if (side.ok() && !side.join()) return MOE_ERR_HIP;
+        return launch_status();
+    }
     const bool down_split = Launch<T, Cfg>::template splits<RAGGED_M, false>(R, E, d);
     if (side.ok() && up_split != down_split) {
         // up split, down whole: down (caller's stream) needs up's partial rows;
@@ -1321,7 +1362,8 @@ moe_status ffn_bwd(const void* d_out, const void* x_perm, const void* h_save,
                    int d, int f, moe_act act, const void* W1, const void* W3,
                    const void* W2, void* dx_perm, void* dW1, void* dW3,
                    void* dW2, void* ws, hipStream_t s, const int32_t* gather = nullptr,
-                   long T_src = 0) {
+                   long T_src = 0, bool accumulate = false) {
+    // accumulate: dW1/dW2/dW3 += the products (fp32 sum, one rounding)
     // gather != NULL: x_perm is the token-order input [T_src,d]; dW1/dW3 read
     // permuted row r as its row gather[r]
     const FfnWs L = ffn_layout(R, E, f, act, MOE_F32, 1);
@@ -1368,8 +1410,12 @@ moe_status ffn_bwd(const void* d_out, const void* x_perm, const void* h_save,
         GemmArgs<T> p = base_args<T>(offsets, pl, E);
         p.A = static_cast<const T*>(a_save); p.lda = f; p.M = f;
         p.B = dO; p.ldb = d; p.N = d;
-        Launch<T, Cfg>::template go<RAGGED_K, MNMAJ, MNMAJ, false, false>(
-            p, EpiStore<T>{static_cast<T*>(dW2), d, (long)f * d}, R, ts, "gemm_dW2");
+        if (accumulate)
+            Launch<T, Cfg>::template go<RAGGED_K, MNMAJ, MNMAJ, false, false>(
+                p, EpiAcc<T>{static_cast<T*>(dW2), d, (long)f * d}, R, ts, "gemm_dW2");
+        else
+            Launch<T, Cfg>::template go<RAGGED_K, MNMAJ, MNMAJ, false, false>(
+                p, EpiStore<T>{static_cast<T*>(dW2), d, (long)f * d}, R, ts, "gemm_dW2");
     }
     // dX = dH1 W1[e]^T (+ dH3 W3[e]^T)   [R, d]
     const bool dX_split = Launch<T, Cfg>::template splits<RAGGED_M, false>(R, E, d);
@@ -1404,12 +1450,18 @@ moe_status ffn_bwd(const void* d_out, const void* x_perm, const void* h_save,
         p.A = static_cast<const T*>(x_perm); p.lda = d; p.M = d;
         p.gather = gather; p.gather_rows = T_src;
         p.B = dH; p.ldb = ldh; p.N = f;
-        Launch<T, Cfg>::template go<RAGGED_K, MNMAJ, MNMAJ, false, false, true>(
-            p, EpiStore<T>{static_cast<T*>(dW1), f, (long)d * f}, R, s, "gemm_dW1");
+        auto dw = [&](void* C, const char* name) {
+            if (accumulate)
+                Launch<T, Cfg>::template go<RAGGED_K, MNMAJ, MNMAJ, false, false, true>(
+                    p, EpiAcc<T>{static_cast<T*>(C), f, (long)d * f}, R, s, name);
+            else
+                Launch<T, Cfg>::template go<RAGGED_K, MNMAJ, MNMAJ, false, false, true>(
+                    p, EpiStore<T>{static_cast<T*>(C), f, (long)d * f}, R, s, name);
+        };
+        dw(dW1, "gemm_dW1");
         if (sw) {
             p.B = dH + f;
-            Launch<T, Cfg>::template go<RAGGED_K, MNMAJ, MNMAJ, false, false, true>(
-                p, EpiStore<T>{static_cast<T*>(dW3), f, (long)d * f}, R, s, "gemm_dW3");
+            dw(dW3, "gemm_dW3");
         }
     }
     if (side.ok() && !side.join()) return MOE_ERR_HIP;
@@ -1446,10 +1498,11 @@ moe_status moe_expert_ffn_fwd(const void* x_perm, const int32_t* offsets,
     moe_status st = ffn_check(R, E, d, f, act, dt);
     if (st != MOE_OK) return st;
     if (R == 0) return MOE_OK;
-    MOE_CHECK_ARG(x_perm && offsets && W1 && W2 && h_save && a_save && out_perm);
+    // out_perm == NULL: GEMM1 only (h_save and a_save), W2 unused
+    MOE_CHECK_ARG(x_perm && offsets && W1 && h_save && a_save && (W2 || !out_perm));
     MOE_CHECK_ARG(act != MOE_ACT_SWIGLU || W3);
-    MOE_CHECK_ARG(aligned16(x_perm) && aligned16(W1) && aligned16(W2) &&
-                  aligned16(h_save) && aligned16(a_save) && aligned16(out_perm) &&
+    MOE_CHECK_ARG(aligned16(x_perm) && aligned16(W1) && (!W2 || aligned16(W2)) &&
+                  aligned16(h_save) && aligned16(a_save) && (!out_perm || aligned16(out_perm)) &&
                   (W3 == nullptr || aligned16(W3)));
     if (!ws || ws_bytes < moe_ffn_workspace_bytes(R, E, d, f, act, dt, 0))
         return MOE_ERR_WORKSPACE;
@@ -1484,6 +1537,32 @@ moe_status moe_expert_ffn_bwd(const void* d_out_perm, const void* x_perm,
                           W1, W3, W2, dx_perm, dW1, dW3, dW2, ws, stream);
 }
 
+// moe_expert_ffn_bwd with dW1/dW2/dW3 += instead of =: the gradient of one
+// chunk of tokens added to the chunks before it.
+moe_status moe_expert_ffn_bwd_accumulate(const void* d_out_perm, const void* x_perm,
+                                         const void* h_save, const void* a_save,
+                                         const int32_t* offsets, int R, int E, int d, int f,
+                                         moe_act act, moe_dtype dt, const void* W1,
+                                         const void* W3, const void* W2, void* dx_perm,
+                                         void* dW1, void* dW3, void* dW2, void* ws,
+                                         size_t ws_bytes, hipStream_t stream) {
+    moe_status st = ffn_check(R, E, d, f, act, dt);
+    if (st != MOE_OK) return st;
+    MOE_CHECK_ARG(offsets && W1 && W2 && dW1 && dW2);
+    MOE_CHECK_ARG(act != MOE_ACT_SWIGLU || (W3 && dW3));
+    MOE_CHECK_ARG(R == 0 || (d_out_perm && x_perm && h_save && a_save && dx_perm));
+    if (!ws || ws_bytes < moe_ffn_workspace_bytes(R, E, d, f, act, dt, 1))
+        return MOE_ERR_WORKSPACE;
+    MOE_CHECK_DEVICE();
+    if (R == 0) return MOE_OK;         // nothing to add
+    if (dt == MOE_BF16)
+        return ffn_bwd<bf16_t>(d_out_perm, x_perm, h_save, a_save, offsets, R, E, d, f, act,
+                               W1, W3, W2, dx_perm, dW1, dW3, dW2, ws, stream, nullptr, 0,
+                               true);
+    return ffn_bwd<float>(d_out_perm, x_perm, h_save, a_save, offsets, R, E, d, f, act, W1,
+                          W3, W2, dx_perm, dW1, dW3, dW2, ws, stream, nullptr, 0, true);
+}
+
 // The permute's row copy fused into the expert GEMMs: x is read in token
 // order through src.  The 32-bit buffer offsets of the bf16 path bound the
 // source at 2^31 bytes.
@@ -1504,10 +1583,11 @@ moe_status moe_expert_ffn_fwd_gather(const void* x, const int32_t* src,
     if (st != MOE_OK) return st;
     if ((st = gather_check(x, src, T, R, d, dt)) != MOE_OK) return st;
     if (R == 0) return MOE_OK;
-    MOE_CHECK_ARG(offsets && W1 && W2 && h_save && a_save && out_perm);
+    MOE_CHECK_ARG(offsets && W1 && h_save && a_save && (W2 || !out_perm));
     MOE_CHECK_ARG(act != MOE_ACT_SWIGLU || W3);
-    MOE_CHECK_ARG(aligned16(W1) && aligned16(W2) && aligned16(h_save) &&
-                  aligned16(a_save) && aligned16(out_perm) && (W3 == nullptr || aligned16(W3)));
+    MOE_CHECK_ARG(aligned16(W1) && (!W2 || aligned16(W2)) && aligned16(h_save) &&
+                  aligned16(a_save) && (!out_perm || aligned16(out_perm)) &&
+                  (W3 == nullptr || aligned16(W3)));
     if (!ws || ws_bytes < moe_ffn_workspace_bytes(R, E, d, f, act, dt, 0))
         return MOE_ERR_WORKSPACE;
     MOE_CHECK_DEVICE();

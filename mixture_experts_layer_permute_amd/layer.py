@@ -136,3 +136,150 @@ class MoELayer:
         return [(n, (lambda n=n, a=a, s=None: check(
             getattr(L, n)(*a, _stream(self.device) if s is None else s), n)))
             for n, a in self._fwd + self._bwd]
+
+
+class ChunkedMoELayer:
+    """The same layer step over the tokens in chunks of at most chunk_tokens,
+    with the dispatch and activation buffers sized for one chunk and reused
+    (MPipeMoE, 研究方法: buffers shared across micro-batches, recomputation;
+    "Flattening Every Memory Peak in Long-Context MoE Training", English
+    abstract: a token cap per dispatch chunk bounds the dispatch peak).
+
+    forward:  moe_gate_topk over all tokens; per chunk moe_permute ->
+              moe_expert_ffn_fwd -> moe_combine (out_perm is kept whole: the
+              gate's backward needs it).
+    backward: chunks in reverse order, the last chunk's saved state still in
+              the buffers; every other chunk re-permutes and recomputes GEMM1
+              (moe_expert_ffn_fwd with out_perm = NULL); moe_combine_bwd ->
+              moe_expert_ffn_bwd (first) / _accumulate (rest) ->
+              moe_unpermute_grad; then moe_gate_topk_bwd over all tokens.
+
+    y, dx, dWg and every routing output are bit-identical to MoELayer's; dW1,
+    dW2, dW3 are the same sums taken chunk by chunk (one rounding per chunk
+    in bf16).
+    """
+
+    def __init__(self, T, d, f, E, k, act="gelu", dtype=torch.bfloat16,
+                 renorm=1, device="cuda", chunk_tokens=4096):
+        self.T, self.d, self.f, self.E, self.k = T, d, f, E, k
+        self.act = MOE_ACT_SWIGLU if act == "swiglu" else MOE_ACT_GELU
+        self.dtype = dtype
+        self.dt = MOE_BF16 if dtype == torch.bfloat16 else MOE_F32
+        self.renorm = renorm
+        self.device = torch.device(device)
+        C = self.C = max(1, min(int(chunk_tokens), T)) if T > 0 else 1
+        self.nch = (T + C - 1) // C
+        L = self.lib = load()
+        R = self.R = T * k
+        Rc = self.Rc = C * k
+        dev = self.device
+        e = lambda *s, dt=dtype: torch.empty(*s, dtype=dt, device=dev)
+        i32, f32 = torch.int32, torch.float32
+        hw = 2 * f if self.act == MOE_ACT_SWIGLU else f
+        # whole-batch tensors
+        self.logits = e(T, E, dt=f32)
+        self.topk_idx = e(T, k, dt=i32)
+        self.topk_w = e(T, k, dt=f32)
+        self.dest = e(T, k, dt=i32)            # rows within the token's chunk
+        self.src = e(R, dt=i32)                # chunk-major; tokens within the chunk
+        self.counts = e(self.nch, E, dt=i32)
+        self.offsets = e(self.nch, E + 1, dt=i32)
+        self.out_perm = e(R, d)                # chunk-major
+        self.y = e(T, d)
+        self.d_topk_w = e(T, k, dt=f32)
+        self.dx = e(T, d)
+        self.dW1 = e(E, d, f)
+        self.dW3 = e(E, d, f) if self.act == MOE_ACT_SWIGLU else None
+        self.dW2 = e(E, f, d)
+        self.dWg = e(d, E)
+        # one chunk's buffers, reused
+        self.x_perm = e(Rc, d)
+        self.h_save = e(Rc, hw)
+        self.a_save = e(Rc, f)
+        self.d_out_perm = e(Rc, d)
+        self.dx_perm = e(Rc, d)
+        ws = lambda n: torch.empty(max(int(n), 1), dtype=torch.uint8, device=dev)
+        self.ws_perm = ws(L.moe_permute_workspace_bytes(C, E, k))
+        self.ws_ffn_f = ws(L.moe_ffn_workspace_bytes(Rc, E, d, f, self.act, self.dt, 0))
+        self.ws_ffn_b = ws(L.moe_ffn_workspace_bytes(Rc, E, d, f, self.act, self.dt, 1))
+        self.ws_gate = ws(L.moe_gate_bwd_workspace_bytes(T, d, E))
+        self._resident = -1                    # chunk whose state the buffers hold
+
+    def bind(self, x, Wg, W1, W2, W3=None, logit_bias=None, dy=None):
+        for t in (x, Wg, W1, W2, W3, dy):
+            if t is not None:
+                assert t.is_cuda and t.is_contiguous() and t.dtype == self.dtype
+        self.x, self.Wg, self.W1, self.W2, self.W3 = x, Wg, W1, W2, W3
+        self.bias, self.dy = logit_bias, dy
+        self._resident = -1
+        return self
+
+    def _chunks(self):
+        for c in range(self.nch):
+            t0 = c * self.C
+            tc = min(self.C, self.T - t0)
+            yield c, t0, tc, c * self.Rc, tc * self.k
+
+    def _permute(self, c, t0, tc, r0, s):
+        p = lambda t: t.data_ptr()
+        L = self.lib
+        check(L.moe_permute(p(self.topk_idx[t0:]), p(self.x[t0:]), tc, self.d, self.E,
+                            self.k, self.dt, p(self.counts[c]), p(self.offsets[c]),
+                            p(self.dest[t0:]), p(self.src[r0:]), p(self.x_perm),
+                            p(self.ws_perm), self.ws_perm.numel(), s), "moe_permute")
+
+    def _ffn_fwd(self, c, rc, out, s):
+        p = lambda t: None if t is None else t.data_ptr()
+        check(self.lib.moe_expert_ffn_fwd(
+            p(self.x_perm), p(self.offsets[c]), rc, self.E, self.d, self.f, self.act, self.dt,
+            p(self.W1), p(self.W3), p(self.W2), p(self.h_save), p(self.a_save), p(out),
+            p(self.ws_ffn_f), self.ws_ffn_f.numel(), s), "moe_expert_ffn_fwd")
+
+    def forward(self, stream=None):
+        s = _stream(self.device) if stream is None else stream
+        p = lambda t: None if t is None else t.data_ptr()
+        L, T, d, E, k = self.lib, self.T, self.d, self.E, self.k
+        check(L.moe_gate_topk(p(self.x), p(self.Wg), p(self.bias), T, d, E, k, self.renorm,
+                              self.dt, p(self.logits), p(self.topk_idx), p(self.topk_w), s),
+              "moe_gate_topk")
+        for c, t0, tc, r0, rc in self._chunks():
+            self._permute(c, t0, tc, r0, s)
+            self._ffn_fwd(c, rc, self.out_perm[r0:], s)
+            self._resident = c
+            check(L.moe_combine(p(self.out_perm[r0:]), p(self.dest[t0:]), p(self.topk_w[t0:]),
+                                tc, k, d, self.dt, p(self.y[t0:]), s), "moe_combine")
+        return self.y
+
+    def backward(self, stream=None):
+        assert self.dy is not None, "bind(dy=...) first"
+        s = _stream(self.device) if stream is None else stream
+        p = lambda t: None if t is None else t.data_ptr()
+        L, T, d, f, E, k = self.lib, self.T, self.d, self.f, self.E, self.k
+        first = True
+        for c, t0, tc, r0, rc in reversed(list(self._chunks())):
+            if c != self._resident:        # the forward's last chunk is still in place
+                self._permute(c, t0, tc, r0, s)
+                self._ffn_fwd(c, rc, None, s)
+                self._resident = c
+            check(L.moe_combine_bwd(p(self.dy[t0:]), p(self.out_perm[r0:]), p(self.dest[t0:]),
+                                    p(self.topk_w[t0:]), tc, k, d, self.dt,
+                                    p(self.d_out_perm), p(self.d_topk_w[t0:]), s),
+                  "moe_combine_bwd")
+            fn = L.moe_expert_ffn_bwd if first else L.moe_expert_ffn_bwd_accumulate
+            check(fn(p(self.d_out_perm), p(self.x_perm), p(self.h_save), p(self.a_save),
+                     p(self.offsets[c]), rc, E, d, f, self.act, self.dt, p(self.W1),
+                     p(self.W3), p(self.W2), p(self.dx_perm), p(self.dW1), p(self.dW3),
+                     p(self.dW2), p(self.ws_ffn_b), self.ws_ffn_b.numel(), s),
+                  "moe_expert_ffn_bwd")
+            first = False
+            check(L.moe_unpermute_grad(p(self.dx_perm), p(self.dest[t0:]), tc, k, d, self.dt,
+                                       p(self.dx[t0:]), 0, s), "moe_unpermute_grad")
+        check(L.moe_gate_topk_bwd(p(self.x), p(self.Wg), p(self.logits), p(self.topk_idx),
+                                  p(self.topk_w), p(self.d_topk_w), T, d, E, k, self.renorm,
+                                  self.dt, p(self.dx), p(self.dWg), p(self.ws_gate),
+                                  self.ws_gate.numel(), s), "moe_gate_topk_bwd")
+        return self.dx
+
+    def step(self, stream=None):
+        self.forward(stream)
+        self.backward(stream)

@@ -1,0 +1,97 @@
+"""ChunkedMoELayer: the layer step over chunks of tokens with one chunk's
+dispatch and activation buffers.  Routing, y, dx and dWg must be bit-identical
+to MoELayer's (the same per-row arithmetic and the same gate backward); dW1,
+dW2, dW3 are the same sums taken chunk by chunk, so they are compared within
+the dtype's tolerance, with MoELayer and with the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_permute_amd as M
+import oracle
+from moe_inputs import device, rng, small_variant
+
+from _gpu import assert_close, banner, host, needs_gpu
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+CASES = [  # workload, overrides, chunk_tokens
+    ("moe_s_like", dict(T=1000, d=256, f=512, E=8, k=2), 256),      # ragged last chunk
+    ("moe_s_like", dict(T=1000, d=256, f=512, E=8, k=2), 1000),     # one chunk
+    ("long_ctx_swiglu", dict(T=777, d=128, f=256, E=16, k=4), 300),
+    ("many_expert_zipf1.0", dict(T=1200, d=128, f=256, E=32, k=2), 400),
+    ("tiny_fp32", {}, 64),
+    ("tiny_fp32", dict(T=100), 1),                                   # one token per chunk
+]
+
+SAME = ["logits", "topk_idx", "topk_w", "y", "d_topk_w", "dx", "dWg"]
+
+
+def run(layer, t):
+    layer.bind(t["x"], t["Wg"], t["W1"], t["W2"], t["W3"], t["bias"], t["dy"])
+    layer.step()
+    torch.cuda.synchronize()
+    return layer
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_chunked_matches_whole_layer(case):
+    name, kw, C = case
+    cfg = small_variant(name, **kw)
+    banner("chunked", cfg.short(), C)
+    t = device.gen_all(cfg)
+    args = (cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.act, device.torch_dtype(cfg), cfg.renorm)
+    whole = run(M.MoELayer(*args), t)
+    ch = run(M.ChunkedMoELayer(*args, chunk_tokens=C), t)
+    for n in SAME:
+        assert torch.equal(getattr(whole, n), getattr(ch, n)), n
+    dt = cfg.dtype
+    wnames = ["dW1", "dW2"] + (["dW3"] if cfg.swiglu else [])
+    for n in wnames:
+        assert_close(getattr(ch, n), host(getattr(whole, n)), dt, n + " vs whole layer")
+    # and against the oracle on the host copy of the inputs
+    x, Wg, dy = (rng.gen(cfg, n) for n in ("x", "Wg", "dy"))
+    W1, W2 = rng.gen_experts(cfg, "W1"), rng.gen_experts(cfg, "W2")
+    W3 = rng.gen_experts(cfg, "W3") if cfg.swiglu else None
+    fw = oracle.layer_forward(x, Wg, W1, W2, W3, k=cfg.k, act=cfg.act,
+                              bias=rng.logit_bias(cfg), renorm=cfg.renorm)
+    gr = oracle.layer_backward(fw, dy, x, Wg, W1, W2, W3, act=cfg.act, renorm=cfg.renorm)
+    for n in wnames:
+        assert_close(getattr(ch, n), gr[n], dt, n + " vs oracle")
+    # a zero-load expert keeps an exact zero gradient through the accumulation
+    counts = host(whole.counts)
+    for e in np.nonzero(counts == 0)[0]:
+        assert float(ch.dW1[e].abs().max()) == 0.0 and float(ch.dW2[e].abs().max()) == 0.0
+
+
+def test_backward_twice_recomputes_every_chunk():
+    cfg = small_variant("moe_s_like", T=900, d=128, f=256, E=8, k=2)
+    banner("chunked backward twice", cfg.short())
+    t = device.gen_all(cfg)
+    ch = M.ChunkedMoELayer(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.act,
+                           device.torch_dtype(cfg), cfg.renorm, chunk_tokens=256)
+    run(ch, t)
+    first = {n: getattr(ch, n).clone() for n in ("dx", "dW1", "dW2", "dWg")}
+    ch.backward()                      # the buffers now hold chunk 0, not the last one
+    torch.cuda.synchronize()
+    for n, v in first.items():
+        assert torch.equal(v, getattr(ch, n)), n
+
+
+def test_chunking_bounds_the_activation_memory():
+    cfg = small_variant("moe_s_like", T=8192, d=1024, f=4096, E=8, k=2)
+    banner("chunked memory", cfg.short())
+    t = device.gen_all(cfg)
+    args = (cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.act, device.torch_dtype(cfg), cfg.renorm)
+    peaks = []
+    for make in (lambda: M.MoELayer(*args), lambda: M.ChunkedMoELayer(*args, chunk_tokens=1024)):
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        layer = run(make(), t)
+        peaks.append(torch.cuda.max_memory_allocated() - base)
+        del layer
+    # per-row activations: x_perm, h_save, a_save, d_out_perm, dx_perm and dH
+    # for T*k rows against one 1024-token chunk (out_perm stays whole)
+    assert peaks[1] < 0.5 * peaks[0], peaks
