@@ -98,6 +98,8 @@ def parse():
     ap.add_argument("--chunk-tokens", type=int, default=0,
                     help="run the step over chunks of this many tokens with one "
                          "chunk's activation buffers (ChunkedMoELayer)")
+    ap.add_argument("--no-graph-pass", action="store_true",
+                    help="skip the timing of the step replayed from a HIP graph")
     ap.add_argument("--no-fused-pass", action="store_true",
                     help="skip the fused_gather timing (profiler runs: one kernel "
                          "variant per name)")
@@ -270,6 +272,34 @@ def main():
     def pct(q):
         return step_ms[min(len(step_ms) - 1, int(q * (len(step_ms) - 1) + 0.5))]
 
+    # ---- the same step captured once in a HIP graph (side-stream fork and
+    # join inside it) and replayed K times; bit-identity: tests/test_gpu_graph.py
+    graph = None
+    if not args.chunk_tokens and not args.no_graph_pass:
+        y0 = layer.y.clone()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            layer.step()
+        stream.wait_stream(cap)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            layer.step()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            for _ in range(args.warmup):
+                g.replay()
+            ev0.record(stream)
+            for _ in range(args.steps):
+                g.replay()
+            ev1.record(stream)
+        torch.cuda.synchronize()
+        gms = ev0.elapsed_time(ev1) / args.steps
+        graph = {"ms_per_step": round(gms, 5), "value": round(cfg.T / (gms * 1e-3), 1),
+                 "y_bit_identical": bool(torch.equal(y0, layer.y))}
+        del g
+
     # ---- per-kernel pass: HIP events around every launch, same K steps
     L = _lib.load()
     _lib.check(L.moe_profile_enable(args.steps * 40), "moe_profile_enable")
@@ -397,6 +427,7 @@ def main():
         "value_at_median_step": round(cfg.T / (pct(0.5) * 1e-3), 1),
         "stream_copy_gbs": round(copy_gbs, 1),
         "roofline": roof,
+        "graph_replay": graph,
         "kernels": kernels,
         "load": load_stats(layer.counts, cfg),
     }
