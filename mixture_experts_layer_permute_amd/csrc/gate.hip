@@ -27,16 +27,16 @@ namespace {
 // to LDS as raw 16-byte vectors (padded rows), the gate columns as fp32
 // transposed to [expert][feature] so that one 16-byte read yields four
 // consecutive features of one expert; the next chunk is fetched into
-// registers while the current one is consumed.
-constexpr int GKC = 64;
-constexpr int GWP = GKC + 4;                   // padded LDS row of a gate column
-
-template <typename T, int TE, int EPT, int MT>
+// registers while the current one is consumed.  With few experts a thread
+// has a single chain, so the chunk is long (256 features): enough
+// dependent multiply-adds to cover the next chunk's fetch.
+template <typename T, int TE, int EPT, int MT, int GKC>
 __global__ __launch_bounds__(256) void gate_logits_kernel(
     const T* __restrict__ x, const T* __restrict__ Wg,
     const float* __restrict__ bias, int Tn, int d, int E,
     float* __restrict__ logits) {
 #pragma clang fp contract(off)
+    constexpr int GWP = GKC + 4;               // padded LDS row of a gate column
     constexpr int TX = TE / EPT;               // threads across experts
     constexpr int TY = 256 / TX;               // threads across tokens
     constexpr int TT = MT * TY;                // tokens per block
@@ -464,19 +464,19 @@ moe_status launch_logits(const void* x, const void* Wg, const float* bias,
     if (E <= 8) {
         dim3 g(cdiv(Tn, 32), cdiv(E, 8));
         MOE_LAUNCH("gate_logits", s,
-            gate_logits_kernel<T, 8, 1, 1><<<g, 256, 0, s>>>(xp, wp, bias, Tn, d, E, logits));
+            gate_logits_kernel<T, 8, 1, 1, 256><<<g, 256, 0, s>>>(xp, wp, bias, Tn, d, E, logits));
     } else if (E <= 16) {
         dim3 g(cdiv(Tn, 16), cdiv(E, 16));
         MOE_LAUNCH("gate_logits", s,
-            gate_logits_kernel<T, 16, 1, 1><<<g, 256, 0, s>>>(xp, wp, bias, Tn, d, E, logits));
+            gate_logits_kernel<T, 16, 1, 1, 256><<<g, 256, 0, s>>>(xp, wp, bias, Tn, d, E, logits));
     } else if (E <= 32) {
         dim3 g(cdiv(Tn, 16), cdiv(E, 32));
         MOE_LAUNCH("gate_logits", s,
-            gate_logits_kernel<T, 32, 2, 1><<<g, 256, 0, s>>>(xp, wp, bias, Tn, d, E, logits));
+            gate_logits_kernel<T, 32, 2, 1, 128><<<g, 256, 0, s>>>(xp, wp, bias, Tn, d, E, logits));
     } else {
         dim3 g(cdiv(Tn, 16), cdiv(E, 64));
         MOE_LAUNCH("gate_logits", s,
-            gate_logits_kernel<T, 64, 4, 1><<<g, 256, 0, s>>>(xp, wp, bias, Tn, d, E, logits));
+            gate_logits_kernel<T, 64, 4, 1, 64><<<g, 256, 0, s>>>(xp, wp, bias, Tn, d, E, logits));
     }
     return launch_status();
 }
