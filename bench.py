@@ -33,13 +33,13 @@ PEAK_HBM_GBS = 8000.0
 # of a plain 1 GiB device copy in the same run (factors 6.0 and 1.0); see
 # profiles/hbm_traffic_moe_s_like.md.  Valid only for the kernel sources
 # whose SHA-256 prefix is TRAFFIC_SRC; null once they change.
-TRAFFIC_SRC = "4a5f1442bdce1af8"
+TRAFFIC_SRC = "dc66335b257a61e2"
 TRAFFIC_SOURCES = ("ggemm.hip", "common.h", "permute.hip", "combine.hip")
-TRAFFIC = {"gemm_up_gelu": 1243298119, "gemm_down": 1091191270,
-           "gemm_dA_gelu": 1544264804, "gemm_dW1": 1577256126,
-           "gemm_dW2": 1577256126, "gemm_dX": 1091132523, "perm_copy": 84789385,
-           "combine": 119104451, "combine_bwd": 186418194,
-           "unpermute_grad": 118328733}
+TRAFFIC = {"gemm_up_gelu": 1241548680, "gemm_down": 1095432356,
+           "gemm_dA_gelu": 1507195340, "gemm_dW1": 1577296336,
+           "gemm_dW2": 1577296336, "gemm_dX": 1091167881, "perm_copy": 84791152,
+           "combine": 119104585, "combine_bwd": 186417934,
+           "unpermute_grad": 118328703}
 
 
 def traffic_for(kernel, workload):
