@@ -432,6 +432,9 @@ __device__ __forceinline__ TileInfo decode_tile(const GemmArgs<T>& p) {
 // part of the tile, so lanes past a ragged segment end, the end of the
 // reduction, a partial tile or the allocation read zeros, with no branch.
 constexpr uint32_t OOB = 0x80000000u;    // an offset past any descriptor range
+// Rows of the reduction-row gather map held in LDS at a time (RAGGED_K); a
+// power of two.
+constexpr int KG_CHUNK = 4096;
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
@@ -570,27 +573,35 @@ struct DmaOperand {
         }
     }
     // Source rows of the loads of the stage of reduction rows k0 .. k0+BK-1:
-    // row k is source row lmap[k - kmap] (lmap in LDS); -1 where the load
-    // is past the segment or the tile's columns.
+    // row k is source row lmap[k - kmap] (lmap in LDS; k - kmap lies inside
+    // the map chunk for a stage of it, so the read is unconditional and the
+    // value is only looked at when the stage is issued: the LDS wait of
+    // this read-ahead stays off the issue path).
     __device__ __forceinline__ void rows_of(long k0, const int32_t* lmap, long kmap,
                                             int32_t* rows) const {
         constexpr int NC = ROWS / 8;
         constexpr int RB = 1024 / (ROWS * 2);
         const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-        for (int i = 0; i < NLOAD; ++i) {
-            const long k = k0 + (w + NW * i) * RB + lane / NC;
-            rows[i] = off[i] != OOB && k < k_lim ? lmap[k - kmap] : -1;
-        }
+        for (int i = 0; i < NLOAD; ++i)
+            rows[i] = lmap[(k0 + (w + NW * i) * RB + lane / NC - kmap) & (KG_CHUNK - 1)];
     }
-    // Issue that stage, given rows_of's result.
-    __device__ __forceinline__ void dma_rows(uint8_t* stage, const int32_t* rows) const {
-        const int w = threadIdx.x >> 6;
+    // Issue the stage at k0, given rows_of's result; loads past the segment
+    // or the tile's columns get an offset past the source.
+    __device__ __forceinline__ void dma_rows(long k0, uint8_t* stage, const int32_t* rows) const {
+        constexpr int NC = ROWS / 8;
+        constexpr int RB = 1024 / (ROWS * 2);
+        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
         const i32x4_t rs = rsrc_words(P, span);
         const uint32_t lds0 = lds_addr(stage) + (uint32_t)(w * 1024);
 #pragma unroll
         for (int i = 0; i < NLOAD; ++i) {
-            const uint32_t o = rows[i] >= 0 ? (uint32_t)((long)rows[i] * ld * 2) + off[i] : OOB;
+            // branch-free: a source row offset is below 2^31 (host check),
+            // so setting bit 31 (a column past the tile: off[i] = OOB, or a
+            // row past the segment) sends the load past the descriptor range
+            const long k = k0 + (w + NW * i) * RB + lane / NC;
+            const uint32_t o = ((uint32_t)rows[i] * (uint32_t)(ld * 2) + off[i]) |
+                               ((uint32_t)(k >= k_lim) << 31);
             lds_dma16(rs, o, lds0 + NW * i * 1024);
         }
     }
@@ -658,9 +669,6 @@ __device__ __forceinline__ void stage_barrier_ahead(int ahead) {
     }
 }
 
-// Rows of the reduction-row gather map held in LDS at a time (RAGGED_K).
-constexpr int KG_CHUNK = 4096;
-
 template <int BM, int BN, int WM, int WN, int NSTG, int BK, int MODE, int ALAY, int BLAY,
           bool DUAL, bool KSPLIT, bool GATHER, class Epi>
 __global__ __launch_bounds__(64 * WM * WN, 2) void ggemm_bf16_dma_kernel(GemmArgs<bf16_t> p,
@@ -712,9 +720,22 @@ __global__ __launch_bounds__(64 * WM * WN, 2) void ggemm_bf16_dma_kernel(GemmArg
     // chunk (the barriers make every wave finish with the old chunk first)
     auto load_kmap = [&](long kmap0) {
         if constexpr (KGATHER) {
+            static_assert(KG_CHUNK % NT == 0, "map chunk per thread");
+            constexpr int PER = KG_CHUNK / NT;
             __syncthreads();
-            for (int q = threadIdx.x; q < KG_CHUNK; q += NT)
-                kmap[q] = kmap0 + q < ti.klen ? p.gather[ti.kbeg + kmap0 + q] : 0;
+            if (kmap0 < ti.klen) {
+                // every load in flight before the first store (clamped
+                // addresses, so no load is conditional)
+                int32_t v[PER];
+                const long last = ti.klen - 1;
+#pragma unroll
+                for (int u = 0; u < PER; ++u) {
+                    const long q = kmap0 + threadIdx.x + u * NT;
+                    v[u] = p.gather[ti.kbeg + (q < last ? q : last)];
+                }
+#pragma unroll
+                for (int u = 0; u < PER; ++u) kmap[threadIdx.x + u * NT] = v[u];
+            }
             __syncthreads();
         }
     };
@@ -749,8 +770,10 @@ __global__ __launch_bounds__(64 * WM * WN, 2) void ggemm_bf16_dma_kernel(GemmArg
                 load_kmap(c0);
                 opA.rows_of(k0, kmap, c0, krow);
             }
-            opA.dma_rows(stg, krow);
-            if ((k0 + BK) % KG_CHUNK != 0) opA.rows_of(k0 + BK, kmap, c0, krow);
+            opA.dma_rows(k0, stg, krow);
+            // the next stage's rows (read modulo the chunk: at a chunk switch
+            // they are read again after the reload)
+            opA.rows_of(k0 + BK, kmap, c0, krow);
         } else {
             opA.dma(k0, stg);
         }
@@ -828,11 +851,15 @@ __global__ __launch_bounds__(64 * WM * WN, 2) void ggemm_bf16_dma_kernel(GemmArg
         const uint8_t* cur = ring(qc);
         const int qn = qc + 1 == NSTG ? 0 : qc + 1;    // slot of stage j+1
         const int qf = qc == 0 ? NSTG - 1 : qc - 1;    // slot of stage j-1 = j+NSTG-1
-        if ((NP < NSTG || j > 0) && j + NSTG - 1 < nj) issue(ring(qf), j + NSTG - 1);
+        const bool more = (NP < NSTG || j > 0) && j + NSTG - 1 < nj;
+        // a gathered issue waits on LDS (its row indices), so it goes behind
+        // the first MFMAs of the stage, whose fragments it waits for anyway
+        if (!KGATHER && more) issue(ring(qf), j + NSTG - 1);
 #pragma unroll
         for (int ks = 0; ks + 1 < KS; ++ks) {
             read_frags(cur, ks + 1, (ks + 1) & 1);
             mfmas(ks & 1);
+            if (KGATHER && ks == 0 && more) issue(ring(qf), j + NSTG - 1);
         }
         stage_barrier_ahead<NL, NSTG - 2>(min(nj - 2 - j, NSTG - 2));  // stage j+1 landed
         read_frags(ring(qn), 0, 0);
