@@ -2,8 +2,8 @@
 entry points chained into a forward and a backward pass.
 
 forward:  moe_gate_topk -> moe_permute -> moe_expert_ffn_fwd -> moe_combine
-backward: moe_combine_bwd -> moe_expert_ffn_bwd -> moe_unpermute_grad
-          -> moe_gate_topk_bwd
+backward: moe_combine_bwd -> (moe_gate_topk_bwd on a second stream, into a
+          zeroed dx) and moe_expert_ffn_bwd -> moe_unpermute_grad (adds to dx)
 """
 import torch
 
@@ -13,11 +13,15 @@ from .ops import _stream
 
 class MoELayer:
     def __init__(self, T, d, f, E, k, act="gelu", dtype=torch.bfloat16,
-                 renorm=1, device="cuda", fuse_gather=False):
+                 renorm=1, device="cuda", fuse_gather=False, overlap_gate=True):
         """fuse_gather: no x_perm buffer; the permute only routes and the FFN
-        calls read rows of x through src (moe_expert_ffn_*_gather)."""
+        calls read rows of x through src (moe_expert_ffn_*_gather).
+        overlap_gate: the gate's backward on a second stream beside the
+        expert GEMMs' backward."""
         self.T, self.d, self.f, self.E, self.k = T, d, f, E, k
         self.fuse_gather = bool(fuse_gather)
+        self.overlap_gate = bool(overlap_gate)
+        self._gstream = None
         self.act = MOE_ACT_SWIGLU if act == "swiglu" else MOE_ACT_GELU
         self.dtype = dtype
         self.dt = MOE_BF16 if dtype == torch.bfloat16 else MOE_F32
@@ -102,12 +106,15 @@ class MoELayer:
                                     p(self.dW1), p(self.dW3), p(self.dW2),
                                     p(self.ws_ffn_b), self.ws_ffn_b.numel())),
             ("moe_unpermute_grad", (p(self.dx_perm), p(self.dest), T, k, d, dt,
-                                    p(self.dx), 0)),
-            ("moe_gate_topk_bwd", (p(x), p(Wg), p(self.logits), p(self.topk_idx),
-                                   p(self.topk_w), p(self.d_topk_w), T, d, E, k,
-                                   self.renorm, dt, p(self.dx), p(self.dWg),
-                                   p(self.ws_gate), self.ws_gate.numel())),
+                                    p(self.dx), 1)),
         ]
+        # the gate's backward needs only combine_bwd's d_topk_w: it runs on a
+        # stream of its own beside the expert GEMMs, into a zeroed dx that
+        # moe_unpermute_grad then adds the dispatch gradient to
+        self._gate = ("moe_gate_topk_bwd", (p(x), p(Wg), p(self.logits), p(self.topk_idx),
+                                            p(self.topk_w), p(self.d_topk_w), T, d, E, k,
+                                            self.renorm, dt, p(self.dx), p(self.dWg),
+                                            p(self.ws_gate), self.ws_gate.numel()))
         return self
 
     def _run(self, calls, stream=None):
@@ -121,21 +128,54 @@ class MoELayer:
         return self.y
 
     def backward(self, stream=None):
+        """combine_bwd; then the gate backward (dx = dl Wg^T, dWg) on a second
+        stream while moe_expert_ffn_bwd runs; then dx += the unpermuted
+        dispatch gradient.  overlap_gate = False runs the same calls in the
+        same order on one stream (identical bits)."""
         assert self.dy is not None, "bind(dy=...) first"
-        self._run(self._bwd, stream)
+        s = _stream(self.device) if stream is None else stream
+        ms = (torch.cuda.current_stream(self.device) if stream is None
+              else torch.cuda.ExternalStream(stream, device=self.device))
+        L = self.lib
+        comb, ffn, unperm = self._bwd
+        check(getattr(L, comb[0])(*comb[1], s), comb[0])
+        # under HIP graph capture everything stays on the capturing stream
+        # (plus the library's own side stream): capturing a second user
+        # stream that shares that side stream ended the capture with a
+        # crash in the runtime on this ROCm
+        if self.overlap_gate and not torch.cuda.is_current_stream_capturing():
+            if self._gstream is None:
+                self._gstream = torch.cuda.Stream(device=self.device)
+            gs = self._gstream
+            gs.wait_stream(ms)
+            with torch.cuda.stream(gs):
+                self.dx.zero_()
+            check(getattr(L, self._gate[0])(*self._gate[1], gs.cuda_stream), self._gate[0])
+            check(getattr(L, ffn[0])(*ffn[1], s), ffn[0])
+            ms.wait_stream(gs)
+        else:
+            with torch.cuda.stream(ms):
+                self.dx.zero_()
+            check(getattr(L, self._gate[0])(*self._gate[1], s), self._gate[0])
+            check(getattr(L, ffn[0])(*ffn[1], s), ffn[0])
+        check(getattr(L, unperm[0])(*unperm[1], s), unperm[0])
         return self.dx
 
     def step(self, stream=None):
         """One forward + backward pass."""
         self._run(self._fwd, stream)
-        self._run(self._bwd, stream)
+        self.backward(stream)
 
     def stage_calls(self):
-        """[(name, callable)] of every entry point of one step, in order."""
+        """[(name, callable)] of every step of one layer step, in order, on one
+        stream (the zeroing of dx is the one step that is not an entry point)."""
         L = self.lib
-        return [(n, (lambda n=n, a=a, s=None: check(
+        mk = lambda n, a: (n, (lambda n=n, a=a, s=None: check(
             getattr(L, n)(*a, _stream(self.device) if s is None else s), n)))
-            for n, a in self._fwd + self._bwd]
+        comb, ffn, unperm = self._bwd
+        return ([mk(n, a) for n, a in self._fwd] + [mk(*comb)] +
+                [("dx_zero", lambda s=None: self.dx.zero_())] +
+                [mk(*self._gate), mk(*ffn), mk(*unperm)])
 
 
 class ChunkedMoELayer:
@@ -148,11 +188,12 @@ class ChunkedMoELayer:
     forward:  moe_gate_topk over all tokens; per chunk moe_permute ->
               moe_expert_ffn_fwd -> moe_combine (out_perm is kept whole: the
               gate's backward needs it).
-    backward: chunks in reverse order, the last chunk's saved state still in
-              the buffers; every other chunk re-permutes and recomputes GEMM1
-              (moe_expert_ffn_fwd with out_perm = NULL); moe_combine_bwd ->
-              moe_expert_ffn_bwd (first) / _accumulate (rest) ->
-              moe_unpermute_grad; then moe_gate_topk_bwd over all tokens.
+    backward: moe_combine_bwd of every chunk (d_topk_w), moe_gate_topk_bwd
+              over all tokens into a zeroed dx; then chunks in reverse order,
+              the last chunk's saved state still in the buffers, every other
+              chunk re-permuted with GEMM1 recomputed (moe_expert_ffn_fwd with
+              out_perm = NULL) and its d_out_perm remade; moe_expert_ffn_bwd
+              (first) / _accumulate (rest) -> moe_unpermute_grad (adds to dx).
 
     y, dx, dWg and every routing output are bit-identical to MoELayer's; dW1,
     dW2, dW3 are the same sums taken chunk by chunk (one rounding per chunk
@@ -253,18 +294,38 @@ class ChunkedMoELayer:
     def backward(self, stream=None):
         assert self.dy is not None, "bind(dy=...) first"
         s = _stream(self.device) if stream is None else stream
+        ms = (torch.cuda.current_stream(self.device) if stream is None
+              else torch.cuda.ExternalStream(stream, device=self.device))
         p = lambda t: None if t is None else t.data_ptr()
         L, T, d, f, E, k = self.lib, self.T, self.d, self.f, self.E, self.k
-        first = True
-        for c, t0, tc, r0, rc in reversed(list(self._chunks())):
-            if c != self._resident:        # the forward's last chunk is still in place
-                self._permute(c, t0, tc, r0, s)
-                self._ffn_fwd(c, rc, None, s)
-                self._resident = c
+
+        def comb(t0, tc, r0):
             check(L.moe_combine_bwd(p(self.dy[t0:]), p(self.out_perm[r0:]), p(self.dest[t0:]),
                                     p(self.topk_w[t0:]), tc, k, d, self.dt,
                                     p(self.d_out_perm), p(self.d_topk_w[t0:]), s),
                   "moe_combine_bwd")
+        # d_topk_w of every token first: the gate's backward (dx = dl Wg^T,
+        # dWg) comes before the dispatch gradient is added, the order
+        # MoELayer uses, so that dx has the same bits
+        chunks = list(self._chunks())
+        for c, t0, tc, r0, rc in chunks:
+            comb(t0, tc, r0)
+        dout = self.nch - 1                    # chunk whose d_out_perm is in place
+        with torch.cuda.stream(ms):
+            self.dx.zero_()
+        check(L.moe_gate_topk_bwd(p(self.x), p(self.Wg), p(self.logits), p(self.topk_idx),
+                                  p(self.topk_w), p(self.d_topk_w), T, d, E, k, self.renorm,
+                                  self.dt, p(self.dx), p(self.dWg), p(self.ws_gate),
+                                  self.ws_gate.numel(), s), "moe_gate_topk_bwd")
+        first = True
+        for c, t0, tc, r0, rc in reversed(chunks):
+            if c != self._resident:        # the forward's last chunk is still in place
+                self._permute(c, t0, tc, r0, s)
+                self._ffn_fwd(c, rc, None, s)
+                self._resident = c
+            if c != dout:
+                comb(t0, tc, r0)
+                dout = c
             fn = L.moe_expert_ffn_bwd if first else L.moe_expert_ffn_bwd_accumulate
             check(fn(p(self.d_out_perm), p(self.x_perm), p(self.h_save), p(self.a_save),
                      p(self.offsets[c]), rc, E, d, f, self.act, self.dt, p(self.W1),
@@ -273,11 +334,7 @@ class ChunkedMoELayer:
                   "moe_expert_ffn_bwd")
             first = False
             check(L.moe_unpermute_grad(p(self.dx_perm), p(self.dest[t0:]), tc, k, d, self.dt,
-                                       p(self.dx[t0:]), 0, s), "moe_unpermute_grad")
-        check(L.moe_gate_topk_bwd(p(self.x), p(self.Wg), p(self.logits), p(self.topk_idx),
-                                  p(self.topk_w), p(self.d_topk_w), T, d, E, k, self.renorm,
-                                  self.dt, p(self.dx), p(self.dWg), p(self.ws_gate),
-                                  self.ws_gate.numel(), s), "moe_gate_topk_bwd")
+                                       p(self.dx[t0:]), 1, s), "moe_unpermute_grad")
         return self.dx
 
     def step(self, stream=None):
