@@ -30,16 +30,17 @@ PEAK_HBM_GBS = 8000.0
 # HBM bytes per call (fetch + write; a GEMM stage's main and partial-tile
 # launches together) of the FFN and row kernels on the MoE-S-like workload,
 # from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs scaled by the readings
-# of a plain 1 GiB device copy in the same run (factors 6.0 and 1.0); see
+# of a plain 4 GiB device copy with a cold source in the same run (factors
+# 4.0 and 2.0); see
 # profiles/hbm_traffic_moe_s_like.md.  Valid only for the kernel sources
 # whose SHA-256 prefix is TRAFFIC_SRC; null once they change.
-TRAFFIC_SRC = "dc66335b257a61e2"
+TRAFFIC_SRC = "2989eeaaa3d5de73"
 TRAFFIC_SOURCES = ("ggemm.hip", "common.h", "permute.hip", "combine.hip")
-TRAFFIC = {"gemm_up_gelu": 1241548680, "gemm_down": 1095432356,
-           "gemm_dA_gelu": 1507195340, "gemm_dW1": 1577296336,
-           "gemm_dW2": 1577296336, "gemm_dX": 1091167881, "perm_copy": 84791152,
-           "combine": 119104585, "combine_bwd": 186417934,
-           "unpermute_grad": 118328703}
+TRAFFIC = {"gemm_up_gelu": 1185267090, "gemm_down": 772604303,
+           "gemm_dA_gelu": 1183873650, "gemm_dW1": 1141077995,
+           "gemm_dW2": 1141077995, "gemm_dX": 772232163, "perm_copy": 101268262,
+           "combine": 101778949, "combine_bwd": 169114443,
+           "unpermute_grad": 134813990}
 
 
 def traffic_for(kernel, workload):
@@ -232,14 +233,21 @@ def main():
     s = stream.cuda_stream
     if args.calib_copy_mb:
         # plain elementwise copy (ordinary loads and stores) of a known size:
-        # reads and writes calib_copy_mb MiB each
+        # reads and writes calib_copy_mb MiB each.  The source is evicted from
+        # the 256 MB MALL first (a 1 GiB read of other data), and the copy
+        # should be many times the MALL, so that few of its writes are still
+        # waiting there when it ends: otherwise the counters see less than
+        # the copy moves
         n = (args.calib_copy_mb << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
+        junk = torch.ones(256 << 20, dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        junk.sum()
         torch.cuda.synchronize()
         torch.add(src, 0.0, out=dst)
         torch.cuda.synchronize()
-        del src, dst
+        del src, dst, junk
 
     for _ in range(args.warmup):
         layer.step(s)
