@@ -95,3 +95,76 @@ def test_chunking_bounds_the_activation_memory():
     # per-row activations: x_perm, h_save, a_save, d_out_perm, dx_perm and dH
     # for T*k rows against one 1024-token chunk (out_perm stays whole)
     assert peaks[1] < 0.5 * peaks[0], peaks
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
+def test_accumulate_entry_point_and_gemm1_only(act, dt):
+    """moe_expert_ffn_bwd_accumulate adds to what dW holds (old + new in fp32,
+    one rounding); R = 0 leaves dW untouched; moe_expert_ffn_fwd with out_perm
+    = NULL writes the same saved state as the full call."""
+    from moe_inputs import stage
+    from _gpu import dev, dev_i32
+    banner("accumulate", act, dt)
+    counts = [300, 0, 17, 513, 64]
+    E, d, f = len(counts), 128, 192
+    offsets = stage.counts_to_offsets(counts)
+    R = int(offsets[-1])
+    xp = stage.normal(51, (R, d), 1.0, dt)
+    W1 = stage.normal(52, (E, d, f), 1 / np.sqrt(d), dt)
+    W2 = stage.normal(53, (E, f, d), 1 / np.sqrt(f), dt)
+    W3 = stage.normal(54, (E, d, f), 1 / np.sqrt(d), dt) if act == "swiglu" else None
+    dO = stage.normal(55, (R, d), 1.0, dt)
+    base1 = stage.normal(56, (E, d, f), 0.1, dt)
+    base2 = stage.normal(57, (E, f, d), 0.1, dt)
+    g = dict(xp=dev(xp, dt), off=dev_i32(offsets), W1=dev(W1, dt), W2=dev(W2, dt),
+             W3=dev(W3, dt) if W3 is not None else None, dO=dev(dO, dt))
+    h, a, o = M.moe_expert_ffn_fwd(g["xp"], g["off"], g["W1"], g["W2"], g["W3"], act)
+    h1, a1 = torch.empty_like(h), torch.empty_like(a)
+    L = M.load()
+    from mixture_experts_layer_permute_amd import _lib
+    ws = torch.empty(max(L.moe_ffn_workspace_bytes(R, E, d, f, 1 if act == "swiglu" else 0,
+                                                   1 if dt == "bf16" else 0, 0), 1),
+                     dtype=torch.uint8, device="cuda")
+    p = lambda t: None if t is None else t.data_ptr()
+    _lib.check(L.moe_expert_ffn_fwd(p(g["xp"]), p(g["off"]), R, E, d, f,
+                                    1 if act == "swiglu" else 0, 1 if dt == "bf16" else 0,
+                                    p(g["W1"]), p(g["W3"]), None, p(h1), p(a1), None, p(ws),
+                                    ws.numel(), torch.cuda.current_stream().cuda_stream),
+               "moe_expert_ffn_fwd (GEMM1 only)")
+    torch.cuda.synchronize()
+    assert torch.equal(h, h1) and torch.equal(a, a1)
+    # accumulate onto base values
+    dW1 = dev(base1, dt)
+    dW2 = dev(base2, dt)
+    dW3 = dev(base1, dt) if act == "swiglu" else None
+    bw = M.moe_expert_ffn_bwd(g["dO"], g["xp"], h, a, g["off"], g["W1"], g["W2"], g["W3"], act)
+    ws_b = torch.empty(max(L.moe_ffn_workspace_bytes(R, E, d, f, 1 if act == "swiglu" else 0,
+                                                     1 if dt == "bf16" else 0, 1), 1),
+                       dtype=torch.uint8, device="cuda")
+    dxp = torch.empty_like(g["dO"])
+    _lib.check(L.moe_expert_ffn_bwd_accumulate(
+        p(g["dO"]), p(g["xp"]), p(h), p(a), p(g["off"]), R, E, d, f,
+        1 if act == "swiglu" else 0, 1 if dt == "bf16" else 0, p(g["W1"]), p(g["W3"]),
+        p(g["W2"]), p(dxp), p(dW1), p(dW3), p(dW2), p(ws_b), ws_b.numel(),
+        torch.cuda.current_stream().cuda_stream), "moe_expert_ffn_bwd_accumulate")
+    torch.cuda.synchronize()
+    assert torch.equal(dxp, bw[0]), "dx_perm"
+    want1 = base1.astype(np.float64) + host(bw[1])
+    want2 = base2.astype(np.float64) + host(bw[3])
+    assert_close(dW1, want1, dt, "dW1 += ")
+    assert_close(dW2, want2, dt, "dW2 += ")
+    if act == "swiglu":
+        assert_close(dW3, base1.astype(np.float64) + host(bw[2]), dt, "dW3 += ")
+    # an empty expert adds nothing: its rows of dW keep the old bits exactly
+    assert torch.equal(dW1[1], dev(base1, dt)[1]) and torch.equal(dW2[1], dev(base2, dt)[1])
+    # R = 0: dW unchanged
+    before = dW1.clone()
+    zero_off = dev_i32(np.zeros(E + 1, np.int32))
+    _lib.check(L.moe_expert_ffn_bwd_accumulate(
+        None, None, None, None, p(zero_off), 0, E, d, f, 1 if act == "swiglu" else 0,
+        1 if dt == "bf16" else 0, p(g["W1"]), p(g["W3"]), p(g["W2"]), None, p(dW1), p(dW3),
+        p(dW2), p(ws_b), ws_b.numel(), torch.cuda.current_stream().cuda_stream),
+        "moe_expert_ffn_bwd_accumulate R=0")
+    torch.cuda.synchronize()
+    assert torch.equal(before, dW1)
