@@ -13,10 +13,24 @@
 // fused multiply-add gives the same bits.
 #include <float.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "common.h"
 
 namespace moe {
 namespace {
+
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>): an
+// unrolled loop whose index is a compile-time constant in the body.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_seq(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_seq(f, std::make_integer_sequence<int, N>{});
+}
 
 // ------------------------------------------------------------ logits
 // Block: 256 threads.  TE experts per block column, EPT of them per thread
@@ -26,11 +40,10 @@ namespace {
 // feature order.  Features come in chunks of GKC: the token rows are copied
 // to LDS as raw 16-byte vectors (padded rows), the gate columns as fp32
 // transposed to [expert][feature] so that one 16-byte read yields four
-// consecutive features of one expert; the next chunk is fetched into
+// consecutive features of one expert; the next NPF chunks are fetched into
 // registers while the current one is consumed.  With few experts a thread
-// has a single chain, so the chunk is long (256 features): enough
-// dependent multiply-adds to cover the next chunk's fetch.
-template <typename T, int TE, int EPT, int MT, int GKC>
+// has a single chain, so the chunk is long (256 features).
+template <typename T, int TE, int EPT, int MT, int GKC, int NPF>
 __global__ __launch_bounds__(256) void gate_logits_kernel(
     const T* __restrict__ x, const T* __restrict__ Wg,
     const float* __restrict__ bias, int Tn, int d, int E,
@@ -54,29 +67,34 @@ __global__ __launch_bounds__(256) void gate_logits_kernel(
     const long t0 = (long)blockIdx.x * TT;
     const int e0 = blockIdx.y * TE;
 
-    uint4 xr[XV];
-    float wr[WV];
-    auto fetch = [&](int k0) {
+    // NPF chunks in flight: chunk c lives in register slot c % NPF from its
+    // fetch until it is copied to LDS
+    uint4 xr_all[NPF][XV];
+    float wr_all[NPF][WV];
+    auto fetch = [&](int k0, uint4 (&xr)[XV], float (&wr)[WV]) {
+        // Every load is issued (out-of-range ones read element 0) and the
+        // value selected afterwards: a load under a branch is followed by a
+        // full wait for it, which would serialise the fetch.
 #pragma unroll
         for (int q = 0; q < XV; ++q) {
             const int idx = tid + 256 * q;
             const int tok = idx / VPR, c = idx % VPR;
             const long t = t0 + tok;
             const int k = k0 + c * V;
-            xr[q] = make_uint4(0, 0, 0, 0);
-            if (idx < TT * VPR && t < Tn && k < d)
-                xr[q] = *reinterpret_cast<const uint4*>(x + t * d + k);
+            const bool ok = idx < TT * VPR && t < Tn && k < d;
+            const uint4 v = *reinterpret_cast<const uint4*>(x + (ok ? t * d + k : 0));
+            xr[q] = ok ? v : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int q = 0; q < WV; ++q) {
             const int idx = tid + 256 * q;
             const int kk = idx / TE, ee = idx % TE;
-            wr[q] = 0.0f;
-            if (idx < GKC * TE && k0 + kk < d && e0 + ee < E)
-                wr[q] = Elem<T>::ld(Wg + (long)(k0 + kk) * E + e0 + ee);
+            const bool ok = idx < GKC * TE && k0 + kk < d && e0 + ee < E;
+            const float v = Elem<T>::ld(Wg + (ok ? (long)(k0 + kk) * E + e0 + ee : 0));
+            wr[q] = ok ? v : 0.0f;
         }
     };
-    auto stash = [&]() {
+    auto stash = [&](const uint4 (&xr)[XV], const float (&wr)[WV]) {
 #pragma unroll
         for (int q = 0; q < XV; ++q) {
             const int idx = tid + 256 * q;
@@ -96,12 +114,14 @@ __global__ __launch_bounds__(256) void gate_logits_kernel(
 #pragma unroll
         for (int b = 0; b < EPT; ++b) acc[m][b] = 0.0f;
 
-    fetch(0);
-    for (int k0 = 0; k0 < d; k0 += GKC) {
+    // one chunk: copy it to LDS, refill its register slot with the chunk
+    // NPF further on, then run every chain over its features
+    auto chunk = [&](int k0, auto slot) {
+        constexpr int c = decltype(slot)::value;
         __syncthreads();
-        stash();
+        stash(xr_all[c], wr_all[c]);
         __syncthreads();
-        if (k0 + GKC < d) fetch(k0 + GKC);
+        if (k0 + NPF * GKC < d) fetch(k0 + NPF * GKC, xr_all[c], wr_all[c]);
         const int kmax = min(GKC, d - k0);          // a multiple of V
         for (int kv = 0; kv < kmax / V; ++kv) {
             float xv[MT][V];
@@ -135,6 +155,17 @@ __global__ __launch_bounds__(256) void gate_logits_kernel(
                         }
             }
         }
+    };
+    if constexpr (NPF == 1) {
+        fetch(0, xr_all[0], wr_all[0]);
+        for (int k0 = 0; k0 < d; k0 += GKC) chunk(k0, std::integral_constant<int, 0>{});
+    } else {
+#pragma unroll
+        for (int c = 0; c < NPF; ++c) fetch(c * GKC, xr_all[c], wr_all[c]);   // zeros past d
+        for (int kb = 0; kb < d; kb += NPF * GKC)
+            static_for<NPF>([&](auto c) {
+                if (kb + c * GKC < d) chunk(kb + c * GKC, c);
+            });
     }
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
@@ -454,6 +485,25 @@ __global__ __launch_bounds__(256) void gate_dx_kernel(
     }
 }
 
+// Chunks in flight per thread: when the grid is at most a couple of blocks
+// per compute unit, a thread's chain is the only work its SIMD has, so the
+// loads of several chunks are put in flight at once; a larger grid hides
+// the fetch with other blocks and keeps its registers for occupancy.
+constexpr int kNpfFew = 4, kNpfMany = 1;
+
+template <typename T, int TE, int EPT, int MT, int GKC>
+void logits_go(dim3 g, const T* xp, const T* wp, const float* bias, int Tn, int d, int E,
+               float* logits, hipStream_t s) {
+    if ((long)g.x * g.y <= 2L * max(device_cus(), 1))
+        MOE_LAUNCH("gate_logits", s,
+            gate_logits_kernel<T, TE, EPT, MT, GKC, kNpfFew><<<g, 256, 0, s>>>(
+                xp, wp, bias, Tn, d, E, logits));
+    else
+        MOE_LAUNCH("gate_logits", s,
+            gate_logits_kernel<T, TE, EPT, MT, GKC, kNpfMany><<<g, 256, 0, s>>>(
+                xp, wp, bias, Tn, d, E, logits));
+}
+
 template <typename T>
 moe_status launch_logits(const void* x, const void* Wg, const float* bias,
                          int Tn, int d, int E, float* logits, hipStream_t s) {
@@ -461,23 +511,18 @@ moe_status launch_logits(const void* x, const void* Wg, const float* bias,
     const T* wp = static_cast<const T*>(Wg);
     // tokens per block = MT * 256 / (TE / EPT); one expert per thread for
     // small E keeps the grid at Tn/32 or more blocks
-    if (E <= 8) {
-        dim3 g(cdiv(Tn, 32), cdiv(E, 8));
-        MOE_LAUNCH("gate_logits", s,
-            gate_logits_kernel<T, 8, 1, 1, 256><<<g, 256, 0, s>>>(xp, wp, bias, Tn, d, E, logits));
-    } else if (E <= 16) {
-        dim3 g(cdiv(Tn, 16), cdiv(E, 16));
-        MOE_LAUNCH("gate_logits", s,
-            gate_logits_kernel<T, 16, 1, 1, 256><<<g, 256, 0, s>>>(xp, wp, bias, Tn, d, E, logits));
-    } else if (E <= 32) {
-        dim3 g(cdiv(Tn, 16), cdiv(E, 32));
-        MOE_LAUNCH("gate_logits", s,
-            gate_logits_kernel<T, 32, 2, 1, 128><<<g, 256, 0, s>>>(xp, wp, bias, Tn, d, E, logits));
-    } else {
-        dim3 g(cdiv(Tn, 16), cdiv(E, 64));
-        MOE_LAUNCH("gate_logits", s,
-            gate_logits_kernel<T, 64, 4, 1, 64><<<g, 256, 0, s>>>(xp, wp, bias, Tn, d, E, logits));
-    }
+    if (E <= 8)
+        logits_go<T, 8, 1, 1, 256>(dim3(cdiv(Tn, 32), cdiv(E, 8)), xp, wp, bias, Tn, d, E,
+                                   logits, s);
+    else if (E <= 16)
+        logits_go<T, 16, 1, 1, 256>(dim3(cdiv(Tn, 16), cdiv(E, 16)), xp, wp, bias, Tn, d, E,
+                                    logits, s);
+    else if (E <= 32)
+        logits_go<T, 32, 2, 1, 128>(dim3(cdiv(Tn, 16), cdiv(E, 32)), xp, wp, bias, Tn, d, E,
+                                    logits, s);
+    else
+        logits_go<T, 64, 4, 1, 64>(dim3(cdiv(Tn, 16), cdiv(E, 64)), xp, wp, bias, Tn, d, E,
+                                   logits, s);
     return launch_status();
 }
 

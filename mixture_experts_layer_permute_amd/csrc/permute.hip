@@ -160,7 +160,9 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(
 }
 
 // x_perm[dest[t,j], :] = x[t, :].  One wave per token; 16-byte lanes; the
-// row is loaded once and stored k times.
+// row is loaded once and stored k times.  The four vectors a lane carries
+// are named values, not an array: an array read back inside the runtime-k
+// loop is placed in LDS by the compiler, with a full wait after every load.
 template <typename T>
 __global__ __launch_bounds__(256) void perm_copy_kernel(
     const T* __restrict__ x, const int32_t* __restrict__ dest, int Tn, int d,
@@ -173,21 +175,20 @@ __global__ __launch_bounds__(256) void perm_copy_kernel(
     const int nvec = d / V;
     const uint4* xr = reinterpret_cast<const uint4*>(x + t * d);
     for (int v0 = 0; v0 < nvec; v0 += 64 * 4) {
-        uint4 buf[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int v = v0 + u * 64 + lane;
-            if (v < nvec) buf[u] = xr[v];
-        }
+        const int va = v0 + lane, vb = va + 64, vc = va + 128, vd = va + 192;
+        // out-of-row lanes load the row's last vector (never stored)
+        const uint4 b0 = xr[min(va, nvec - 1)];
+        const uint4 b1 = xr[min(vb, nvec - 1)];
+        const uint4 b2 = xr[min(vc, nvec - 1)];
+        const uint4 b3 = xr[min(vd, nvec - 1)];
         for (int j = 0; j < k; ++j) {
             const int r = dest[t * k + j];
             if ((unsigned)r >= (unsigned)(Tn * k)) continue;
             uint4* outr = reinterpret_cast<uint4*>(x_perm + (long)r * d);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int v = v0 + u * 64 + lane;
-                if (v < nvec) outr[v] = buf[u];
-            }
+            if (va < nvec) outr[va] = b0;
+            if (vb < nvec) outr[vb] = b1;
+            if (vc < nvec) outr[vc] = b2;
+            if (vd < nvec) outr[vd] = b3;
         }
     }
 }
