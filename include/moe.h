@@ -281,8 +281,9 @@ moe_status moe_unpermute_grad(const void *dx_perm, const int32_t *dest, int T,
  *   renorm=0: dl[t,e] = p_e (g_e - sum_j w_j dw_j), p = softmax(logits[t,:]),
  *             g_e = dw_j where e = idx_j else 0
  *   dWg = x^T dl (overwritten; the sum over tokens runs in fixed chunks
- *         reduced in order), dx += dl Wg^T (accumulated: call after
- *         moe_unpermute_grad has written dx).
+ *         reduced in order); dx = dl Wg^T, or dx += dl Wg^T when
+ *         accumulate != 0 (then dx must hold values, e.g. the output of
+ *         moe_unpermute_grad).
  *   x [T,d] dt, Wg [d,E] dt, logits [T,E], topk_idx [T,k], topk_w [T,k],
  *   d_topk_w [T,k] float, dx [T,d] dt, dWg [d,E] dt.
  *   ws: at least moe_gate_bwd_workspace_bytes(T,d,E).
@@ -291,8 +292,9 @@ size_t moe_gate_bwd_workspace_bytes(int T, int d, int E);
 moe_status moe_gate_topk_bwd(const void *x, const void *Wg, const float *logits,
                              const int32_t *topk_idx, const float *topk_w,
                              const float *d_topk_w, int T, int d, int E, int k,
-                             int renorm, moe_dtype dt, void *dx, void *dWg,
-                             void *ws, size_t ws_bytes, hipStream_t stream);
+                             int renorm, moe_dtype dt, void *dx,
+                             int accumulate, void *dWg, void *ws,
+                             size_t ws_bytes, hipStream_t stream);
 
 /*
  * Kernel timing (benchmark support, off by default).

@@ -429,14 +429,16 @@ __global__ void gate_transpose_kernel(const T* __restrict__ Wg, int d, int E,
     WgT[(long)e * d + i] = Elem<T>::ld(Wg + q);
 }
 
-// dx[t,:] += sum_e dl[t,e] WgT[e,:].  renorm=1 uses the k nonzero entries
-// only (coefficients recomputed from w and dw); renorm=0 reads dl.
+// dx[t,:] (+)= sum_e dl[t,e] WgT[e,:].  renorm=1 uses the k nonzero entries
+// only (coefficients recomputed from w and dw); renorm=0 reads dl.  Without
+// accumulate the old dx is not read: the sum is added to +0, which gives the
+// bits that adding it to a zeroed dx gives.
 // One block of 256 threads per token, 16 bytes of dx per thread step.
 template <typename T>
 __global__ __launch_bounds__(256) void gate_dx_kernel(
     const float* __restrict__ WgT, const float* __restrict__ dl,
     const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_w,
-    const float* __restrict__ dw, int d, int E, int k, int renorm,
+    const float* __restrict__ dw, int d, int E, int k, int renorm, int accumulate,
     T* __restrict__ dx) {
     extern __shared__ float coef_mem[];       // [E] coefficients (renorm=0) or [2k]
     const long t = blockIdx.x;
@@ -478,7 +480,12 @@ __global__ __launch_bounds__(256) void gate_dx_kernel(
             for (int q = 0; q < V; ++q) acc[q] = fmaf(cf, w[q], acc[q]);
         }
         float cur[V];
-        Vec16<T>::ld(dx + t * d + i0, cur);
+        if (accumulate) {
+            Vec16<T>::ld(dx + t * d + i0, cur);
+        } else {
+#pragma unroll
+            for (int q = 0; q < V; ++q) cur[q] = 0.0f;
+        }
 #pragma unroll
         for (int q = 0; q < V; ++q) cur[q] = cur[q] + acc[q];
         Vec16<T>::st(dx + t * d + i0, cur);
@@ -582,7 +589,7 @@ template <typename T>
 moe_status launch_gate_bwd(const void* x, const void* Wg, const float* logits,
                            const int32_t* idx, const float* w, const float* dw,
                            int Tn, int d, int E, int k, int renorm, void* dx,
-                           void* dWg, void* ws, hipStream_t s) {
+                           int accumulate, void* dWg, void* ws, hipStream_t s) {
     const GateBwdWs L = gate_bwd_layout(Tn, d, E);
     char* base = static_cast<char*>(ws);
     float* dl = reinterpret_cast<float*>(base + L.dl);
@@ -613,7 +620,8 @@ moe_status launch_gate_bwd(const void* x, const void* Wg, const float* logits,
     if (Tn > 0)     // no tokens: dWg is zero (one empty chunk), dx is empty
         MOE_LAUNCH("gate_dx", s,
             gate_dx_kernel<T><<<Tn, 256, lds_dx + 16, s>>>(wgt, dl, idx, w, dw, d, E, k,
-                                                            renorm, static_cast<T*>(dx)));
+                                                            renorm, accumulate ? 1 : 0,
+                                                            static_cast<T*>(dx)));
     if (side.ok() && !side.join()) return MOE_ERR_HIP;
     return launch_status();
 }
@@ -652,8 +660,8 @@ size_t moe_gate_bwd_workspace_bytes(int T, int d, int E) {
 moe_status moe_gate_topk_bwd(const void* x, const void* Wg, const float* logits,
                              const int32_t* topk_idx, const float* topk_w,
                              const float* d_topk_w, int T, int d, int E, int k,
-                             int renorm, moe_dtype dt, void* dx, void* dWg,
-                             void* ws, size_t ws_bytes, hipStream_t stream) {
+                             int renorm, moe_dtype dt, void* dx, int accumulate,
+                             void* dWg, void* ws, size_t ws_bytes, hipStream_t stream) {
     MOE_CHECK_ARG(T >= 0 && d >= 1 && E >= 1 && E <= 1024 && k >= 1 && k <= E);
     MOE_CHECK_ARG((long long)T * k < (1ll << 31));
     MOE_CHECK_ARG(dt == MOE_F32 || dt == MOE_BF16);
@@ -667,9 +675,9 @@ moe_status moe_gate_topk_bwd(const void* x, const void* Wg, const float* logits,
     MOE_CHECK_DEVICE();
     return dt == MOE_BF16
         ? launch_gate_bwd<bf16_t>(x, Wg, logits, topk_idx, topk_w, d_topk_w, T, d,
-                                  E, k, renorm, dx, dWg, ws, stream)
+                                  E, k, renorm, dx, accumulate, dWg, ws, stream)
         : launch_gate_bwd<float>(x, Wg, logits, topk_idx, topk_w, d_topk_w, T, d,
-                                 E, k, renorm, dx, dWg, ws, stream);
+                                 E, k, renorm, dx, accumulate, dWg, ws, stream);
 }
 
 }  // extern "C"

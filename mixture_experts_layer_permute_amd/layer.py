@@ -2,13 +2,27 @@
 entry points chained into a forward and a backward pass.
 
 forward:  moe_gate_topk -> moe_permute -> moe_expert_ffn_fwd -> moe_combine
-backward: moe_combine_bwd -> (moe_gate_topk_bwd on a second stream, into a
-          zeroed dx) and moe_expert_ffn_bwd -> moe_unpermute_grad (adds to dx)
+backward: moe_combine_bwd -> (moe_gate_topk_bwd on a second stream, writes
+          dx) and moe_expert_ffn_bwd -> moe_unpermute_grad (adds to dx)
 """
 import torch
 
 from ._lib import MOE_ACT_GELU, MOE_ACT_SWIGLU, MOE_BF16, MOE_F32, check, load
 from .ops import _stream
+
+
+def _torch_stream(handle, device):
+    """torch's stream object for a raw stream handle.  The current and the
+    default stream map to torch's own objects: an ExternalStream wrapped
+    around handle 0 did not order events against work on the default stream
+    (a dx computed on a second stream joined through it raced on the GPU)."""
+    cur = torch.cuda.current_stream(device)
+    if handle is None or handle == cur.cuda_stream:
+        return cur
+    dflt = torch.cuda.default_stream(device)
+    if handle == dflt.cuda_stream:
+        return dflt
+    return torch.cuda.ExternalStream(handle, device=device)
 
 
 class MoELayer:
@@ -109,11 +123,11 @@ class MoELayer:
                                     p(self.dx), 1)),
         ]
         # the gate's backward needs only combine_bwd's d_topk_w: it runs on a
-        # stream of its own beside the expert GEMMs, into a zeroed dx that
+        # stream of its own beside the expert GEMMs; it writes dx, and
         # moe_unpermute_grad then adds the dispatch gradient to
         self._gate = ("moe_gate_topk_bwd", (p(x), p(Wg), p(self.logits), p(self.topk_idx),
                                             p(self.topk_w), p(self.d_topk_w), T, d, E, k,
-                                            self.renorm, dt, p(self.dx), p(self.dWg),
+                                            self.renorm, dt, p(self.dx), 0, p(self.dWg),
                                             p(self.ws_gate), self.ws_gate.numel()))
         return self
 
@@ -134,8 +148,7 @@ class MoELayer:
         same order on one stream (identical bits)."""
         assert self.dy is not None, "bind(dy=...) first"
         s = _stream(self.device) if stream is None else stream
-        ms = (torch.cuda.current_stream(self.device) if stream is None
-              else torch.cuda.ExternalStream(stream, device=self.device))
+        ms = _torch_stream(stream, self.device)
         L = self.lib
         comb, ffn, unperm = self._bwd
         check(getattr(L, comb[0])(*comb[1], s), comb[0])
@@ -148,14 +161,10 @@ class MoELayer:
                 self._gstream = torch.cuda.Stream(device=self.device)
             gs = self._gstream
             gs.wait_stream(ms)
-            with torch.cuda.stream(gs):
-                self.dx.zero_()
             check(getattr(L, self._gate[0])(*self._gate[1], gs.cuda_stream), self._gate[0])
             check(getattr(L, ffn[0])(*ffn[1], s), ffn[0])
             ms.wait_stream(gs)
         else:
-            with torch.cuda.stream(ms):
-                self.dx.zero_()
             check(getattr(L, self._gate[0])(*self._gate[1], s), self._gate[0])
             check(getattr(L, ffn[0])(*ffn[1], s), ffn[0])
         check(getattr(L, unperm[0])(*unperm[1], s), unperm[0])
@@ -168,13 +177,12 @@ class MoELayer:
 
     def stage_calls(self):
         """[(name, callable)] of every step of one layer step, in order, on one
-        stream (the zeroing of dx is the one step that is not an entry point)."""
+        stream."""
         L = self.lib
         mk = lambda n, a: (n, (lambda n=n, a=a, s=None: check(
             getattr(L, n)(*a, _stream(self.device) if s is None else s), n)))
         comb, ffn, unperm = self._bwd
         return ([mk(n, a) for n, a in self._fwd] + [mk(*comb)] +
-                [("dx_zero", lambda s=None: self.dx.zero_())] +
                 [mk(*self._gate), mk(*ffn), mk(*unperm)])
 
 
@@ -189,7 +197,7 @@ class ChunkedMoELayer:
               moe_expert_ffn_fwd -> moe_combine (out_perm is kept whole: the
               gate's backward needs it).
     backward: moe_combine_bwd of every chunk (d_topk_w), moe_gate_topk_bwd
-              over all tokens into a zeroed dx; then chunks in reverse order,
+              over all tokens, which writes dx; then chunks in reverse order,
               the last chunk's saved state still in the buffers, every other
               chunk re-permuted with GEMM1 recomputed (moe_expert_ffn_fwd with
               out_perm = NULL) and its d_out_perm remade; moe_expert_ffn_bwd
@@ -294,8 +302,6 @@ class ChunkedMoELayer:
     def backward(self, stream=None):
         assert self.dy is not None, "bind(dy=...) first"
         s = _stream(self.device) if stream is None else stream
-        ms = (torch.cuda.current_stream(self.device) if stream is None
-              else torch.cuda.ExternalStream(stream, device=self.device))
         p = lambda t: None if t is None else t.data_ptr()
         L, T, d, f, E, k = self.lib, self.T, self.d, self.f, self.E, self.k
 
@@ -311,11 +317,9 @@ class ChunkedMoELayer:
         for c, t0, tc, r0, rc in chunks:
             comb(t0, tc, r0)
         dout = self.nch - 1                    # chunk whose d_out_perm is in place
-        with torch.cuda.stream(ms):
-            self.dx.zero_()
         check(L.moe_gate_topk_bwd(p(self.x), p(self.Wg), p(self.logits), p(self.topk_idx),
                                   p(self.topk_w), p(self.d_topk_w), T, d, E, k, self.renorm,
-                                  self.dt, p(self.dx), p(self.dWg), p(self.ws_gate),
+                                  self.dt, p(self.dx), 0, p(self.dWg), p(self.ws_gate),
                                   self.ws_gate.numel(), s), "moe_gate_topk_bwd")
         first = True
         for c, t0, tc, r0, rc in reversed(chunks):

@@ -245,8 +245,8 @@ def moe_unpermute_grad(dx_perm, dest, dx=None, accumulate=0):
 
 
 def moe_gate_topk_bwd(x, Wg, logits, topk_idx, topk_w, d_topk_w, dx, renorm=1,
-                      dWg=None, ws=None):
-    """dx += dl Wg^T in place; -> dWg [d,E]."""
+                      dWg=None, ws=None, accumulate=True):
+    """dx += dl Wg^T in place (dx = dl Wg^T with accumulate=False); -> dWg [d,E]."""
     _need_gpu(x, Wg, logits, topk_idx, topk_w, d_topk_w, dx)
     T, d = x.shape
     E = Wg.shape[1]
@@ -259,6 +259,7 @@ def moe_gate_topk_bwd(x, Wg, logits, topk_idx, topk_w, d_topk_w, dx, renorm=1,
         ws = _ws(L.moe_gate_bwd_workspace_bytes(T, d, E), dev)
     check(L.moe_gate_topk_bwd(_p(x), _p(Wg), _p(logits), _p(topk_idx), _p(topk_w),
                               _p(d_topk_w), T, d, E, k, renorm, _dt(x), _p(dx),
-                              _p(dWg), _p(ws), ws.numel(), _stream(dev)),
+                              int(bool(accumulate)), _p(dWg), _p(ws), ws.numel(),
+                              _stream(dev)),
           "moe_gate_topk_bwd")
     return dWg

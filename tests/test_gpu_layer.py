@@ -95,3 +95,57 @@ def test_stream_overlap_bit_identical(name):
         M.moe_set_overlap(True)
     for n in outs[0]:
         assert torch.equal(outs[0][n], outs[1][n]), n
+
+
+@pytest.mark.parametrize("stream_kind", ["default", "created"])
+def test_back_to_back_steps(stream_kind):
+    """Steps issued back to back with no host synchronisation, alternating
+    two input sets (x and dy negated/halved: other routing, other
+    gradients), under every schedule: the library's side stream on/off and
+    the gate backward on its own stream or not, on torch's default stream
+    (raw handle 0) and on a created stream.  The last step's outputs must
+    equal one serial step on the same inputs, bit for bit: a missing wait
+    between streams shows up as a stale read or a raced read-modify-write of
+    dx."""
+    cfg = CONFIGS["moe_s_like"]
+    banner("back-to-back steps", stream_kind)
+    t = device.gen_all(cfg)
+    xB = (-t["x"]).contiguous()
+    dyB = (t["dy"] * -0.5).contiguous()
+    names = ("logits", "topk_idx", "y", "out_perm", "d_out_perm", "d_topk_w",
+             "dx_perm", "dx", "dWg", "dW1", "dW2")
+
+    def make(og):
+        return M.MoELayer(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.act,
+                          device.torch_dtype(cfg), cfg.renorm, overlap_gate=og)
+
+    def bind(layer, x, dy):
+        layer.bind(x, t["Wg"], t["W1"], t["W2"], t["W3"], t["bias"], dy)
+
+    other = torch.cuda.Stream()
+    handle = 0 if stream_kind == "default" else other.cuda_stream
+    try:
+        M.moe_set_overlap(False)
+        ref = make(False)
+        bind(ref, xB, dyB)
+        ref.step()
+        torch.cuda.synchronize()
+        want = {n: getattr(ref, n).clone() for n in names}
+        del ref
+        torch.cuda.synchronize()
+        for lib_overlap in (True, False):
+            M.moe_set_overlap(lib_overlap)
+            for og in (False, True):
+                layer = make(og)
+                for i in range(8):
+                    if i % 2:
+                        bind(layer, xB, dyB)
+                    else:
+                        bind(layer, t["x"], t["dy"])
+                    layer.step(handle)
+                torch.cuda.synchronize()
+                bad = [n for n in names if not torch.equal(getattr(layer, n), want[n])]
+                assert not bad, (lib_overlap, og, bad)
+                del layer
+    finally:
+        M.moe_set_overlap(True)

@@ -240,3 +240,11 @@ def test_gate_topk_bwd(case, dt):
     else:
         assert np.all(host(dWg) == 0)
     assert_close(g_dx, dx0 + rdx, dt, "dx += dl Wg^T")
+    # overwrite mode: the old dx is not read (NaN garbage stays out)
+    g_dx.fill_(float("nan"))
+    dWg2 = M.moe_gate_topk_bwd(dev(x, dt), dev(Wg, dt), dev(l), dev_i32(idx), dev(w),
+                               dev(dw), g_dx, renorm, accumulate=False)
+    torch.cuda.synchronize()
+    assert torch.equal(dWg2, dWg)
+    assert bool(torch.isfinite(g_dx).all())
+    assert_close(g_dx, rdx, dt, "dx = dl Wg^T")
