@@ -310,10 +310,17 @@ def main():
 
     # ---- per-kernel pass: HIP events around every launch, same K steps
     L = _lib.load()
+    # every kernel alone: the library keeps its side stream off while events
+    # are on, and the layer's gate backward stays on the step's stream
+    og = getattr(layer, "overlap_gate", None)
+    if og is not None:
+        layer.overlap_gate = False
     _lib.check(L.moe_profile_enable(args.steps * 40), "moe_profile_enable")
     for _ in range(args.steps):
         layer.step(s)
     torch.cuda.synchronize()
+    if og is not None:
+        layer.overlap_gate = og
     recs = _lib.profile_records()
     L.moe_profile_disable()
     per = {}

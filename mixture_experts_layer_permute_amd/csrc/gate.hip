@@ -253,52 +253,57 @@ __global__ __launch_bounds__(256) void topk_kernel(
         topk_w[t * k + j] = expf(sv[j] - best0) * inv;
 }
 
-// ---------------------------------------------------------- backward
-// dl[t,:]: one wave per token (4 tokens per block).  slot[e] maps an expert
-// to its slot in the token's top-k, or -1.
-__global__ __launch_bounds__(256) void gate_dlogits_kernel(
-    const float* __restrict__ logits, const int32_t* __restrict__ topk_idx,
-    const float* __restrict__ topk_w, const float* __restrict__ dw, int Tn,
-    int E, int k, int renorm, float* __restrict__ dl) {
-    extern __shared__ int slot_mem[];         // [4][E]
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const long t = (long)blockIdx.x * 4 + wv;
-    const bool active = t < Tn;
-    int* slot = slot_mem + wv * E;
-    for (int e = lane; e < E; e += 64) slot[e] = -1;
-    __syncthreads();
+// s = sum_j w_j dw_j of one token, in slot order.  The gate's dl and the
+// dx kernel both take their coefficients w_j (dw_j - s) from this sum.
+__device__ __forceinline__ float coef_sum(const float* __restrict__ w,
+                                          const float* __restrict__ dw, int k) {
     float s = 0.0f;
-    if (active) {
-        for (int j = lane; j < k; j += 64) {
-            const int e = topk_idx[t * k + j];
-            if (e >= 0 && e < E) slot[e] = j;
-            s += topk_w[t * k + j] * dw[t * k + j];
-        }
+    for (int j = 0; j < k; ++j) s = fmaf(w[j], dw[j], s);
+    return s;
+}
+
+// dl[t,:] (the logits' gradient), one token per thread:
+//   renorm=1: dl[t,idx_j] = w_j (dw_j - s), 0 elsewhere;
+//   renorm=0: dl[t,e] = p_e (g_e - s), p = softmax(logits[t,:]), g_e = dw_j
+//             where e = idx_j else 0.
+// Blocks past the tokens' write WgT[e][i] = Wg[i][e] (a gate column
+// contiguous, in the gate's own type, for the dx kernel).
+template <typename T>
+__global__ __launch_bounds__(256) void gate_prep_kernel(
+    const float* __restrict__ logits, const int32_t* __restrict__ topk_idx,
+    const float* __restrict__ topk_w, const float* __restrict__ dw, int Tn, int E,
+    int k, int renorm, float* __restrict__ dl, const T* __restrict__ Wg, int d,
+    T* __restrict__ WgT, int tblocks) {
+    if ((int)blockIdx.x >= tblocks) {
+        const long q = (long)(blockIdx.x - tblocks) * 256 + threadIdx.x;
+        if (q < (long)d * E) WgT[(q % E) * d + q / E] = Wg[q];
+        return;
     }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
-    __syncthreads();
-    if (!active) return;
+    const long t = (long)blockIdx.x * 256 + threadIdx.x;
+    if (t >= Tn) return;
+    const int32_t* it = topk_idx + t * k;
+    const float* wt = topk_w + t * k;
+    const float* dwt = dw + t * k;
+    const float s = coef_sum(wt, dwt, k);
+    float* out = dl + t * E;
     if (renorm) {
-        for (int e = lane; e < E; e += 64) {
-            const int j = slot[e];
-            dl[t * E + e] = j >= 0 ? topk_w[t * k + j] * (dw[t * k + j] - s) : 0.0f;
+        for (int e = 0; e < E; ++e) out[e] = 0.0f;
+        for (int j = 0; j < k; ++j) {
+            const int e = it[j];
+            if (e >= 0 && e < E) out[e] = wt[j] * (dwt[j] - s);
         }
         return;
     }
+    const float* lt = logits + t * E;
     float m = -FLT_MAX;
-    for (int e = lane; e < E; e += 64) m = fmaxf(m, logits[t * E + e]);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    for (int e = 0; e < E; ++e) m = fmaxf(m, lt[e]);
     float z = 0.0f;
-    for (int e = lane; e < E; e += 64) z += expf(logits[t * E + e] - m);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off);
+    for (int e = 0; e < E; ++e) z += expf(lt[e] - m);
     const float inv = 1.0f / z;
-    for (int e = lane; e < E; e += 64) {
-        const int j = slot[e];
-        const float g = j >= 0 ? dw[t * k + j] : 0.0f;
-        dl[t * E + e] = expf(logits[t * E + e] - m) * inv * (g - s);
+    for (int e = 0; e < E; ++e) out[e] = expf(lt[e] - m) * inv * (0.0f - s);
+    for (int j = 0; j < k; ++j) {
+        const int e = it[j];
+        if (e >= 0 && e < E) out[e] = expf(lt[e] - m) * inv * (dwt[j] - s);
     }
 }
 
@@ -419,77 +424,59 @@ __global__ __launch_bounds__(256) void gate_dwg_reduce_kernel(const float* __res
     for (int v = 0; v < 4; ++v) Elem<T>::st(dWg + q + v, tot[v]);
 }
 
-// WgT[e][i] = Wg[i][e] in fp32, so a gate column is contiguous.
-template <typename T>
-__global__ void gate_transpose_kernel(const T* __restrict__ Wg, int d, int E,
-                                      float* __restrict__ WgT) {
-    const long q = (long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (q >= (long)d * E) return;
-    const int i = (int)(q / E), e = (int)(q % E);
-    WgT[(long)e * d + i] = Elem<T>::ld(Wg + q);
-}
-
-// dx[t,:] (+)= sum_e dl[t,e] WgT[e,:].  renorm=1 uses the k nonzero entries
-// only (coefficients recomputed from w and dw); renorm=0 reads dl.  Without
-// accumulate the old dx is not read: the sum is added to +0, which gives the
-// bits that adding it to a zeroed dx gives.
-// One block of 256 threads per token, 16 bytes of dx per thread step.
+// dx[t,:] (+)= sum_e dl[t,e] WgT[e,:], one thread per V consecutive features
+// of a token.  renorm=1 takes the k nonzero entries (coefficients
+// w_j (dw_j - s) recomputed from w and dw, as gate_prep does); renorm=0 reads
+// dl.  Without accumulate the old dx is not read: the sum is added to +0,
+// which gives the bits that adding it to a zeroed dx gives.
 template <typename T>
 __global__ __launch_bounds__(256) void gate_dx_kernel(
-    const float* __restrict__ WgT, const float* __restrict__ dl,
+    const T* __restrict__ WgT, const float* __restrict__ dl,
     const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_w,
-    const float* __restrict__ dw, int d, int E, int k, int renorm, int accumulate,
+    const float* __restrict__ dw, int Tn, int d, int E, int k, int renorm, int accumulate,
     T* __restrict__ dx) {
-    extern __shared__ float coef_mem[];       // [E] coefficients (renorm=0) or [2k]
-    const long t = blockIdx.x;
-    const int tid = threadIdx.x;
-    int n;
-    if (renorm) {
-        // s = sum_j w_j dw_j, computed by one wave in a fixed tree order
-        float* c = coef_mem;
-        int* ci = reinterpret_cast<int*>(coef_mem + k);
-        if (tid < 64) {
-            float s = 0.0f;
-            for (int j = tid; j < k; j += 64) s += topk_w[t * k + j] * dw[t * k + j];
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
-            for (int j = tid; j < k; j += 64) {
-                const int e = topk_idx[t * k + j];
-                const bool ok = e >= 0 && e < E;
-                c[j] = ok ? topk_w[t * k + j] * (dw[t * k + j] - s) : 0.0f;
-                ci[j] = ok ? e : 0;
-            }
-        }
-        n = k;
-    } else {
-        for (int e = tid; e < E; e += 256) coef_mem[e] = dl[t * E + e];
-        n = E;
-    }
-    __syncthreads();
     constexpr int V = Vec16<T>::N;
-    const int* ci = reinterpret_cast<const int*>(coef_mem + k);
-    for (int i0 = tid * V; i0 < d; i0 += 256 * V) {
-        float acc[V];
+    const int nq = d / V;
+    const long q = (long)blockIdx.x * 256 + threadIdx.x;
+    if (q >= (long)Tn * nq) return;
+    const long t = q / nq;
+    const int i0 = (int)(q - t * nq) * V;
+    float acc[V];
 #pragma unroll
-        for (int q = 0; q < V; ++q) acc[q] = 0.0f;
-        for (int j = 0; j < n; ++j) {
-            const int e = renorm ? ci[j] : j;
-            const float cf = coef_mem[j];
-            const float* w = WgT + (long)e * d + i0;
+    for (int u = 0; u < V; ++u) acc[u] = 0.0f;
+    if (renorm) {
+        const int32_t* it = topk_idx + t * k;
+        const float* wt = topk_w + t * k;
+        const float* dwt = dw + t * k;
+        const float s = coef_sum(wt, dwt, k);
+        for (int j = 0; j < k; ++j) {
+            const int e = it[j];
+            if (e < 0 || e >= E) continue;
+            const float cf = wt[j] * (dwt[j] - s);
+            float wg[V];
+            Vec16<T>::ld(WgT + (long)e * d + i0, wg);
 #pragma unroll
-            for (int q = 0; q < V; ++q) acc[q] = fmaf(cf, w[q], acc[q]);
+            for (int u = 0; u < V; ++u) acc[u] = fmaf(cf, wg[u], acc[u]);
         }
-        float cur[V];
-        if (accumulate) {
-            Vec16<T>::ld(dx + t * d + i0, cur);
-        } else {
+    } else {
+        for (int e = 0; e < E; ++e) {
+            const float cf = dl[t * E + e];
+            float wg[V];
+            Vec16<T>::ld(WgT + (long)e * d + i0, wg);
 #pragma unroll
-            for (int q = 0; q < V; ++q) cur[q] = 0.0f;
+            for (int u = 0; u < V; ++u) acc[u] = fmaf(cf, wg[u], acc[u]);
         }
-#pragma unroll
-        for (int q = 0; q < V; ++q) cur[q] = cur[q] + acc[q];
-        Vec16<T>::st(dx + t * d + i0, cur);
     }
+    float cur[V];
+    if (accumulate) {
+        Vec16<T>::ld(dx + t * d + i0, cur);
+    } else {
+#pragma unroll
+        for (int u = 0; u < V; ++u) cur[u] = 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < V; ++u) cur[u] = cur[u] + acc[u];
+    Vec16<T>::st(dx + t * d + i0, cur);
 }
 
 // Chunks in flight per thread: when the grid is at most a couple of blocks
@@ -593,35 +580,32 @@ moe_status launch_gate_bwd(const void* x, const void* Wg, const float* logits,
     const GateBwdWs L = gate_bwd_layout(Tn, d, E);
     char* base = static_cast<char*>(ws);
     float* dl = reinterpret_cast<float*>(base + L.dl);
-    float* wgt = reinterpret_cast<float*>(base + L.wgt);
+    T* wgt = reinterpret_cast<T*>(base + L.wgt);
     float* partial = reinterpret_cast<float*>(base + L.partial);
     const T* xp = static_cast<const T*>(x);
 
-    MOE_LAUNCH("gate_transpose", s,
-        gate_transpose_kernel<T><<<cdiv((long)d * E, 256), 256, 0, s>>>(
-            static_cast<const T*>(Wg), d, E, wgt));
-    if (Tn > 0)
-        MOE_LAUNCH("gate_dlogits", s,
-            gate_dlogits_kernel<<<cdiv(Tn, 4), 256, sizeof(int) * 4 * (size_t)E, s>>>(
-                logits, idx, w, dw, Tn, E, k, renorm, dl));
-    // dWg = x^T dl (side stream) and dx += dl Wg^T (caller's stream) only
+    const int tblocks = cdiv(Tn, 256);
+    MOE_LAUNCH("gate_prep", s,
+        gate_prep_kernel<T><<<tblocks + cdiv((long)d * E, 256), 256, 0, s>>>(
+            logits, idx, w, dw, Tn, E, k, renorm, dl, static_cast<const T*>(Wg), d, wgt,
+            tblocks));
+    // dWg = x^T dl (side stream) and dx (+)= dl Wg^T (caller's stream) only
     // share dl: they run side by side and join before the call returns
     SideStream side(s);
     hipStream_t ss = side.ok() ? side.get() : s;
     const DwgSplit z = dwg_split(Tn, d, E);
-    dim3 g(cdiv(z.nft, 4), z.net, z.nchunk);
+    const dim3 g(cdiv(z.nft, 4), z.net, z.nchunk);
     MOE_LAUNCH("gate_dwg_partial", ss,
         gate_dwg_partial_kernel<T><<<g, 256, 0, ss>>>(xp, dl, Tn, d, E, z.tc, z.nft, partial));
     const long n = (long)d * E;
     MOE_LAUNCH("gate_dwg_reduce", ss,
         gate_dwg_reduce_kernel<T><<<cdiv(n / 4, 256 / DW_RG), 256, 0, ss>>>(
             partial, z.nchunk, n, static_cast<T*>(dWg)));
-    const size_t lds_dx = renorm ? sizeof(float) * 2 * (size_t)k : sizeof(float) * (size_t)E;
     if (Tn > 0)     // no tokens: dWg is zero (one empty chunk), dx is empty
         MOE_LAUNCH("gate_dx", s,
-            gate_dx_kernel<T><<<Tn, 256, lds_dx + 16, s>>>(wgt, dl, idx, w, dw, d, E, k,
-                                                            renorm, accumulate ? 1 : 0,
-                                                            static_cast<T*>(dx)));
+            gate_dx_kernel<T><<<cdiv((long)Tn * (d / Vec16<T>::N), 256), 256, 0, s>>>(
+                wgt, dl, idx, w, dw, Tn, d, E, k, renorm, accumulate ? 1 : 0,
+                static_cast<T*>(dx)));
     if (side.ok() && !side.join()) return MOE_ERR_HIP;
     return launch_status();
 }
