@@ -34,13 +34,13 @@ PEAK_HBM_GBS = 8000.0
 # 4.0 and 2.0); see
 # profiles/hbm_traffic_moe_s_like.md.  Valid only for the kernel sources
 # whose SHA-256 prefix is TRAFFIC_SRC; null once they change.
-TRAFFIC_SRC = "2989eeaaa3d5de73"
+TRAFFIC_SRC = "74945bda7a0eec81"
 TRAFFIC_SOURCES = ("ggemm.hip", "common.h", "permute.hip", "combine.hip")
-TRAFFIC = {"gemm_up_gelu": 1185267090, "gemm_down": 772604303,
-           "gemm_dA_gelu": 1183873650, "gemm_dW1": 1141077995,
-           "gemm_dW2": 1141077995, "gemm_dX": 772232163, "perm_copy": 101268262,
-           "combine": 101778949, "combine_bwd": 169114443,
-           "unpermute_grad": 134813990}
+TRAFFIC = {"gemm_up_gelu": 1185102368, "gemm_down": 773724896,
+           "gemm_dA_gelu": 1184232570, "gemm_dW1": 1141070112,
+           "gemm_dW2": 1141070112, "gemm_dX": 772226982, "perm_copy": 101239164,
+           "combine": 101777255, "combine_bwd": 169112921,
+           "unpermute_grad": 134812792}
 
 
 def traffic_for(kernel, workload):
@@ -85,8 +85,9 @@ def parse():
                     help="workload name (moe_inputs.configs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--serial", action="store_true",
-                    help="run every kernel on one stream (moe_set_overlap(0)) in the "
-                         "headline too; the per-kernel pass is always serial")
+                    help="run every kernel on one stream (moe_set_overlap(0), the gate "
+                         "backward on the step's stream) in the headline too; the "
+                         "per-kernel pass is always serial")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU work for the oracle baseline")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
@@ -227,7 +228,8 @@ def main():
                                   chunk_tokens=args.chunk_tokens)
     else:
         layer = M.MoELayer(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.act,
-                           device.torch_dtype(cfg), cfg.renorm, fuse_gather=args.fuse_gather)
+                           device.torch_dtype(cfg), cfg.renorm, fuse_gather=args.fuse_gather,
+                           overlap_gate=not args.serial)
     layer.bind(t["x"], t["Wg"], t["W1"], t["W2"], t["W3"], t["bias"], t["dy"])
     stream = torch.cuda.current_stream()
     s = stream.cuda_stream
@@ -458,7 +460,8 @@ def main():
         del layer
         torch.cuda.empty_cache()
         fl = M.MoELayer(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.act,
-                        device.torch_dtype(cfg), cfg.renorm, fuse_gather=True)
+                        device.torch_dtype(cfg), cfg.renorm, fuse_gather=True,
+                        overlap_gate=not args.serial)
         fl.bind(t["x"], t["Wg"], t["W1"], t["W2"], t["W3"], t["bias"], t["dy"])
         for _ in range(args.warmup):
             fl.step(s)
