@@ -155,6 +155,16 @@ def parity(cfg, layer, fw, gr):
     return out
 
 
+ORACLE_HOST_GIB = 64
+
+
+def oracle_host_bytes(cfg):
+    """Rough host footprint of one full-layer oracle pass: the expert
+    weights in fp32 and about ten [R, f] / [R, d] arrays in fp64."""
+    nw = 3 if cfg.swiglu else 2
+    return 4 * cfg.E * cfg.d * cfg.f * nw + 8 * 10 * cfg.R * max(cfg.f, cfg.d)
+
+
 def cpu_baseline(cfg, budget_s):
     """The oracle, as it stands, on the host cores: full layer fwd+bwd."""
     import numpy as np
@@ -317,13 +327,19 @@ def main():
     og = getattr(layer, "overlap_gate", None)
     if og is not None:
         layer.overlap_gate = False
-    _lib.check(L.moe_profile_enable(args.steps * 40), "moe_profile_enable")
+    # room for every launch of the step (a chunked step launches per chunk);
+    # the library drops records past its capacity, so a full buffer is an error
+    per_step = 64 * (getattr(layer, "nch", 0) + 1)
+    cap = args.steps * per_step
+    _lib.check(L.moe_profile_enable(cap), "moe_profile_enable")
     for _ in range(args.steps):
         layer.step(s)
     torch.cuda.synchronize()
     if og is not None:
         layer.overlap_gate = og
     recs = _lib.profile_records()
+    if len(recs) >= cap:
+        raise RuntimeError("per-kernel pass: %d launch records filled the buffer" % len(recs))
     L.moe_profile_disable()
     per = {}
     for name, kms in recs:
@@ -337,13 +353,16 @@ def main():
         junk = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
         calls = layer.stage_calls()
         nsteps = max(1, min(args.steps, 10))
-        _lib.check(L.moe_profile_enable(nsteps * 40), "moe_profile_enable")
+        _lib.check(L.moe_profile_enable(nsteps * per_step), "moe_profile_enable")
         for _ in range(nsteps):
             for _, call in calls:
                 junk.sum()
                 call()
         torch.cuda.synchronize()
-        for name, kms in _lib.profile_records():
+        frecs = _lib.profile_records()
+        if len(frecs) >= nsteps * per_step:
+            raise RuntimeError("flushed pass: launch records filled the buffer")
+        for name, kms in frecs:
             flushed.setdefault(name, []).append(kms)
         L.moe_profile_disable()
         del junk
@@ -448,7 +467,14 @@ def main():
         "kernels": kernels,
         "load": load_stats(layer.counts, cfg),
     }
-    if not args.no_cpu_baseline:
+    host_gb = oracle_host_bytes(cfg) / 2 ** 30
+    if not args.no_cpu_baseline and host_gb > ORACLE_HOST_GIB:
+        out["cpu_baseline"] = {
+            "skipped": "the full-layer oracle needs about %.0f GiB of host memory here "
+                       "(fp32 weights, fp64 activations), over the %d GiB this run allows; "
+                       "parity of this workload is the GPU test of routing in full and "
+                       "four seeded experts" % (host_gb, ORACLE_HOST_GIB)}
+    elif not args.no_cpu_baseline:
         base, fw, gr = cpu_baseline(cfg, args.cpu_seconds)
         base["parity"] = parity(cfg, layer, fw, gr)
         out["cpu_baseline"] = base
