@@ -45,8 +45,9 @@ SideState g_side[kMaxDevices];
 
 std::atomic<int> g_overlap{1};
 
-SideStream::SideStream(hipStream_t main) : main_(main) {
-    if (!g_overlap.load(std::memory_order_relaxed) || g_prof_on) return;   // caller's stream only
+SideStream::SideStream(hipStream_t main, bool allow) : main_(main) {
+    if (!allow || !g_overlap.load(std::memory_order_relaxed) || g_prof_on)
+        return;                                                // caller's stream only
     int d = -1;
     if (hipGetDevice(&d) != hipSuccess || d < 0 || d >= kMaxDevices) return;
     SideState& st = g_side[d];

@@ -106,7 +106,9 @@ inline int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 // the whole call stays ordered on the caller's stream.
 class SideStream {
    public:
-    explicit SideStream(hipStream_t main);
+    // allow = false: the call stays on the caller's stream (as with
+    // moe_set_overlap(0)); the callers decide this from the product's shape
+    explicit SideStream(hipStream_t main, bool allow = true);
     ~SideStream();
     bool ok() const { return ok_; }
     hipStream_t get() const { return side_; }

@@ -1318,6 +1318,15 @@ struct Launch<float, Cfg> {
     static constexpr int BM = FB;
 };
 
+// Whether an FFN call runs its partial-tile launches and dW2 on the side
+// stream beside the main launches.  With per-expert weights up to 8 Mi
+// elements (16 MB in bf16; the MoE-S-like and 64-expert shapes) the side
+// work fills the last, partly idle rounds: 1-2% faster steps.  With larger
+// ones (d 2048 x f 8192, d 4096 x f 14336) two products in flight at once
+// lost more to each other than they gained: the skewed and long-context
+// steps were 3% and 1% faster with everything on the caller's stream.
+inline bool side_stream_pays(int d, int f) { return (long)d * f <= (8L << 20); }
+
 template <typename T, class Cfg = DefaultCfg>
 moe_status ffn_fwd(const void* x_perm, const int32_t* offsets, int R, int E,
                    int d, int f, moe_act act, const void* W1, const void* W3,
@@ -1359,7 +1368,7 @@ moe_status ffn_fwd(const void* x_perm, const int32_t* offsets, int R, int E,
     // and of their partial last tiles (tail launches, side stream) are
     // independent through both GEMMs; where only one of the two products is
     // split, the stream of the partial rows' consumer waits for their producer.
-    SideStream side(s);
+    SideStream side(s, side_stream_pays(d, f));
     hipStream_t ts = side.ok() ? side.get() : s;
     bool up_split = false;
     if (act == MOE_ACT_GELU)
@@ -1413,7 +1422,7 @@ moe_status ffn_bwd(const void* d_out, const void* x_perm, const void* h_save,
     // dW2 depends on neither dA nor dX; dW1/dW3 need every row of dH.  A
     // product that is not split runs whole on the caller's stream, and the
     // stream that consumes its rows waits for it.
-    SideStream side(s);
+    SideStream side(s, side_stream_pays(d, f));
     hipStream_t ts = side.ok() ? side.get() : s;
     bool dA_split = false;
     // dA = dO W2[e]^T with the activation derivative in the epilogue -> dH
