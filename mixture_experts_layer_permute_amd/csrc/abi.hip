@@ -194,7 +194,7 @@ const char* moe_status_string(moe_status s) {
     return "unknown status";
 }
 
-int moe_abi_version(void) { return 4; }
+int moe_abi_version(void) { return 5; }
 
 moe_status moe_set_overlap(int enable) {
     moe::g_overlap.store(enable != 0 ? 1 : 0, std::memory_order_relaxed);

@@ -50,7 +50,7 @@ def test_binding_names_match_c_names():
 
 
 def test_status_strings_and_version(lib):
-    assert lib.moe_abi_version() == 4
+    assert lib.moe_abi_version() == 5
     for s in (0, -1, -2, -3, -4):
         assert lib.moe_status_string(s)
 
@@ -122,3 +122,44 @@ def test_no_gpu_means_error_not_fallback(lib):
         pytest.skip("GPU present")
     # valid arguments reach the device check, which fails without a GPU
     assert lib.moe_init(0) in (_lib.MOE_ERR_HIP, _lib.MOE_ERR_UNSUPPORTED)
+
+
+def _ctype_of(decl):
+    """ctypes kind of one C parameter or return type in include/moe.h."""
+    decl = decl.strip()
+    if "*" in decl or decl.startswith("hipStream_t"):
+        return "char_p" if decl.startswith("const char") and decl.count("*") == 1 and \
+            not re.search(r"\w\s*$", decl.replace("*", "")) else "ptr"
+    t = decl.split()[0] if decl.split()[0] != "const" else decl.split()[1]
+    return {"int": "int", "moe_status": "int", "moe_dtype": "int", "moe_act": "int",
+            "int32_t": "int", "size_t": "size", "void": "void"}[t]
+
+
+def header_signatures():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    out = {}
+    for m in re.finditer(r"([A-Za-z_][\w\s\*]*?)\b(moe_[a-z0-9_]+)\s*\(([^)]*)\)\s*;", text):
+        ret, name, args = m.group(1), m.group(2), m.group(3).strip()
+        params = [] if args in ("", "void") else [a for a in args.split(",")]
+        # a parameter is "type name": drop the name
+        kinds = [_ctype_of(re.sub(r"\b\w+\s*$", "", p)) for p in params]
+        rk = "char_p" if re.search(r"const\s+char\s*\*", ret) else _ctype_of(ret.split()[-1])
+        out[name] = (rk, kinds)
+    return out
+
+
+def test_binding_types_match_the_header():
+    """Every argument list in the ctypes table has the header's length and
+    kinds (pointer / int / size_t), so a changed C signature cannot be
+    called with stale marshalling."""
+    kind = {ctypes.c_void_p: "ptr", ctypes.c_int: "int", ctypes.c_size_t: "size",
+            ctypes.c_char_p: "char_p", None: "void"}
+    decl = header_signatures()
+    assert len(decl) >= 20
+    for name, (rk, kinds) in decl.items():
+        assert name in _lib.SIGNATURES, name
+        res, args = _lib.SIGNATURES[name]
+        got = [kind.get(a, "ptr") for a in args]     # POINTER(...) is a pointer
+        assert got == kinds, (name, got, kinds)
+        assert kind.get(res) == rk, (name, res, rk)
