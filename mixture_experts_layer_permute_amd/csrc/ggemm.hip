@@ -1318,8 +1318,9 @@ struct Launch<float, Cfg> {
     static constexpr int BM = FB;
 };
 
-// Whether an FFN call runs its partial-tile launches and dW2 on the side
-// stream beside the main launches.  With per-expert weights up to 8 Mi
+// Whether the FFN backward runs its partial-tile launches and dW2 on the side
+// stream beside the main launches (the forward keeps everything on the
+// caller's stream).  With per-expert weights up to 8 Mi
 // elements (16 MB in bf16; the MoE-S-like and 64-expert shapes) the side
 // work fills the last, partly idle rounds: 1-2% faster steps.  With larger
 // ones (d 2048 x f 8192, d 4096 x f 14336) two products in flight at once
@@ -1364,31 +1365,19 @@ moe_status ffn_fwd(const void* x_perm, const int32_t* offsets, int R, int E,
         Launch<T, Cfg>::template go<RAGGED_M, KMAJ, MNMAJ, true, false, true>(
             p, EpiSwigluFwd<T>{H, A, f}, R, s, "gemm_up_swiglu");
     }
-    // The rows of the experts' full tiles (main launches, caller's stream)
-    // and of their partial last tiles (tail launches, side stream) are
-    // independent through both GEMMs; where only one of the two products is
-    // split, the stream of the partial rows' consumer waits for their producer.
-    SideStream side(s, side_stream_pays(d, f));
-    hipStream_t ts = side.ok() ? side.get() : s;
-    bool up_split = false;
+    // The experts' full tiles (main launches) and their partial last tiles
+    // (tail launches) run one after the other on the caller's stream.  On
+    // the side stream the tails only stretched the up GEMM's main launch
+    // (kernel trace of the MoE-S-like step: 177 -> 277 us), and the steps were
+    // 0.2-0.6% slower than with the forward on one stream.
     if (act == MOE_ACT_GELU)
-        up_split = Launch<T, Cfg>::template go<RAGGED_M, KMAJ, MNMAJ, false, false, true>(
-            p, EpiGeluFwd<T>{H, A, f}, R, s, "gemm_up_gelu", "gemm_up_gelu_tail", ts);
-    if (!out_perm) {                   // GEMM1 only (recomputation of the saved state)
-        if (side.ok() && !side.join()) return MOE_ERR_HIP;
+        Launch<T, Cfg>::template go<RAGGED_M, KMAJ, MNMAJ, false, false, true>(
+            p, EpiGeluFwd<T>{H, A, f}, R, s, "gemm_up_gelu", "gemm_up_gelu_tail", s);
+    if (!out_perm)                     // GEMM1 only (recomputation of the saved state)
         return launch_status();
-    }
-    const bool down_split = Launch<T, Cfg>::template splits<RAGGED_M, false>(R, E, d);
-    if (side.ok() && up_split != down_split) {
-        // up split, down whole: down (caller's stream) needs up's partial rows;
-        // up whole, down split: down's tail (side stream) needs rows made on s
-        const bool ok = up_split ? side.mark(1) && side.wait(1) : side.follow();
-        if (!ok) return MOE_ERR_HIP;
-    }
     Launch<T, Cfg>::template go<RAGGED_M, KMAJ, MNMAJ, false, false>(
         q, EpiStore<T>{static_cast<T*>(out_perm), d, 0}, R, s, "gemm_down", "gemm_down_tail",
-        ts);
-    if (side.ok() && !side.join()) return MOE_ERR_HIP;
+        s);
     return launch_status();
 }
 
