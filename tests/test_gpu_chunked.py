@@ -168,3 +168,27 @@ def test_accumulate_entry_point_and_gemm1_only(act, dt):
         "moe_expert_ffn_bwd_accumulate R=0")
     torch.cuda.synchronize()
     assert torch.equal(before, dW1)
+
+
+def test_chunked_back_to_back_steps():
+    """Six steps issued with no host synchronisation, re-bound each time to
+    one of two input sets (x and dy negated/halved: other routing, other
+    gradients): the last step equals one step of a fresh layer on the same
+    inputs, bit for bit (dW accumulation across chunks restarts every step,
+    and a re-bind drops the resident chunk)."""
+    cfg = small_variant("moe_s_like", T=1000, d=256, f=512, E=8, k=2)
+    banner("chunked back-to-back", cfg.short())
+    t = device.gen_all(cfg)
+    tb = dict(t)
+    tb["x"] = (-t["x"]).contiguous()
+    tb["dy"] = (t["dy"] * -0.5).contiguous()
+    args = (cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.act, device.torch_dtype(cfg), cfg.renorm)
+    ref = run(M.ChunkedMoELayer(*args, chunk_tokens=256), tb)
+    ch = M.ChunkedMoELayer(*args, chunk_tokens=256)
+    for i in range(6):
+        u = tb if i % 2 else t
+        ch.bind(u["x"], u["Wg"], u["W1"], u["W2"], u["W3"], u["bias"], u["dy"])
+        ch.step()
+    torch.cuda.synchronize()
+    for n in SAME + ["dW1", "dW2"]:
+        assert torch.equal(getattr(ch, n), getattr(ref, n)), n

@@ -215,7 +215,7 @@ def test_unpermute_grad(case, dt):
 
 GB_CASES = [(1000, 128, 16, 2, 1), (3000, 64, 8, 2, 1), (517, 128, 64, 8, 1),
             (300, 64, 4, 1, 1), (200, 128, 32, 4, 0), (1, 64, 4, 2, 0),
-            (2500, 256, 128, 8, 0)]
+            (2500, 256, 128, 8, 0), (97, 64, 1024, 4, 1), (61, 64, 1024, 3, 0)]
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
