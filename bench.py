@@ -34,13 +34,13 @@ PEAK_HBM_GBS = 8000.0
 # 4.0 and 2.0); see
 # profiles/hbm_traffic_moe_s_like.md.  Valid only for the kernel sources
 # whose SHA-256 prefix is TRAFFIC_SRC; null once they change.
-TRAFFIC_SRC = "74945bda7a0eec81"
+TRAFFIC_SRC = "2741dcd9cbc3b572"
 TRAFFIC_SOURCES = ("ggemm.hip", "common.h", "permute.hip", "combine.hip")
-TRAFFIC = {"gemm_up_gelu": 1185102368, "gemm_down": 773724896,
-           "gemm_dA_gelu": 1184232570, "gemm_dW1": 1141070112,
-           "gemm_dW2": 1141070112, "gemm_dX": 772226982, "perm_copy": 101239164,
-           "combine": 101777255, "combine_bwd": 169112921,
-           "unpermute_grad": 134812792}
+TRAFFIC = {"gemm_up_gelu": 1183561795, "gemm_down": 772682879,
+           "gemm_dA_gelu": 1183705354, "gemm_dW1": 1141068001,
+           "gemm_dW2": 1141068001, "gemm_dX": 772225240, "perm_copy": 101238743,
+           "combine": 101776378, "combine_bwd": 169111577,
+           "unpermute_grad": 134812261}
 
 
 def traffic_for(kernel, workload):
