@@ -76,15 +76,17 @@ int moe_abi_version(void);
 moe_status moe_init(int device);
 
 /*
- * moe_set_overlap -- whether the expert FFN and gate backward calls may run
- * launches that do not depend on each other (the experts' partial last
- * tiles, dW2, dWg) on a library-owned side stream of the current device,
- * concurrently with the rest of the call on `stream` (enable != 0, the
- * default), or run every kernel in order on `stream` (enable = 0).  Either way a call is ordered on
- * `stream` as a whole (the side stream forks from it and joins back through
- * events) and the results are bit-identical.  Process-wide setting.
- * While kernel timing is enabled (moe_profile_enable) the library runs as
- * with enable = 0 so that every timed kernel runs alone.
+ * moe_set_overlap -- whether moe_expert_ffn_bwd (and its _accumulate and
+ * _gather forms) may run launches that do not depend on each other (the
+ * experts' partial last tiles, dW2) on a library-owned side stream of the
+ * current device, concurrently with the rest of the call on `stream`
+ * (enable != 0, the default; used only when an expert's weight has at most
+ * 8 Mi elements, where it pays), or run every kernel in order on `stream`
+ * (enable = 0).  Either way a call is ordered on `stream` as a whole (the
+ * side stream forks from it and joins back through events) and the results
+ * are bit-identical.  Every other call runs in order on `stream`.
+ * Process-wide setting.  While kernel timing is enabled (moe_profile_enable)
+ * the library runs as with enable = 0 so that every timed kernel runs alone.
  */
 moe_status moe_set_overlap(int enable);
 

@@ -52,7 +52,7 @@ def moe_init(device=0):
 
 
 def moe_set_overlap(enable=True):
-    """Let the FFN calls run independent launches on a side stream (default)."""
+    """Let the FFN backward run independent launches on a side stream (default)."""
     check(load().moe_set_overlap(1 if enable else 0), "moe_set_overlap")
 
 
