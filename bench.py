@@ -215,8 +215,8 @@ def load_stats(counts, cfg):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(sharding is described in DESIGN.md); run with --gpus 1",
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(no collectives, no sharding); run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
     import torch
