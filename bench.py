@@ -105,6 +105,11 @@ def parse():
     ap.add_argument("--no-fused-pass", action="store_true",
                     help="skip the fused_gather timing (profiler runs: one kernel "
                          "variant per name)")
+    ap.add_argument("--offload-experts", type=int, default=0,
+                    help="after the headline, time the step with the expert weights "
+                         "in pinned host memory, uploaded this many experts at a time "
+                         "beside the GEMMs (OffloadedMoELayer); reported as "
+                         "'offloaded', never as the value (it includes PCIe)")
     ap.add_argument("--flush-mall", action="store_true",
                     help="add a per-kernel pass that reads a 512 MiB buffer before "
                          "every entry point, so memory kernels read from HBM")
@@ -503,7 +508,65 @@ def main():
                                "y_bit_identical": bool(torch.equal(y0, fl.y)),
                                "x_perm_bytes_not_allocated": cfg.T * cfg.k * cfg.d
                                * (2 if cfg.dtype == "bf16" else 4)}
+        del fl
+        layer = None
+    if args.offload_experts and not args.chunk_tokens:
+        if layer is not None:             # the headline layer's buffers out of HBM
+            y0 = layer.y.clone()
+            del layer
+        out["offloaded"] = offloaded_pass(args, cfg, t, y0, s, stream)
     print(json.dumps(out), flush=True)
+
+
+def offloaded_pass(args, cfg, t, y0, s, stream):
+    """The same step with the expert weights in pinned host memory
+    (OffloadedMoELayer): the weights of G experts at a time are uploaded
+    beside the GEMMs, the weight gradients downloaded.  The device copies of
+    the weights are freed first, so the HBM peak is the offloaded one."""
+    import torch
+    import mixture_experts_layer_permute_amd as M
+    from moe_inputs import device
+
+    def pinned(name):
+        if t[name] is None:
+            return None
+        h = torch.empty(t[name].shape, dtype=t[name].dtype, pin_memory=True)
+        h.copy_(t[name])
+        t[name] = None                      # drop the device copy
+        return h
+    W1, W2, W3 = pinned("W1"), pinned("W2"), pinned("W3")
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats()
+    G = args.offload_experts
+    lay = M.OffloadedMoELayer(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.act,
+                              device.torch_dtype(cfg), cfg.renorm, group_experts=G)
+    lay.bind(t["x"], t["Wg"], W1, W2, W3, t["bias"], t["dy"])
+    for _ in range(args.warmup):
+        lay.step(s)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        lay.step(s)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    b = 2 if cfg.dtype == "bf16" else 4
+    per_expert = cfg.d * cfg.f * (3 if cfg.swiglu else 2) * b
+    n = len(lay.groups)
+    # uploads: every group in the forward, all but the last two again in the
+    # backward; downloads: every expert's weight gradients
+    up = (cfg.E + sum(ne for _, ne in lay.groups[:max(0, n - 2)])) * per_expert
+    down = cfg.E * per_expert
+    return {"experts_per_group": lay.G, "ms_per_step": round(ms, 5),
+            "value": round(cfg.T / (ms * 1e-3), 1), "unit": "tokens/s",
+            "pcie_bytes_per_step": up + down,
+            "pcie_gbs": round((up + down) / (ms * 1e-3) / 1e9, 1),
+            "hbm_peak_bytes": torch.cuda.max_memory_allocated(),
+            "expert_weight_bytes_on_host": cfg.E * per_expert,
+            "y_bit_identical": bool(torch.equal(y0, lay.y))}
 
 
 if __name__ == "__main__":

@@ -147,7 +147,10 @@ moe_status moe_permute(const int32_t *topk_idx, const void *x, int T, int d,
  * Source: FastMoE review, 제안 방법 (dedicated expert FFN, parallel expert
  * linear layers); ES-MoE review, 三 技术架构 (experts take their tokens in
  * sequence, no padding).
- *   x_perm [R,d] dt, offsets [E+1] int32 (device; R = offsets[E]),
+ *   x_perm [R,d] dt, offsets [E+1] int32 (device; absolute row indices,
+ *     nondecreasing, offsets[E] <= R; rows outside offsets[0]..offsets[E] are
+ *     neither read nor written, so experts e0..e0+E-1 of a larger routing are
+ *     passed as offsets + e0 with E = their count and their own weights),
  *   W1 [E,d,f], W3 [E,d,f] (SwiGLU only, else NULL), W2 [E,f,d] dt,
  *   h_save: what the backward needs of the pre-activation, computed from the
  *     fp32 accumulator: GeLU: [R,f] = GeLU'(H); SwiGLU: [R,2f], row r =
@@ -176,6 +179,9 @@ moe_status moe_expert_ffn_fwd(const void *x_perm, const int32_t *offsets,
  * segment length; each output tile is summed by one workgroup in order.
  *   d_out_perm [R,d], x_perm [R,d], h_save, a_save as written by the forward,
  *   dx_perm [R,d], dW1 [E,d,f], dW3 [E,d,f] (SwiGLU only), dW2 [E,f,d], dt.
+ *   offsets as for moe_expert_ffn_fwd (a subset of experts: offsets + e0,
+ *   their count, their weights and weight gradients; dx_perm rows of other
+ *   experts are left as they are).
  *   ws: at least moe_ffn_workspace_bytes(R,E,d,f,act,dt,1) (holds dH).
  */
 moe_status moe_expert_ffn_bwd(const void *d_out_perm, const void *x_perm,

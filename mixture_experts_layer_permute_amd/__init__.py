@@ -15,4 +15,4 @@ from .ops import (moe_combine, moe_combine_bwd, moe_expert_ffn_bwd,  # noqa: F40
                   moe_expert_ffn_bwd_gather, moe_gate_topk, moe_gate_topk_bwd,
                   moe_permute, moe_unpermute_grad, moe_init,
                   moe_set_overlap)
-from .layer import ChunkedMoELayer, MoELayer  # noqa: F401
+from .layer import ChunkedMoELayer, MoELayer, OffloadedMoELayer  # noqa: F401

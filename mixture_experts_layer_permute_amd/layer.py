@@ -344,3 +344,201 @@ class ChunkedMoELayer:
     def step(self, stream=None):
         self.forward(stream)
         self.backward(stream)
+
+
+class OffloadedMoELayer:
+    """The layer step with the expert weights in pinned host memory and only
+    the weights (and weight gradients) of G experts on the GPU at a time:
+    experts are processed group by group, and the next group's parameters
+    move in while the current group computes (ES-MoE review, 三 技术架构 /
+    专家级卸载与处理: expert-wise processing with parameter transfers
+    overlapped with expert compute).
+
+    forward:  moe_gate_topk -> moe_permute -> per group of G experts: the
+              group's W1/W2(/W3) uploaded on an upload stream into one of two
+              staging slots (the next group's upload overlaps this group's
+              GEMMs) -> moe_expert_ffn_fwd over the group's segments ->
+              moe_combine
+    backward: moe_combine_bwd -> moe_gate_topk_bwd (writes dx) -> per group,
+              last first: the group's weights (uploaded again unless the
+              forward left them in a slot) -> moe_expert_ffn_bwd over its
+              segments -> its dW
+              downloaded on a download stream -> moe_unpermute_grad (adds to dx)
+
+    A group call passes offsets + e0 and the group's expert count; rows stay
+    absolute, so every tile is the same fixed-order sum as in MoELayer and
+    every output (y, dx, dWg, dW1, dW2, dW3) is bit-identical to it.
+    Inputs: x, Wg, logit_bias, dy on the GPU; W1, W2, W3 as pinned host
+    tensors (bind).  dW1, dW2, dW3 are pinned host tensors, final once the
+    step's stream has been synchronised.
+    """
+
+    def __init__(self, T, d, f, E, k, act="gelu", dtype=torch.bfloat16, renorm=1,
+                 device="cuda", group_experts=4):
+        self.T, self.d, self.f, self.E, self.k = T, d, f, E, k
+        self.act = MOE_ACT_SWIGLU if act == "swiglu" else MOE_ACT_GELU
+        self.dtype = dtype
+        self.dt = MOE_BF16 if dtype == torch.bfloat16 else MOE_F32
+        self.renorm = renorm
+        self.device = torch.device(device)
+        self.G = G = max(1, min(int(group_experts), E))
+        self.groups = [(e0, min(G, E - e0)) for e0 in range(0, E, G)]
+        L = self.lib = load()
+        R = self.R = T * k
+        dev = self.device
+        e = lambda *s, dt=dtype: torch.empty(*s, dtype=dt, device=dev)
+        h = lambda *s: torch.empty(*s, dtype=dtype, pin_memory=True)
+        i32, f32 = torch.int32, torch.float32
+        sw = self.act == MOE_ACT_SWIGLU
+        hw = 2 * f if sw else f
+        self.logits = e(T, E, dt=f32)
+        self.topk_idx = e(T, k, dt=i32)
+        self.topk_w = e(T, k, dt=f32)
+        self.counts = e(E, dt=i32)
+        self.offsets = e(E + 1, dt=i32)
+        self.dest = e(T, k, dt=i32)
+        self.src = e(R, dt=i32)
+        self.x_perm = e(R, d)
+        self.h_save = e(R, hw)
+        self.a_save = e(R, f)
+        self.out_perm = e(R, d)
+        self.y = e(T, d)
+        self.d_out_perm = e(R, d)
+        self.d_topk_w = e(T, k, dt=f32)
+        self.dx_perm = e(R, d)
+        self.dx = e(T, d)
+        self.dWg = e(d, E)
+        # two staging slots of G experts' weights and weight gradients
+        self.W1s = [e(G, d, f) for _ in range(2)]
+        self.W2s = [e(G, f, d) for _ in range(2)]
+        self.W3s = [e(G, d, f) if sw else None for _ in range(2)]
+        self.dW1s = [e(G, d, f) for _ in range(2)]
+        self.dW2s = [e(G, f, d) for _ in range(2)]
+        self.dW3s = [e(G, d, f) if sw else None for _ in range(2)]
+        # weight gradients on the host (pinned)
+        self.dW1 = h(E, d, f)
+        self.dW2 = h(E, f, d)
+        self.dW3 = h(E, d, f) if sw else None
+        ws = lambda n: torch.empty(max(int(n), 1), dtype=torch.uint8, device=dev)
+        self.ws_perm = ws(L.moe_permute_workspace_bytes(T, E, k))
+        self.ws_ffn_f = ws(L.moe_ffn_workspace_bytes(R, G, d, f, self.act, self.dt, 0))
+        self.ws_ffn_b = ws(L.moe_ffn_workspace_bytes(R, G, d, f, self.act, self.dt, 1))
+        self.ws_gate = ws(L.moe_gate_bwd_workspace_bytes(T, d, E))
+        self._up_stream = torch.cuda.Stream(device=dev)
+        self._dn_stream = torch.cuda.Stream(device=dev)
+        ev = lambda: [torch.cuda.Event(), torch.cuda.Event()]
+        self._up, self._free, self._dl = ev(), ev(), ev()
+        self._slot = [-1, -1]          # group whose weights each slot holds
+
+    def bind(self, x, Wg, W1, W2, W3=None, logit_bias=None, dy=None):
+        """x, Wg, logit_bias, dy on the GPU; W1 [E,d,f], W2 [E,f,d], W3 as
+        pinned, contiguous host tensors of the layer's dtype."""
+        for t in (x, Wg, dy):
+            if t is not None:
+                assert t.is_cuda and t.is_contiguous() and t.dtype == self.dtype
+        for t in (W1, W2, W3):
+            if t is not None:
+                assert (not t.is_cuda and t.is_pinned() and t.is_contiguous()
+                        and t.dtype == self.dtype)
+        assert (W3 is not None) == (self.act == MOE_ACT_SWIGLU)
+        self.x, self.Wg, self.bias, self.dy = x, Wg, logit_bias, dy
+        self.W1h, self.W2h, self.W3h = W1, W2, W3
+        self._slot = [-1, -1]
+        return self
+
+    def _upload(self, g):
+        """The weights of group g into slot g % 2 on the upload stream, once
+        the GEMMs that last read that slot are done."""
+        b = g % 2
+        if self._slot[b] == g:
+            return
+        e0, ne = self.groups[g]
+        us = self._up_stream
+        us.wait_event(self._free[b])
+        with torch.cuda.stream(us):
+            self.W1s[b][:ne].copy_(self.W1h[e0:e0 + ne], non_blocking=True)
+            self.W2s[b][:ne].copy_(self.W2h[e0:e0 + ne], non_blocking=True)
+            if self.W3h is not None:
+                self.W3s[b][:ne].copy_(self.W3h[e0:e0 + ne], non_blocking=True)
+        self._up[b].record(us)
+        self._slot[b] = g
+
+    def forward(self, stream=None):
+        s = _stream(self.device) if stream is None else stream
+        ms = _torch_stream(stream, self.device)
+        p = lambda t: None if t is None else t.data_ptr()
+        L, T, d, f, E, k, R = self.lib, self.T, self.d, self.f, self.E, self.k, self.R
+        dt, a = self.dt, self.act
+        check(L.moe_gate_topk(p(self.x), p(self.Wg), p(self.bias), T, d, E, k, self.renorm,
+                              dt, p(self.logits), p(self.topk_idx), p(self.topk_w), s),
+              "moe_gate_topk")
+        check(L.moe_permute(p(self.topk_idx), p(self.x), T, d, E, k, dt, p(self.counts),
+                            p(self.offsets), p(self.dest), p(self.src), p(self.x_perm),
+                            p(self.ws_perm), self.ws_perm.numel(), s), "moe_permute")
+        n = len(self.groups)
+        # the host weights may have changed since the last step: upload all
+        self._slot = [-1, -1]
+        self._upload(0)
+        for g, (e0, ne) in enumerate(self.groups):
+            b = g % 2
+            if g + 1 < n:
+                self._upload(g + 1)
+            ms.wait_event(self._up[b])
+            check(L.moe_expert_ffn_fwd(p(self.x_perm), p(self.offsets) + 4 * e0, R, ne, d, f,
+                                       a, dt, p(self.W1s[b]), p(self.W3s[b]), p(self.W2s[b]),
+                                       p(self.h_save), p(self.a_save), p(self.out_perm),
+                                       p(self.ws_ffn_f), self.ws_ffn_f.numel(), s),
+                  "moe_expert_ffn_fwd")
+            self._free[b].record(ms)
+        check(L.moe_combine(p(self.out_perm), p(self.dest), p(self.topk_w), T, k, d, dt,
+                            p(self.y), s), "moe_combine")
+        return self.y
+
+    def backward(self, stream=None):
+        assert self.dy is not None, "bind(dy=...) first"
+        s = _stream(self.device) if stream is None else stream
+        ms = _torch_stream(stream, self.device)
+        p = lambda t: None if t is None else t.data_ptr()
+        L, T, d, f, E, k, R = self.lib, self.T, self.d, self.f, self.E, self.k, self.R
+        dt, a = self.dt, self.act
+        check(L.moe_combine_bwd(p(self.dy), p(self.out_perm), p(self.dest), p(self.topk_w),
+                                T, k, d, dt, p(self.d_out_perm), p(self.d_topk_w), s),
+              "moe_combine_bwd")
+        check(L.moe_gate_topk_bwd(p(self.x), p(self.Wg), p(self.logits), p(self.topk_idx),
+                                  p(self.topk_w), p(self.d_topk_w), T, d, E, k, self.renorm,
+                                  dt, p(self.dx), 0, p(self.dWg), p(self.ws_gate),
+                                  self.ws_gate.numel(), s), "moe_gate_topk_bwd")
+        order = list(range(len(self.groups)))[::-1]   # the forward's last groups are resident
+        ds = self._dn_stream
+        self._upload(order[0])
+        for i, g in enumerate(order):
+            e0, ne = self.groups[g]
+            b = g % 2
+            if i + 1 < len(order):
+                self._upload(order[i + 1])
+            ms.wait_event(self._up[b])
+            ms.wait_event(self._dl[b])            # slot b's previous dW is on the host
+            check(L.moe_expert_ffn_bwd(p(self.d_out_perm), p(self.x_perm), p(self.h_save),
+                                       p(self.a_save), p(self.offsets) + 4 * e0, R, ne, d, f,
+                                       a, dt, p(self.W1s[b]), p(self.W3s[b]), p(self.W2s[b]),
+                                       p(self.dx_perm), p(self.dW1s[b]), p(self.dW3s[b]),
+                                       p(self.dW2s[b]), p(self.ws_ffn_b),
+                                       self.ws_ffn_b.numel(), s), "moe_expert_ffn_bwd")
+            self._free[b].record(ms)
+            ds.wait_event(self._free[b])
+            with torch.cuda.stream(ds):
+                self.dW1[e0:e0 + ne].copy_(self.dW1s[b][:ne], non_blocking=True)
+                self.dW2[e0:e0 + ne].copy_(self.dW2s[b][:ne], non_blocking=True)
+                if self.dW3 is not None:
+                    self.dW3[e0:e0 + ne].copy_(self.dW3s[b][:ne], non_blocking=True)
+            self._dl[b].record(ds)
+        check(L.moe_unpermute_grad(p(self.dx_perm), p(self.dest), T, k, d, dt, p(self.dx), 1,
+                                   s), "moe_unpermute_grad")
+        # the step ends on the caller's stream with every download done
+        ms.wait_event(self._dl[0])
+        ms.wait_event(self._dl[1])
+        return self.dx
+
+    def step(self, stream=None):
+        self.forward(stream)
+        self.backward(stream)
