@@ -370,7 +370,10 @@ class OffloadedMoELayer:
     every output (y, dx, dWg, dW1, dW2, dW3) is bit-identical to it.
     Inputs: x, Wg, logit_bias, dy on the GPU; W1, W2, W3 as pinned host
     tensors (bind).  dW1, dW2, dW3 are pinned host tensors, final once the
-    step's stream has been synchronised.
+    step's stream has been synchronised.  The host weights may change between
+    steps (every forward uploads them again), not between a forward and its
+    backward (which reuses the two groups still staged), and not while the
+    step's uploads are in flight.
     """
 
     def __init__(self, T, d, f, E, k, act="gelu", dtype=torch.bfloat16, renorm=1,
