@@ -550,6 +550,7 @@ def offloaded_pass(args, cfg, t, y0, s, stream):
     e0.record(stream)
     for _ in range(args.steps):
         lay.step(s)
+    stream.wait_event(lay.grads_ready)     # the last step's gradients are on the host
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps

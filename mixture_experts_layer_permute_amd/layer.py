@@ -370,10 +370,12 @@ class OffloadedMoELayer:
     every output (y, dx, dWg, dW1, dW2, dW3) is bit-identical to it.
     Inputs: x, Wg, logit_bias, dy on the GPU; W1, W2, W3 as pinned host
     tensors (bind).  dW1, dW2, dW3 are pinned host tensors, final once the
-    step's stream has been synchronised.  The host weights may change between
-    steps (every forward uploads them again), not between a forward and its
-    backward (which reuses the two groups still staged), and not while the
-    step's uploads are in flight.
+    event grads_ready has completed (grads_ready.synchronize(), a stream that
+    waits for it, or torch.cuda.synchronize()): the last downloads run beside
+    the next step's uploads, not on the step's stream.  The host weights may
+    change between steps (every forward uploads them again), not between a
+    forward and its backward (which reuses the two groups still staged), and
+    not while the step's uploads are in flight.
     """
 
     def __init__(self, T, d, f, E, k, act="gelu", dtype=torch.bfloat16, renorm=1,
@@ -432,6 +434,9 @@ class OffloadedMoELayer:
         ev = lambda: [torch.cuda.Event(), torch.cuda.Event()]
         self._up, self._free, self._dl = ev(), ev(), ev()
         self._slot = [-1, -1]          # group whose weights each slot holds
+        # recorded on the download stream once a backward's weight gradients
+        # are all on the host
+        self.grads_ready = torch.cuda.Event()
 
     def bind(self, x, Wg, W1, W2, W3=None, logit_bias=None, dy=None):
         """x, Wg, logit_bias, dy on the GPU; W1 [E,d,f], W2 [E,f,d], W3 as
@@ -512,15 +517,18 @@ class OffloadedMoELayer:
                                   dt, p(self.dx), 0, p(self.dWg), p(self.ws_gate),
                                   self.ws_gate.numel(), s), "moe_gate_topk_bwd")
         order = list(range(len(self.groups)))[::-1]   # the forward's last groups are resident
-        ds = self._dn_stream
         self._upload(order[0])
+        pending = [None, None]                # group whose dW a slot holds, not yet downloaded
         for i, g in enumerate(order):
             e0, ne = self.groups[g]
             b = g % 2
             if i + 1 < len(order):
                 self._upload(order[i + 1])
+            if pending[b] is not None:        # the slot's previous dW goes out first
+                self._download(pending[b])
+                pending[b] = None
             ms.wait_event(self._up[b])
-            ms.wait_event(self._dl[b])            # slot b's previous dW is on the host
+            ms.wait_event(self._dl[b])        # slot b's previous dW is on the host
             check(L.moe_expert_ffn_bwd(p(self.d_out_perm), p(self.x_perm), p(self.h_save),
                                        p(self.a_save), p(self.offsets) + 4 * e0, R, ne, d, f,
                                        a, dt, p(self.W1s[b]), p(self.W3s[b]), p(self.W2s[b]),
@@ -528,19 +536,31 @@ class OffloadedMoELayer:
                                        p(self.dW2s[b]), p(self.ws_ffn_b),
                                        self.ws_ffn_b.numel(), s), "moe_expert_ffn_bwd")
             self._free[b].record(ms)
-            ds.wait_event(self._free[b])
-            with torch.cuda.stream(ds):
-                self.dW1[e0:e0 + ne].copy_(self.dW1s[b][:ne], non_blocking=True)
-                self.dW2[e0:e0 + ne].copy_(self.dW2s[b][:ne], non_blocking=True)
-                if self.dW3 is not None:
-                    self.dW3[e0:e0 + ne].copy_(self.dW3s[b][:ne], non_blocking=True)
-            self._dl[b].record(ds)
+            pending[b] = g
         check(L.moe_unpermute_grad(p(self.dx_perm), p(self.dest), T, k, d, dt, p(self.dx), 1,
                                    s), "moe_unpermute_grad")
-        # the step ends on the caller's stream with every download done
-        ms.wait_event(self._dl[0])
-        ms.wait_event(self._dl[1])
+        # the last groups' gradients go out after the step's GEMMs: downloads
+        # into pinned memory run as copy kernels on all compute units, and
+        # beside a GEMM they slowed it several times over
+        for g in order[-2:]:
+            if pending[g % 2] == g:
+                self._download(g)
+        self.grads_ready.record(self._dn_stream)
         return self.dx
+
+    def _download(self, g):
+        """Group g's weight gradients from slot g % 2 to the host (download
+        stream, after the GEMMs that wrote them)."""
+        b = g % 2
+        e0, ne = self.groups[g]
+        ds = self._dn_stream
+        ds.wait_event(self._free[b])
+        with torch.cuda.stream(ds):
+            self.dW1[e0:e0 + ne].copy_(self.dW1s[b][:ne], non_blocking=True)
+            self.dW2[e0:e0 + ne].copy_(self.dW2s[b][:ne], non_blocking=True)
+            if self.dW3 is not None:
+                self.dW3[e0:e0 + ne].copy_(self.dW3s[b][:ne], non_blocking=True)
+        self._dl[b].record(ds)
 
     def step(self, stream=None):
         self.forward(stream)
