@@ -85,3 +85,21 @@ def test_offloaded_back_to_back_steps():
         off.step()
     torch.cuda.synchronize()
     same(off, ref, cfg.swiglu)
+
+
+def test_grads_ready_covers_the_downloads():
+    """Waiting on grads_ready alone (no device synchronisation) is enough
+    for the host weight gradients: they equal the resident layer's."""
+    cfg = small_variant("moe_s_like", T=1000, d=256, f=512, E=8, k=2)
+    banner("offload grads_ready", cfg.short())
+    t = device.gen_all(cfg)
+    ref = whole_step(cfg, t)
+    for G in (2, 4):                  # four groups (downloads as slots recycle), two groups
+        off = offloaded(cfg, t, G)
+        off.dW1.zero_()
+        off.dW2.zero_()
+        off.step()
+        off.grads_ready.synchronize()
+        assert torch.equal(off.dW1, ref.dW1.cpu()), G
+        assert torch.equal(off.dW2, ref.dW2.cpu()), G
+        torch.cuda.synchronize()
