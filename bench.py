@@ -116,6 +116,28 @@ def parse():
     return ap.parse_args()
 
 
+def mfma_loop_tflops(torch, L, s, stream, iters=50000, reps=3):
+    """Attainable bf16 matrix-instruction rate: moe_mfma_loop on two
+    workgroups of 4 waves per compute unit (two waves per SIMD), register
+    operands only, timed with events on the step's stream."""
+    from mixture_experts_layer_permute_amd import _lib
+    blocks = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(blocks * 4, dtype=torch.float32, device="cuda")
+    run = lambda: _lib.check(L.moe_mfma_loop(blocks, iters, out.data_ptr(), out.numel(), s),
+                             "moe_mfma_loop")
+    run()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return blocks * 4 * 4 * iters * 2.0 * 32 * 32 * 16 / (ms * 1e-3) / 1e12
+
+
 def stream_copy_gbs(torch, mib=1024, reps=5):
     """Measured device copy bandwidth (read + write bytes / time), the
     reference for the memory kernels' GB/s."""
@@ -373,6 +395,7 @@ def main():
         del junk
         torch.cuda.empty_cache()
     copy_gbs = stream_copy_gbs(torch)
+    mfma_tf = mfma_loop_tflops(torch, L, s, stream)
     work = kernel_work(cfg)
     kernels = {}
     for name, v in per.items():
@@ -408,6 +431,8 @@ def main():
         if unit == "flop":
             ent["tflops"] = round(amt / (per_call * 1e-3) / 1e12, 2)
             ent["frac_of_peak"] = round(ent["tflops"] / PEAK_BF16_TFLOPS, 4)
+            if cfg.dtype == "bf16":
+                ent["frac_of_mfma_loop"] = round(ent["tflops"] / mfma_tf, 4)
             gemm_ms += per_call * calls
         else:
             ent["gbs"] = round(amt / (per_call * 1e-3) / 1e9, 1)
@@ -467,6 +492,9 @@ def main():
                     "p90": round(pct(0.9), 5)},
         "value_at_median_step": round(cfg.T / (pct(0.5) * 1e-3), 1),
         "stream_copy_gbs": round(copy_gbs, 1),
+        "mfma_loop_tflops": round(mfma_tf, 1),
+        "gemm_frac_of_mfma_loop": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / mfma_tf, 4)
+        if gemm_ms and cfg.dtype == "bf16" else None,
         "roofline": roof,
         "graph_replay": graph,
         "kernels": kernels,

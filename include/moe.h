@@ -321,6 +321,19 @@ void moe_profile_reset(void);
 int moe_profile_count(void);
 moe_status moe_profile_get(int i, const char **name, float *ms);
 
+/*
+ * moe_mfma_loop -- benchmark support: the attainable rate of the bf16 matrix
+ * instructions.  `blocks` workgroups of 4 waves each run `iters` rounds of
+ * four independent v_mfma_f32_32x32x16_bf16 on register operands (no memory
+ * traffic): 4 * 4 * iters * 2*32*32*16 FLOP per workgroup.  Timed by the
+ * caller on `stream`, it gives the matrix cores' rate at the clock they run
+ * at under load, against which the grouped GEMMs are also rated.
+ *   out: device buffer of at least blocks * 4 floats (one value per wave,
+ *   meaningless; written so that the work is not optimised away).
+ */
+moe_status moe_mfma_loop(int blocks, int iters, float *out, size_t out_floats,
+                         hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

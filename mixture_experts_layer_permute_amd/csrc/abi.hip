@@ -129,9 +129,51 @@ void prof_mark(const char* name, hipStream_t s, int end) {
     }
 }
 
+// ------------------------------------------------- attainable MFMA rate
+// Every wave issues iters rounds of four independent bf16 32x32x16 matrix
+// instructions on register operands (no memory traffic), so the kernel's
+// rate is what the matrix cores sustain at the clock they run at.  Lane 0
+// of each wave stores one sum so that nothing is optimised away.
+__global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, float* __restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    bf16x8 a, b;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        a[q] = (__bf16)(0.001f * (float)(lane + q));
+        b[q] = (__bf16)(0.002f * (float)(lane - q));
+    }
+    f32x16 acc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[c][v] = 0.0f;
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s += acc[c][v];
+    if (lane == 0) out[blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6)] = s;
+}
+
 }  // namespace moe
 
 extern "C" {
+
+moe_status moe_mfma_loop(int blocks, int iters, float* out, size_t out_floats,
+                         hipStream_t stream) {
+    using namespace moe;
+    MOE_CHECK_ARG(blocks >= 1 && iters >= 1 && out);
+    MOE_CHECK_ARG(out_floats >= (size_t)blocks * 4);
+    MOE_CHECK_DEVICE();
+    MOE_LAUNCH("mfma_loop", stream,
+               mfma_loop_kernel<<<blocks, 256, 0, stream>>>(iters, out));
+    return launch_status();
+}
 
 void moe_profile_disable(void) {
     using namespace moe;

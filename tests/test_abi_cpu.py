@@ -163,3 +163,10 @@ def test_binding_types_match_the_header():
         got = [kind.get(a, "ptr") for a in args]     # POINTER(...) is a pointer
         assert got == kinds, (name, got, kinds)
         assert kind.get(res) == rk, (name, res, rk)
+
+
+def test_mfma_loop_rejects_bad_arguments(lib):
+    INV = _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_mfma_loop(0, 10, None, 0, None) == INV          # no blocks, no buffer
+    assert lib.moe_mfma_loop(4, 0, 16, 16, None) == INV            # no iterations
+    assert lib.moe_mfma_loop(4, 10, 16, 15, None) == INV           # buffer under blocks * 4
