@@ -127,8 +127,11 @@ moe_status moe_gate_topk(const void *x, const void *Wg, const float *logit_bias,
  *   x_perm == NULL skips the row copy (x may then be NULL too): routing only,
  *   for the *_gather FFN entry points, which read x through src.
  *   ws: device workspace of at least moe_permute_workspace_bytes(T,E,k).
- * Entries of topk_idx outside [0,E) give MOE_ERR_INVALID_ARG only if detected
- * on the host; the kernels skip them (their dest entries are then undefined).
+ * Entries of topk_idx outside [0,E) are a caller error that the device
+ * cannot report: such a pair is left out of counts and offsets (offsets[E]
+ * is then the number of valid pairs), its dest entry is set to -1 (which
+ * moe_combine, moe_combine_bwd and moe_unpermute_grad skip) and src holds
+ * no entry for it (src[offsets[E]..T*k-1] are left as they were).
  */
 size_t moe_permute_workspace_bytes(int T, int E, int k);
 moe_status moe_permute(const int32_t *topk_idx, const void *x, int T, int d,
@@ -177,6 +180,12 @@ moe_status moe_expert_ffn_fwd(const void *x_perm, const int32_t *offsets,
  *   dx_perm = dH W1[e]^T (+ dH3 W3[e]^T)
  * An expert with no rows gets dW = 0.  The dW products sum over the ragged
  * segment length; each output tile is summed by one workgroup in order.
+ * Sources: "Flattening Every Memory Peak in Long-Context MoE Training",
+ * English abstract (reordering the work leaves loss and gradients exact, so
+ * the gradients of the permuted, unpadded layout are those of the dense
+ * layer); FastMoE review, 제안 방법 (the experts' linear layers over the
+ * scatter/gather layout -- their backward is the same grouped products,
+ * transposed).
  *   d_out_perm [R,d], x_perm [R,d], h_save, a_save as written by the forward,
  *   dx_perm [R,d], dW1 [E,d,f], dW3 [E,d,f] (SwiGLU only), dW2 [E,f,d], dt.
  *   offsets as for moe_expert_ffn_fwd (a subset of experts: offsets + e0,
@@ -263,6 +272,10 @@ moe_status moe_combine(const void *out_perm, const int32_t *dest,
  * moe_combine_bwd -- derivative of moe_combine:
  *   d_out_perm[dest[t,j],:] = topk_w[t,j] * dy[t,:]
  *   d_topk_w[t,j]           = sum_i dy[t,i] * out_perm[dest[t,j],i]  (fp32)
+ * The derivative of the gather-combine of the scatter/gather layout (FastMoE
+ * review, 제안 방법), written as a gather over dest so that no two lanes write
+ * one row; exact under the reordering ("Flattening Every Memory Peak in
+ * Long-Context MoE Training", English abstract: loss and gradients exact).
  *   dy [T,d] dt, out_perm [T*k,d] dt, dest [T,k], topk_w [T,k] float,
  *   d_out_perm [T*k,d] dt, d_topk_w [T,k] float.
  */
@@ -274,7 +287,11 @@ moe_status moe_combine_bwd(const void *dy, const void *out_perm,
 /*
  * moe_unpermute_grad -- backward of moe_permute's row copy, the sum back to
  * token order: dx[t,:] (+)= sum_j dx_perm[dest[t,j],:], gathered per token in
- * slot order (deterministic, no atomics).
+ * slot order (deterministic, no atomics).  Sources: FastMoE review, 제안 방법
+ * (the scatter of token rows into the per-expert layout; its derivative
+ * returns each row's gradient to the token that sent it); "Flattening Every
+ * Memory Peak in Long-Context MoE Training", English abstract (reordering
+ * leaves the gradients exact).
  *   dx_perm [T*k,d] dt, dest [T,k] int32, dx [T,d] dt;
  *   accumulate != 0 adds to dx instead of overwriting it.
  */
@@ -284,7 +301,12 @@ moe_status moe_unpermute_grad(const void *dx_perm, const int32_t *dest, int T,
 
 /*
  * moe_gate_topk_bwd -- backward of moe_gate_topk through the gate weights
- * (the selection itself is piecewise constant):
+ * (the selection itself is piecewise constant).  Sources: ES-MoE review,
+ * 三 技术架构 (the gating network's output decides each token's experts;
+ * the gate is trained with the layer); "Flattening Every Memory Peak in
+ * Long-Context MoE Training", English abstract (gradients stay exact under
+ * the reordering, so the gate's gradient is the dense layer's).  The gate
+ * formula is not printed: the derivative of softmax top-k is the reading.
  *   renorm=1: dl[t,idx_j] = w_j (dw_j - sum_j' w_j' dw_j'), 0 elsewhere
  *   renorm=0: dl[t,e] = p_e (g_e - sum_j w_j dw_j), p = softmax(logits[t,:]),
  *             g_e = dw_j where e = idx_j else 0

@@ -152,6 +152,8 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(
                             wcnt[w * E + e] + popc64(peers & lt);
             dest[i] = pos;
             src[pos] = (int)(i / k);
+        } else if (i < end) {
+            dest[i] = -1;            // an expert id outside [0,E): no row
         }
         __builtin_amdgcn_wave_barrier();
         if (valid && (peers & lt) == 0) wcnt[w * E + e] += popc64(peers);

@@ -154,9 +154,12 @@ class MoELayer:
         check(getattr(L, comb[0])(*comb[1], s), comb[0])
         # under HIP graph capture everything stays on the capturing stream
         # (plus the library's own side stream): capturing a second user
-        # stream that shares that side stream ended the capture with a
-        # crash in the runtime on this ROCm
-        if self.overlap_gate and not torch.cuda.is_current_stream_capturing():
+        # stream that shared that side stream once ended the capture with a
+        # crash in the runtime, whose cause is not known.  The capture state
+        # is that of the stream the step runs on, not of torch's current one
+        with torch.cuda.stream(ms):
+            capturing = torch.cuda.is_current_stream_capturing()
+        if self.overlap_gate and not capturing:
             if self._gstream is None:
                 self._gstream = torch.cuda.Stream(device=self.device)
             gs = self._gstream

@@ -18,7 +18,7 @@ import mixture_experts_layer_permute_amd as M
 import oracle
 from moe_inputs import CONFIGS, device, rng, small_variant, stage
 
-from _gpu import (assert_close, assert_equal_i, banner, dev, dev_i32, host,
+from _gpu import (assert_close, assert_equal_i, banner, dev, dev_i32, host, host_i,
                   needs_gpu, saved_state)
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
@@ -174,3 +174,30 @@ def test_random_gate_and_permute(dt):
         assert_equal_i(src, rs, "src")
         got = host(xp)
         assert np.array_equal(got, oracle.dispatch_rows(x, rs)), "x_perm"
+
+
+def test_permute_skips_invalid_expert_ids():
+    """Pairs whose expert id lies outside [0,E) are left out of counts and
+    offsets and get dest = -1; the valid pairs keep their stable order."""
+    g = np.random.default_rng(99)
+    T, k, E, d = 300, 3, 7, 64
+    idx = np.stack([g.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    bad = g.choice(T * k, size=11, replace=False)
+    flat = idx.reshape(-1)
+    flat[bad[:6]] = E                      # one past the last expert
+    flat[bad[6:]] = -1
+    x = stage.normal(5, (T, d), 1.0, "bf16")
+    banner("permute with invalid ids", T, k, E)
+    counts, offsets, dest, src, xp = M.moe_permute(dev_i32(idx), dev(x, "bf16"), E)
+    torch.cuda.synchronize()
+    valid = (flat >= 0) & (flat < E)
+    nv = int(valid.sum())
+    order = np.argsort(np.where(valid, flat, E), kind="stable")
+    want_dest = np.full(T * k, -1, np.int64)
+    want_dest[order[:nv]] = np.arange(nv)
+    want_counts = np.bincount(flat[valid], minlength=E)
+    assert_equal_i(counts, want_counts, "counts")
+    assert_equal_i(offsets, np.concatenate([[0], np.cumsum(want_counts)]), "offsets")
+    assert_equal_i(dest, want_dest.reshape(T, k), "dest")
+    assert_equal_i(host_i(src)[:nv], order[:nv] // k, "src")
+    assert np.array_equal(host(xp)[:nv], x.astype(np.float64)[order[:nv] // k]), "x_perm"
