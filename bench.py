@@ -4,8 +4,9 @@
 A step is the whole path: moe_gate_topk -> moe_permute -> moe_expert_ffn_fwd
 -> moe_combine -> moe_combine_bwd -> moe_expert_ffn_bwd -> moe_unpermute_grad
 -> moe_gate_topk_bwd, on inputs already resident in HBM.  Default workload:
-the MoE-S-like layer (T=8192 tokens, d=1024, f=4096, 8 experts, top-2,
-GeLU, bf16 storage with fp32 accumulation), seeded synthetic inputs.
+the long-context chunk (T=65536 tokens, d=4096, f=14336, 128 SwiGLU
+experts, top-8, Zipf 0.8 routing skew, bf16 storage with fp32
+accumulation), the largest workload, seeded synthetic inputs.
 
 Prints ONE JSON line.  Besides tokens/s it reports the grouped-GEMM TFLOP/s,
 a per-kernel table from HIP events recorded around every kernel launch in a
@@ -28,32 +29,32 @@ PEAK_F32_TFLOPS = 157.3       # fp32 vector
 PEAK_HBM_GBS = 8000.0
 
 # HBM bytes per call (fetch + write; a GEMM stage's main and partial-tile
-# launches together) of the FFN and row kernels on the MoE-S-like workload,
-# from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs scaled by the readings
-# of a plain 4 GiB device copy with a cold source in the same run (factors
-# 4.0 and 2.0); see
-# profiles/hbm_traffic_moe_s_like.md.  Valid only for the kernel sources
-# whose SHA-256 prefix is TRAFFIC_SRC; null once they change.
-TRAFFIC_SRC = "2741dcd9cbc3b572"
+# launches together) per workload, from rocprofv3 --pmc FETCH_SIZE and
+# WRITE_SIZE runs scaled by the readings of a plain 4 GiB device copy with a
+# cold source in the same run (the summaries under profiles/ give commands
+# and factors).  Valid only for the kernel sources whose SHA-256 prefix is
+# TRAFFIC_SRC; null once they change.
+TRAFFIC_SRC = ""
 TRAFFIC_SOURCES = ("ggemm.hip", "common.h", "permute.hip", "combine.hip")
-TRAFFIC = {"gemm_up_gelu": 1183561795, "gemm_down": 772682879,
-           "gemm_dA_gelu": 1183705354, "gemm_dW1": 1141068001,
-           "gemm_dW2": 1141068001, "gemm_dX": 772225240, "perm_copy": 101238743,
-           "combine": 101776378, "combine_bwd": 169111577,
-           "unpermute_grad": 134812261}
+TRAFFIC = {}
 
 
-def traffic_for(kernel, workload):
-    """Measured HBM bytes per launch, or None if stale or not measured."""
+def source_hash():
     import hashlib
-    if workload != "moe_s_like" or kernel not in TRAFFIC:
-        return None
     h = hashlib.sha256()
     for f in TRAFFIC_SOURCES:
         with open(os.path.join(ROOT, "mixture_experts_layer_permute_amd", "csrc", f),
                   "rb") as fh:
             h.update(fh.read())
-    return TRAFFIC[kernel] if h.hexdigest()[:16] == TRAFFIC_SRC else None
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel, workload):
+    """Measured HBM bytes per launch, or None if stale or not measured."""
+    t = TRAFFIC.get(workload, {})
+    if kernel not in t:
+        return None
+    return t[kernel] if source_hash() == TRAFFIC_SRC else None
 
 
 def kernel_work(cfg):
@@ -71,7 +72,8 @@ def kernel_work(cfg):
         "perm_copy": (T * d * b + R * d * b + 4 * R, "byte"),
         "combine": (R * d * b + T * d * b + 8 * R, "byte"),
         "combine_bwd": (T * d * b + 2 * R * d * b + 12 * R, "byte"),
-        "unpermute_grad": (R * d * b + T * d * b + 4 * R, "byte"),
+        # the layer calls it in accumulate mode: dx is read and written
+        "unpermute_grad": (R * d * b + 2 * T * d * b + 4 * R, "byte"),
     }
     return w
 
@@ -79,9 +81,9 @@ def kernel_work(cfg):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="moe_s_like",
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long_ctx_swiglu",
                     help="workload name (moe_inputs.configs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--serial", action="store_true",
@@ -90,6 +92,12 @@ def parse():
                          "per-kernel pass is always serial")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU work for the oracle baseline")
+    ap.add_argument("--cpu-tokens", type=int, default=2048,
+                    help="sampled oracle baseline of a large workload: tokens "
+                         "routed and carried through the row steps")
+    ap.add_argument("--cpu-rows", type=int, default=64,
+                    help="sampled oracle baseline: rows of each of the four "
+                         "seeded experts carried through the FFN")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB before the "
                          "steps (a known-size reference for HBM byte counters)")
@@ -182,14 +190,15 @@ def parity(cfg, layer, fw, gr):
     return out
 
 
-ORACLE_HOST_GIB = 64
+# Largest workload (grouped-GEMM FLOPs of a step) the full-layer oracle is
+# timed on; beyond it a bounded sample of the same workload is timed.
+ORACLE_FULL_FLOPS = 2e12
 
 
-def oracle_host_bytes(cfg):
-    """Rough host footprint of one full-layer oracle pass: the expert
-    weights in fp32 and about ten [R, f] / [R, d] arrays in fp64."""
-    nw = 3 if cfg.swiglu else 2
-    return 4 * cfg.E * cfg.d * cfg.f * nw + 8 * 10 * cfg.R * max(cfg.f, cfg.d)
+def oracle_threads():
+    from threadpoolctl import threadpool_info
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return min(threads, len(os.sched_getaffinity(0)))
 
 
 def cpu_baseline(cfg, budget_s):
@@ -197,7 +206,6 @@ def cpu_baseline(cfg, budget_s):
     import numpy as np
     import oracle
     from moe_inputs import rng
-    from threadpoolctl import threadpool_info
 
     # bounded sample: the first Ts tokens of the workload (all of it when it
     # fits the budget); weights are the workload's own
@@ -220,12 +228,128 @@ def cpu_baseline(cfg, budget_s):
         reps += 1
         if t_tot >= budget_s or reps >= 5:
             break
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    cores = min(threads, len(os.sched_getaffinity(0)))
-    return {"value": reps * Ts / t_tot, "unit": "tokens/s", "cores": cores,
+    return {"value": reps * Ts / t_tot, "unit": "tokens/s", "cores": oracle_threads(),
             "kind": "oracle",
             "sample": "NumPy float64 oracle, full layer fwd+bwd of all %d tokens "
                       "(%d rep%s, %.1f s)" % (Ts, reps, "s" if reps > 1 else "", t_tot)}, fw, gr
+
+
+def cpu_baseline_sampled(cfg, layer, args):
+    """The oracle, as it stands, on a bounded sample of a workload whose full
+    host pass would not fit: the routing of the first Ts tokens (fixed-order
+    logits, top-k, weights, counting sort), the FFN forward and backward of
+    sampled rows of the four seeded experts (weight gradients over those
+    rows), and the row steps of the Ts tokens (combine, its backward, the
+    unpermute, the gate backward) fed the GPU's own out_perm / dx_perm rows.
+    Each part is timed; the per-token cost is (routing + row steps) / Ts +
+    k * FFN / rows, reported as tokens/s.  Parity on the same sample: logits
+    bits and top-k of the Ts tokens; y, d_out_perm, d_topk_w and dx rows of
+    the Ts tokens; out_perm and dx_perm rows of the seeded experts."""
+    import numpy as np
+    import torch
+    import oracle
+    from moe_inputs import rng
+
+    T, k, d, E, f = cfg.T, cfg.k, cfg.d, cfg.E, cfg.f
+    Ts = max(1, min(T, args.cpu_tokens))
+    toks = np.arange(Ts)
+    tol = 2e-2 if cfg.dtype == "bf16" else 1e-5
+
+    def rows(t, r):
+        i = torch.as_tensor(np.asarray(r, np.int64), device=t.device)
+        return t.index_select(0, i).float().cpu().numpy().astype(np.float64)
+
+    def rel(g, r):
+        den = float(np.abs(r).max())
+        e = float(np.abs(g - r).max())
+        return e / den if den > 0 else e
+
+    x = rng.gen_rows(cfg, "x", toks)
+    dy = rng.gen_rows(cfg, "dy", toks)
+    Wg = rng.gen(cfg, "Wg")
+    bias = rng.logit_bias(cfg)
+    g_dest = layer.dest[:Ts].cpu().numpy()
+    g_out = rows(layer.out_perm, g_dest.reshape(-1))
+    g_dxp = rows(layer.dx_perm, g_dest.reshape(-1))
+    dest_local = np.arange(Ts * k).reshape(Ts, k)
+
+    t0 = time.perf_counter()
+    logits = oracle.gate_logits(x, Wg, bias)
+    idx = oracle.topk_select(logits, k)
+    w = oracle.gate_weights(logits, idx, cfg.renorm)
+    oracle.permute(idx, E)
+    t_route = time.perf_counter() - t0
+
+    t0 = time.perf_counter()
+    y = oracle.combine(g_out, dest_local, w)
+    d_out, dw = oracle.combine_bwd(dy, g_out, dest_local, w)
+    dx = oracle.unpermute_grad(g_dxp, dest_local)
+    _, _, dx_gate = oracle.gate_bwd(x, Wg, logits, idx, w, dw, cfg.renorm)
+    dx = dx + dx_gate
+    t_rows = time.perf_counter() - t0
+
+    par = {"sample_tokens": Ts}
+    par["logits_bit_exact"] = bool(np.array_equal(
+        layer.logits[:Ts].cpu().numpy().view(np.uint32), logits.view(np.uint32)))
+    par["topk_idx_exact"] = bool(np.array_equal(layer.topk_idx[:Ts].cpu().numpy(), idx))
+    par["y"] = rel(rows(layer.y, toks), y)
+    par["d_out_perm"] = rel(rows(layer.d_out_perm, g_dest.reshape(-1)),
+                            d_out.reshape(Ts * k, d))
+    par["d_topk_w"] = rel(layer.d_topk_w[:Ts].cpu().numpy().astype(np.float64), dw)
+    par["dx"] = rel(rows(layer.dx, toks), dx)
+
+    # FFN: sampled rows of the seeded experts (rows and tokens from the GPU's
+    # routing; each token's gate weight from the oracle's own routing of it)
+    offsets = layer.offsets.cpu().numpy()
+    src = layer.src.cpu().numpy()
+    g = np.random.default_rng(cfg.seed + 5)
+    t_ffn, n_rows, e_out, e_dxp = 0.0, 0, 0.0, 0.0
+    for e in rng.seeded_experts(cfg):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b == a:
+            continue
+        r = np.sort(g.choice(np.arange(a, b), size=min(args.cpu_rows, b - a),
+                             replace=False))
+        tok = src[r]
+        W1e = rng.gen(cfg, "W1", int(e))
+        W2e = rng.gen(cfg, "W2", int(e))
+        W3e = rng.gen(cfg, "W3", int(e)) if cfg.swiglu else None
+        xr = rng.gen_rows(cfg, "x", tok)
+        dyr = rng.gen_rows(cfg, "dy", tok)
+        t0 = time.perf_counter()
+        lr = oracle.gate_logits(xr, Wg, bias)
+        ir = oracle.topk_select(lr, k)
+        wr = oracle.gate_weights(lr, ir, cfg.renorm)
+        slot = np.argmax(ir == e, axis=1)
+        assert np.all(ir[np.arange(len(r)), slot] == e), "routing of a sampled row"
+        dO = wr[np.arange(len(r)), slot][:, None] * dyr
+        _, _, _, O = oracle.ffn_fwd_segment(xr, W1e, W2e, W3e, cfg.act)
+        dX = oracle.ffn_bwd_segment(dO, xr, W1e, W2e, W3e, cfg.act)[0]
+        t_ffn += time.perf_counter() - t0
+        n_rows += len(r)
+        e_out = max(e_out, rel(rows(layer.out_perm, r), O))
+        e_dxp = max(e_dxp, rel(rows(layer.dx_perm, r), dX))
+        del W1e, W2e, W3e
+    par["out_perm_seeded_rows"] = e_out
+    par["dx_perm_seeded_rows"] = e_dxp
+    par["seeded_rows"] = n_rows
+    par["tolerance"] = tol
+    par["pass"] = bool(par["logits_bit_exact"] and par["topk_idx_exact"] and
+                       max(par[n] for n in ("y", "d_out_perm", "d_topk_w", "dx",
+                                            "out_perm_seeded_rows",
+                                            "dx_perm_seeded_rows")) <= tol)
+    for n in ("y", "d_out_perm", "d_topk_w", "dx", "out_perm_seeded_rows",
+              "dx_perm_seeded_rows"):
+        par[n] = round(par[n], 6)
+    per_tok = (t_route + t_rows) / Ts + (k * t_ffn / n_rows if n_rows else 0.0)
+    return {"value": round(1.0 / per_tok, 2), "unit": "tokens/s", "cores": oracle_threads(),
+            "kind": "oracle",
+            "sample": "NumPy float64 oracle on a bounded sample: routing of %d tokens "
+                      "(%.2f s), row steps of those tokens (%.2f s), FFN forward and "
+                      "backward of %d rows of the 4 seeded experts (%.2f s); tokens/s = "
+                      "1 / ((routing + row steps) / %d + k * FFN / %d)"
+                      % (Ts, t_route, t_rows, n_rows, t_ffn, Ts, n_rows),
+            "parity": par}
 
 
 def load_stats(counts, cfg):
@@ -500,13 +624,11 @@ def main():
         "kernels": kernels,
         "load": load_stats(layer.counts, cfg),
     }
-    host_gb = oracle_host_bytes(cfg) / 2 ** 30
-    if not args.no_cpu_baseline and host_gb > ORACLE_HOST_GIB:
-        out["cpu_baseline"] = {
-            "skipped": "the full-layer oracle needs about %.0f GiB of host memory here "
-                       "(fp32 weights, fp64 activations), over the %d GiB this run allows; "
-                       "parity of this workload is the GPU test of routing in full and "
-                       "four seeded experts" % (host_gb, ORACLE_HOST_GIB)}
+    full_oracle = cfg.gemm_flops_fwd_bwd() <= ORACLE_FULL_FLOPS
+    if not args.no_cpu_baseline and not full_oracle:
+        # the sample reads the step's whole-batch buffers (not a chunked step's)
+        if isinstance(layer, M.MoELayer):
+            out["cpu_baseline"] = cpu_baseline_sampled(cfg, layer, args)
     elif not args.no_cpu_baseline:
         base, fw, gr = cpu_baseline(cfg, args.cpu_seconds)
         base["parity"] = parity(cfg, layer, fw, gr)

@@ -192,3 +192,45 @@ def test_chunked_back_to_back_steps():
     torch.cuda.synchronize()
     for n in SAME + ["dW1", "dW2"]:
         assert torch.equal(getattr(ch, n), getattr(ref, n)), n
+
+
+def test_chunked_many_chunks_at_full_width():
+    """Sixteen chunks of the skewed workload at its full sizes (T 16384,
+    d 2048, f 8192, 16 experts): every chunk adds one bf16 rounding of the
+    running weight gradient.  The four seeded experts and the heaviest one
+    are compared with the oracle on every entry of dW1 and dW2; y, dx and dWg
+    must equal the whole layer's bit for bit."""
+    cfg = small_variant("skewed_zipf1.2")
+    C = 1024
+    banner("chunked 16 chunks", cfg.short(), C)
+    t = device.gen_all(cfg)
+    args = (cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.act, device.torch_dtype(cfg), cfg.renorm)
+    ch = run(M.ChunkedMoELayer(*args, chunk_tokens=C), t)
+    whole = run(M.MoELayer(*args), t)
+    for n in SAME:
+        assert torch.equal(getattr(whole, n), getattr(ch, n)), n
+    counts = whole.counts.cpu().numpy()
+    offsets = whole.offsets.cpu().numpy()
+    src = whole.src.cpu().numpy()
+    dest = whole.dest.cpu().numpy()
+    w = whole.topk_w.cpu().numpy().astype(np.float64)
+    del whole
+    torch.cuda.empty_cache()
+    x, dy = rng.gen(cfg, "x"), rng.gen(cfg, "dy")
+    wrow = np.empty(cfg.R)
+    wrow[dest.reshape(-1)] = w.reshape(-1)
+    checked = [int(e) for e in rng.seeded_experts(cfg)]
+    heavy = int(np.argmax(counts))
+    checked += [heavy] if heavy not in checked else []
+    for e in checked:
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        banner("expert", e, "rows", b - a)
+        if b == a:
+            assert float(ch.dW1[e].abs().max()) == 0.0
+            continue
+        W1e, W2e = rng.gen(cfg, "W1", e), rng.gen(cfg, "W2", e)
+        xs = x[src[a:b]]
+        dO = wrow[a:b, None] * dy[src[a:b]]
+        _, dW1, _, dW2 = oracle.ffn_bwd_segment(dO, xs, W1e, W2e, None, cfg.act)
+        assert_close(host(ch.dW1[e]), dW1, cfg.dtype, "dW1[e=%d]" % e)
+        assert_close(host(ch.dW2[e]), dW2, cfg.dtype, "dW2[e=%d]" % e)

@@ -5,9 +5,13 @@ configuration the benchmark uses.
 * The whole layer runs on the GPU once.  Routing is compared in full and bit
   for bit (logits, top-k, counts, offsets, dest, src); the gate weights to
   fp32 precision.
-* Four seeded experts: sampled rows of H, A, out_perm, d_out_perm and dx_perm,
-  and sampled hidden units of dW1 / dW3 / dW2 against the oracle (which
-  computes those rows or units exactly, on the host copy of the inputs).  An
+* Four seeded experts plus the heaviest one (the ragged segments the skewed
+  workloads exist for) against the oracle on the host copy of the inputs.
+  On the 16- and 64-expert workloads every row of H, A, out_perm,
+  d_out_perm and dx_perm and the whole dW1 / dW2 of those experts are
+  compared.  On the long-context chunk (57 K rows in its heaviest expert)
+  48 sampled rows per expert, and one hidden unit in every 256-wide column
+  tile of dW1 / dW3 (all d rows) and row tile of dW2 (all d columns).  An
   expert with no rows must have dW exactly 0.
 * The row kernels (combine, combine backward, unpermute, gate backward) are
   fed independent seeded tensors of the full sizes, and their outputs are
@@ -29,6 +33,21 @@ from _gpu import (assert_close, assert_equal_i, banner, dev, dev_i32, host,
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
 LARGE = ["skewed_zipf1.2", "many_expert_zipf1.0", "long_ctx_swiglu"]
+# workloads whose checked experts are compared on every row and every dW entry
+FULL = {"skewed_zipf1.2", "many_expert_zipf1.0"}
+TILE = 256          # column tile of the dW products
+
+
+def checked_experts(cfg, counts):
+    """The four seeded experts, then the heaviest (lowest index on a tie)."""
+    out = [int(e) for e in rng.seeded_experts(cfg)]
+    heavy = int(np.argmax(counts))
+    return out + ([heavy] if heavy not in out else [])
+
+
+def tile_units(g, f):
+    """One hidden unit in every TILE-wide block of [0, f)."""
+    return np.array([lo + int(g.integers(min(TILE, f - lo))) for lo in range(0, f, TILE)])
 
 
 def take_rows(t, rows):
@@ -90,9 +109,11 @@ def test_large_layer(name):
     wrow = np.empty(cfg.R)
     wrow[h["dest"].reshape(-1)] = h["w"].reshape(-1)      # gate weight of each row
     f = cfg.f
-    for e in rng.seeded_experts(cfg):
+    full = name in FULL
+    for e in checked_experts(cfg, h["counts"]):
         a, b = int(h["offsets"][e]), int(h["offsets"][e + 1])
-        banner("expert", int(e), "rows", b - a, "%.1fs" % (time.time() - t0))
+        banner("expert", int(e), "rows", b - a, "full" if full else "sampled",
+               "%.1fs" % (time.time() - t0))
         if b == a:
             assert float(layer.dW1[e].abs().max()) == 0.0
             assert float(layer.dW2[e].abs().max()) == 0.0
@@ -102,7 +123,7 @@ def test_large_layer(name):
         W1e = rng.gen(cfg, "W1", int(e))
         W2e = rng.gen(cfg, "W2", int(e))
         W3e = rng.gen(cfg, "W3", int(e)) if cfg.swiglu else None
-        r = sample(g, a, b, 48)
+        r = np.arange(a, b) if full else sample(g, a, b, 48)
         xr = h["x"][h["src"][r]]
         H, H3, A, O = oracle.ffn_fwd_segment(xr, W1e, W2e, W3e, cfg.act)
         hs = take_rows(layer.h_save, r)
@@ -112,15 +133,29 @@ def test_large_layer(name):
             assert_close(hs[:, f:], want[:, f:], dt, "SiLU(H1)[e=%d]" % e)
         else:
             assert_close(hs, want, dt, "GeLU'(H)[e=%d]" % e)
+        del hs, want
         assert_close(take_rows(layer.a_save, r), A, dt, "A[e=%d]" % e)
         assert_close(take_rows(layer.out_perm, r), O, dt, "out_perm[e=%d]" % e)
         # backward: dO of every row of the segment, from the gate and dy
         dO_seg = wrow[a:b, None] * dy[h["src"][a:b]]
         assert_close(take_rows(layer.d_out_perm, r), dO_seg[r - a], dt,
                      "d_out_perm[e=%d]" % e)
-        dXr = oracle.ffn_bwd_segment(dO_seg[r - a], xr, W1e, W2e, W3e, cfg.act)[0]
+        saved = (H, H3, A)
+        del O
+        if full:
+            # every row of dx_perm and every entry of dW1 / dW2
+            dX, dW1, _, dW2 = oracle.ffn_bwd_segment(dO_seg, xr, W1e, W2e, W3e,
+                                                     cfg.act, saved=saved)
+            assert_close(take_rows(layer.dx_perm, r), dX, dt, "dx_perm[e=%d]" % e)
+            assert_close(host(layer.dW1[e]), dW1, dt, "dW1[e=%d]" % e)
+            assert_close(host(layer.dW2[e]), dW2, dt, "dW2[e=%d]" % e)
+            del dX, dW1, dW2, saved, H, H3, A
+            continue
+        dXr = oracle.ffn_bwd_segment(dO_seg[r - a], xr, W1e, W2e, W3e, cfg.act,
+                                     saved=saved)[0]
         assert_close(take_rows(layer.dx_perm, r), dXr, dt, "dx_perm[e=%d]" % e)
-        cols = np.sort(g.choice(f, size=8, replace=False))
+        # one hidden unit per column tile of dW1 / dW3 and row tile of dW2
+        cols = tile_units(g, f)
         c1, c3, c2 = oracle.ffn_bwd_columns(dO_seg, h["x"][h["src"][a:b]], W1e, W2e,
                                            W3e, cfg.act, cols)
         ci = torch.as_tensor(cols, device="cuda")

@@ -103,3 +103,34 @@ def test_grads_ready_covers_the_downloads():
         assert torch.equal(off.dW1, ref.dW1.cpu()), G
         assert torch.equal(off.dW2, ref.dW2.cpu()), G
         torch.cuda.synchronize()
+
+
+def test_offloaded_against_oracle():
+    """The offloaded step against the oracle itself (not only against the
+    resident layer): routing bit-exact, y, dx, dWg and every expert's weight
+    gradients within the dtype's tolerance (SwiGLU, ragged last group)."""
+    import numpy as np
+    import oracle
+    from moe_inputs import rng
+    from _gpu import assert_close, assert_equal_i, host
+    cfg = small_variant("long_ctx_swiglu", T=777, d=128, f=256, E=16, k=4)
+    banner("offload vs oracle", cfg.short())
+    t = device.gen_all(cfg)
+    off = offloaded(cfg, t, 5)
+    off.step()
+    off.grads_ready.synchronize()
+    torch.cuda.synchronize()
+    x, Wg, dy = (rng.gen(cfg, n) for n in ("x", "Wg", "dy"))
+    W1, W2, W3 = (rng.gen_experts(cfg, n) for n in ("W1", "W2", "W3"))
+    fw = oracle.layer_forward(x, Wg, W1, W2, W3, k=cfg.k, act=cfg.act,
+                              bias=rng.logit_bias(cfg), renorm=cfg.renorm)
+    gr = oracle.layer_backward(fw, dy, x, Wg, W1, W2, W3, act=cfg.act, renorm=cfg.renorm)
+    assert_equal_i(off.logits.cpu().numpy().view(np.uint32), fw["logits"].view(np.uint32),
+                   "logits")
+    assert_equal_i(off.topk_idx, fw["idx"], "topk_idx")
+    dt = cfg.dtype
+    assert_close(off.y, fw["y"], dt, "y")
+    assert_close(off.dx, gr["dx"], dt, "dx")
+    assert_close(off.dWg, gr["dWg"], dt, "dWg")
+    for n in ("dW1", "dW2", "dW3"):
+        assert_close(host(getattr(off, n)), gr[n], dt, n)
