@@ -173,6 +173,28 @@ moe_status moe_expert_ffn_fwd(const void *x_perm, const int32_t *offsets,
                               hipStream_t stream);
 
 /*
+ * moe_expert_ffn_fwd_noalloc -- moe_expert_ffn_fwd for callers that cannot
+ * allocate device memory or pass a workspace: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments and
+ * results (bit-identical) without ws/ws_bytes: the tile plan the forward
+ * needs (17 KiB at most, E <= 1024) lives in a library-owned static device
+ * array of 32 KiB per GPU, held until the process ends; its address is
+ * resolved by moe_init (or by the first call on a device).  The call
+ * allocates nothing and calls no allocating routine.  Every call on one GPU
+ * shares that array: calls that overlap in time on one GPU (other streams or
+ * host threads) race on it and must be ordered by the caller; consecutive
+ * calls on one stream are safe.  A plan larger than the array gives
+ * MOE_ERR_WORKSPACE.
+ */
+moe_status moe_expert_ffn_fwd_noalloc(const void *x_perm,
+                                      const int32_t *offsets, int R, int E,
+                                      int d, int f, moe_act act, moe_dtype dt,
+                                      const void *W1, const void *W3,
+                                      const void *W2, void *h_save,
+                                      void *a_save, void *out_perm,
+                                      hipStream_t stream);
+
+/*
  * moe_expert_ffn_bwd -- gradients of moe_expert_ffn_fwd.
  *   dA = dO W2[e]^T;  GeLU: dH = dA * GeLU'(H)
  *                     SwiGLU: dH1 = dA*H3*SiLU'(H1), dH3 = dA*SiLU(H1)

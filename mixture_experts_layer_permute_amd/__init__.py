@@ -12,6 +12,7 @@ from ._lib import (MOE_ACT_GELU, MOE_ACT_SWIGLU, MOE_BF16, MOE_F32,  # noqa: F40
                    MoEError, load)
 from .ops import (moe_combine, moe_combine_bwd, moe_expert_ffn_bwd,  # noqa: F401
                   moe_expert_ffn_fwd, moe_expert_ffn_fwd_gather,
+                  moe_expert_ffn_fwd_noalloc,
                   moe_expert_ffn_bwd_gather, moe_gate_topk, moe_gate_topk_bwd,
                   moe_permute, moe_unpermute_grad, moe_init,
                   moe_set_overlap)

@@ -28,6 +28,8 @@ SIGNATURES = {
     "moe_ffn_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
     "moe_expert_ffn_fwd": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P,
                                 _P, _P, _Z, _P]),
+    "moe_expert_ffn_fwd_noalloc": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P,
+                                        _P, _P, _P]),
     "moe_expert_ffn_bwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P,
                                 _P, _P, _P, _P, _P, _P, _Z, _P]),
     "moe_expert_ffn_bwd_accumulate": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,

@@ -236,7 +236,7 @@ const char* moe_status_string(moe_status s) {
     return "unknown status";
 }
 
-int moe_abi_version(void) { return 5; }
+int moe_abi_version(void) { return 6; }
 
 moe_status moe_set_overlap(int enable) {
     moe::g_overlap.store(enable != 0 ? 1 : 0, std::memory_order_relaxed);
@@ -248,6 +248,8 @@ moe_status moe_init(int device) {
     if (hipGetDevice(&cur) != hipSuccess) return MOE_ERR_HIP;
     if (device != cur && hipSetDevice(device) != hipSuccess) return MOE_ERR_HIP;
     int r = moe::device_cus();
+    // the no-alloc entry point's scratch address on this device
+    if (r >= 0) r = moe::ffn_scratch_init();
     if (device != cur) (void)hipSetDevice(cur);
     return r < 0 ? (moe_status)r : MOE_OK;
 }

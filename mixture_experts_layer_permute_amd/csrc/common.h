@@ -131,6 +131,10 @@ class SideStream {
 extern bool g_prof_on;
 void prof_mark(const char* name, hipStream_t s, int end);
 
+// Resolves the device address of the no-alloc FFN scratch array on the
+// current device (called by moe_init).
+moe_status ffn_scratch_init();
+
 inline moe_status launch_status() {
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;

@@ -30,9 +30,19 @@
 // and a partial-tile launch; independent launches may run on a side stream.
 // fp32 path (tiny fp32 workload): a plain LDS-tiled FMA kernel with the same
 // tile scheduler and epilogues.
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
+
+// Scratch of moe_expert_ffn_fwd_noalloc: the forward's tile plan (four int32
+// arrays of E+1 entries, 256-byte aligned; 17 KiB at E = 1024) in a
+// library-owned array, one copy per GPU, held until the process ends.  Host
+// code never passes `scratch` itself to a kernel (in host code the name is a
+// host-side stand-in): it uses the device address that hipGetSymbolAddress
+// returned for the current device.
+constexpr size_t kFfnScratchBytes = 32u << 10;
+static __device__ __align__(256) unsigned char scratch[kFfnScratchBytes];
 
 namespace moe {
 namespace {
@@ -1493,6 +1503,27 @@ moe_status ffn_bwd(const void* d_out, const void* x_perm, const void* h_save,
     return launch_status();
 }
 
+// Device address of `scratch` per device, resolved once per device with that
+// device current (moe_init, or the first no-alloc call on the device).
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices];
+
+moe_status scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+    if (dev < 0 || dev >= kScratchDevices) return MOE_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return MOE_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
 moe_status ffn_check(int R, int E, int d, int f, moe_act act, moe_dtype dt) {
     if (R < 0 || E < 1 || E > 1024 || d < 64 || f < 64) return MOE_ERR_INVALID_ARG;
     if (d % 64 != 0 || f % 64 != 0) return MOE_ERR_INVALID_ARG;
@@ -1502,6 +1533,13 @@ moe_status ffn_check(int R, int E, int d, int f, moe_act act, moe_dtype dt) {
 }
 
 }  // namespace
+
+// moe_init's set-up of this file: the scratch address of the current device.
+moe_status ffn_scratch_init() {
+    void* p = nullptr;
+    return scratch_address(&p);
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -1586,6 +1624,25 @@ moe_status moe_expert_ffn_bwd_accumulate(const void* d_out_perm, const void* x_p
                                true);
     return ffn_bwd<float>(d_out_perm, x_perm, h_save, a_save, offsets, R, E, d, f, act, W1,
                           W3, W2, dx_perm, dW1, dW3, dW2, ws, stream, nullptr, 0, true);
+}
+
+// moe_expert_ffn_fwd with its workspace (the tile plan) in the library's
+// static scratch array of the current device: no allocation, no workspace
+// argument.  Calls that overlap in time on one GPU share that array and race.
+moe_status moe_expert_ffn_fwd_noalloc(const void* x_perm, const int32_t* offsets, int R,
+                                      int E, int d, int f, moe_act act, moe_dtype dt,
+                                      const void* W1, const void* W3, const void* W2,
+                                      void* h_save, void* a_save, void* out_perm,
+                                      hipStream_t stream) {
+    moe_status st = ffn_check(R, E, d, f, act, dt);
+    if (st != MOE_OK) return st;
+    if (moe_ffn_workspace_bytes(R, E, d, f, act, dt, 0) > kFfnScratchBytes)
+        return MOE_ERR_WORKSPACE;
+    MOE_CHECK_DEVICE();
+    void* ws = nullptr;
+    if ((st = scratch_address(&ws)) != MOE_OK) return st;
+    return moe_expert_ffn_fwd(x_perm, offsets, R, E, d, f, act, dt, W1, W3, W2, h_save,
+                              a_save, out_perm, ws, kFfnScratchBytes, stream);
 }
 
 // The permute's row copy fused into the expert GEMMs: x is read in token

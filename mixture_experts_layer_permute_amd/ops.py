@@ -124,6 +124,28 @@ def moe_expert_ffn_fwd(x_perm, offsets, W1, W2, W3=None, act="gelu", out=None,
     return h_save, a_save, out_perm
 
 
+def moe_expert_ffn_fwd_noalloc(x_perm, offsets, W1, W2, W3=None, act="gelu", out=None):
+    """moe_expert_ffn_fwd with the library's static scratch instead of a
+    workspace.  -> (h_save, a_save [R,f], out_perm [R,d]); pass ``out`` to
+    allocate nothing at all."""
+    _need_gpu(x_perm, offsets, W1, W2, W3)
+    a = _act(act)
+    R, d = x_perm.shape
+    E, _, f = W1.shape
+    dev = x_perm.device
+    if out is None:
+        hw = 2 * f if a == MOE_ACT_SWIGLU else f
+        out = (torch.empty(R, hw, dtype=x_perm.dtype, device=dev),
+               torch.empty(R, f, dtype=x_perm.dtype, device=dev),
+               torch.empty(R, d, dtype=x_perm.dtype, device=dev))
+    h_save, a_save, out_perm = out
+    check(load().moe_expert_ffn_fwd_noalloc(_p(x_perm), _p(offsets), R, E, d, f, a,
+                                            _dt(x_perm), _p(W1), _p(W3), _p(W2),
+                                            _p(h_save), _p(a_save), _p(out_perm),
+                                            _stream(dev)), "moe_expert_ffn_fwd_noalloc")
+    return h_save, a_save, out_perm
+
+
 def moe_expert_ffn_bwd(d_out_perm, x_perm, h_save, a_save, offsets, W1, W2,
                        W3=None, act="gelu", out=None, ws=None):
     """-> (dx_perm [R,d], dW1 [E,d,f], dW3 or None, dW2 [E,f,d])."""

@@ -50,7 +50,7 @@ def test_binding_names_match_c_names():
 
 
 def test_status_strings_and_version(lib):
-    assert lib.moe_abi_version() == 5
+    assert lib.moe_abi_version() == 6
     for s in (0, -1, -2, -3, -4):
         assert lib.moe_status_string(s)
 
