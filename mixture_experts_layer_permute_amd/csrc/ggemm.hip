@@ -30,6 +30,7 @@
 // and a partial-tile launch; independent launches may run on a side stream.
 // fp32 path (tiny fp32 workload): a plain LDS-tiled FMA kernel with the same
 // tile scheduler and epilogues.
+#include <algorithm>
 #include <mutex>
 #include <type_traits>
 
@@ -74,6 +75,15 @@ struct GemmArgs {
     // segment's rows) is A[gather[r]].  A then has gather_rows rows.
     const int32_t* gather;
     long gather_rows;
+    // RAGGED_K work items (NULL: one item per expert, in `order`): x expert,
+    // y first row, z rows, w partial slot (-1: the item is the expert's
+    // whole segment and its tile is finished in the epilogue; >= 0: one
+    // chunk of a split segment, stored in fp32 at partial + w * partial_ld).
+    const int4* items;
+    const int32_t* item_count;
+    int item_max;        // host bound on the work items (grid size)
+    float* partial;
+    long partial_ld;
 };
 
 // ------------------------------------------------------------ epilogues
@@ -352,6 +362,7 @@ struct TileInfo {
     int m0, n0;     // RAGGED_K: tile origin in C_e; n0 also used by RAGGED_M
     long kbeg;      // RAGGED_K: first row of the segment
     int klen;       // reduction length
+    int pslot;      // RAGGED_K: partial slot of a split segment's chunk, or -1
     bool live;
 };
 
@@ -416,18 +427,30 @@ __device__ __forceinline__ TileInfo decode_tile(const GemmArgs<T>& p) {
         ti.m0 = 0;
         ti.kbeg = 0;
         ti.klen = p.K;
+        ti.pslot = -1;
     } else {
         const int per = p.nM * p.nN;
         const int es = L / per, rem = L % per;
-        ti.live = es < p.E;
-        if (!ti.live) return ti;
-        ti.e = p.order ? p.order[es] : es;
         ti.m0 = (rem % p.nM) * BM;
         ti.n0 = (rem / p.nM) * BN;
-        ti.kbeg = p.offsets[ti.e];
-        ti.klen = p.offsets[ti.e + 1] - p.offsets[ti.e];
         ti.r0 = 0;
         ti.rows = BM;
+        if (p.items) {
+            ti.live = es < *p.item_count;
+            if (!ti.live) return ti;
+            const int4 it = p.items[es];
+            ti.e = it.x;
+            ti.kbeg = it.y;
+            ti.klen = it.z;
+            ti.pslot = it.w;
+        } else {
+            ti.live = es < p.E;
+            if (!ti.live) return ti;
+            ti.e = p.order ? p.order[es] : es;
+            ti.kbeg = p.offsets[ti.e];
+            ti.klen = p.offsets[ti.e + 1] - p.offsets[ti.e];
+            ti.pslot = -1;
+        }
     }
     return ti;
 }
@@ -679,6 +702,112 @@ __device__ __forceinline__ void stage_barrier_ahead(int ahead) {
     }
 }
 
+// Epilogue of the bf16 kernels, through LDS: each wave stages its own 16-row
+// slabs of the accumulators in the ring (which every wave is done with), so
+// the waves only order their own LDS writes and reads: no block barriers.
+template <int BM, int BN, int WM, int WN, int NSTG, int STAGE, int MODE, bool DUAL, class Epi,
+          int FM, int FN, int FMD, int FND>
+__device__ __forceinline__ void bf16_epilogue(uint8_t* ringbuf, const TileInfo& ti,
+                                              const GemmArgs<bf16_t>& p, const Epi& epi,
+                                              const f32x16 (&acc)[FM][FN],
+                                              const f32x16 (&acc2)[FMD][FND]) {
+    constexpr int NT = 64 * WM * WN;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int NBT = DUAL ? 2 : 1;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int wm = wv / WN, wn = wv % WN;
+    constexpr int LDW = WTN + 4;
+    constexpr int SLAB = 16 * LDW;                   // floats per wave half-slab
+    constexpr int WPS = STAGE / (SLAB * NBT * 4);    // wave slabs per stage array
+    static_assert(WPS * NSTG >= NT / 64, "epilogue slabs do not fit");
+    uint8_t* home = ringbuf + (wv / WPS) * STAGE;
+    float* slab = reinterpret_cast<float*>(home) + (wv % WPS) * SLAB * NBT;
+    constexpr int LPR = WTN / 8;
+    constexpr int RPP = 64 / LPR;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int vv = 0; vv < 8; ++vv) {
+                    const int v = h * 8 + vv;
+                    const int r = (vv >> 2) * 8 + (lane >> 5) * 4 + (vv & 3);
+                    slab[r * LDW + j * 32 + (lane & 31)] = acc[i][j][v];
+                    if constexpr (DUAL)
+                        slab[SLAB + r * LDW + j * 32 + (lane & 31)] = acc2[i][j][v];
+                }
+            wave_lds_sync();
+            constexpr int NPS = 16 / RPP;                 // sub-passes of this slab
+            auto row_of = [&](int ps) { return wm * WTM + i * 32 + h * 16 + ps * RPP + lane / LPR; };
+            const int c0 = (lane % LPR) * 8;
+            const int col = ti.n0 + wn * WTN + c0;
+            auto ok_of = [&](int rl) {
+                return col < p.N && (MODE == RAGGED_M ? rl < ti.rows : ti.m0 + rl < p.M);
+            };
+            // a chunk of a split dW segment: its fp32 partial product, summed
+            // with the segment's other chunks (in order) by the reduce kernel
+            const bool split = MODE == RAGGED_K && ti.pslot >= 0;
+            auto to_partial = [&](int rl, const float* v) {
+                float* q = p.partial + (long)ti.pslot * p.partial_ld +
+                           ((long)ti.m0 + rl) * p.N + col;
+                *reinterpret_cast<float4*>(q) = *reinterpret_cast<const float4*>(v);
+                *reinterpret_cast<float4*>(q + 4) = *reinterpret_cast<const float4*>(v + 4);
+            };
+            if constexpr (Epi::kPre && !DUAL) {
+                // every read of this slab in flight before the first is used
+                auto grow = [&](int rl) {
+                    return MODE == RAGGED_M ? ti.r0 + rl : (long)ti.m0 + rl;
+                };
+                typename Epi::Pre pre[NPS];
+#pragma unroll
+                for (int ps = 0; ps < NPS; ++ps)
+                    if (!split && ok_of(row_of(ps)))
+                        pre[ps] = epi.pre8(ti.e, grow(row_of(ps)), col);
+#pragma unroll
+                for (int ps = 0; ps < NPS; ++ps) {
+                    const int rl = row_of(ps);
+                    const float* src = &slab[(ps * RPP + lane / LPR) * LDW + c0];
+                    float v[8];
+                    *reinterpret_cast<float4*>(v) = *reinterpret_cast<const float4*>(src);
+                    *reinterpret_cast<float4*>(v + 4) = *reinterpret_cast<const float4*>(src + 4);
+                    if (ok_of(rl)) {
+                        if (split) to_partial(rl, v);
+                        else epi.vec8p(ti.e, grow(rl), col, v, pre[ps]);
+                    }
+                }
+            } else {
+#pragma unroll 1
+                for (int ps = 0; ps < NPS; ++ps) {
+                    const int rl = row_of(ps);
+                    const float* src = &slab[(ps * RPP + lane / LPR) * LDW + c0];
+                    float v[8];
+                    *reinterpret_cast<float4*>(v) = *reinterpret_cast<const float4*>(src);
+                    *reinterpret_cast<float4*>(v + 4) = *reinterpret_cast<const float4*>(src + 4);
+                    if (ok_of(rl)) {
+                        if constexpr (DUAL) {
+                            float v3[8];
+                            *reinterpret_cast<float4*>(v3) =
+                                *reinterpret_cast<const float4*>(src + SLAB);
+                            *reinterpret_cast<float4*>(v3 + 4) =
+                                *reinterpret_cast<const float4*>(src + SLAB + 4);
+                            epi.vec8(ti.e, ti.r0 + rl, col, v, v3);
+                        } else if (MODE == RAGGED_M) {
+                            epi.vec8(ti.e, ti.r0 + rl, col, v);
+                        } else if (split) {
+                            to_partial(rl, v);
+                        } else {
+                            epi.vec8(ti.e, (long)ti.m0 + rl, col, v);
+                        }
+                    }
+                }
+            }
+            wave_lds_sync();
+        }
+    }
+}
+
 template <int BM, int BN, int WM, int WN, int NSTG, int BK, int MODE, int ALAY, int BLAY,
           bool DUAL, bool KSPLIT, bool GATHER, class Epi>
 __global__ __launch_bounds__(64 * WM * WN, 2) void ggemm_bf16_dma_kernel(GemmArgs<bf16_t> p,
@@ -886,85 +1015,7 @@ __global__ __launch_bounds__(64 * WM * WN, 2) void ggemm_bf16_dma_kernel(GemmArg
         mfmas((KS - 1) & 1);
     }
     __syncthreads();
-
-    // ---- epilogue through LDS.  Each wave stages its own 16-row slabs, so
-    // after the barrier above (every wave is done with the ring) the waves
-    // only order their own LDS writes and reads: no block barriers.
-    constexpr int LDW = WTN + 4;
-    constexpr int SLAB = 16 * LDW;                   // floats per wave half-slab
-    constexpr int WPS = STAGE / (SLAB * NBT * 4);    // wave slabs per stage array
-    static_assert(WPS * NSTG >= NT / 64, "epilogue slabs do not fit");
-    uint8_t* home = ring(wv / WPS);
-    float* slab = reinterpret_cast<float*>(home) + (wv % WPS) * SLAB * NBT;
-    constexpr int LPR = WTN / 8;
-    constexpr int RPP = 64 / LPR;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-                for (int vv = 0; vv < 8; ++vv) {
-                    const int v = h * 8 + vv;
-                    const int r = (vv >> 2) * 8 + (lane >> 5) * 4 + (vv & 3);
-                    slab[r * LDW + j * 32 + (lane & 31)] = acc[i][j][v];
-                    if constexpr (DUAL)
-                        slab[SLAB + r * LDW + j * 32 + (lane & 31)] = acc2[i][j][v];
-                }
-            wave_lds_sync();
-            constexpr int NPS = 16 / RPP;                 // sub-passes of this slab
-            auto row_of = [&](int ps) { return wm * WTM + i * 32 + h * 16 + ps * RPP + lane / LPR; };
-            const int c0 = (lane % LPR) * 8;
-            const int col = ti.n0 + wn * WTN + c0;
-            auto ok_of = [&](int rl) {
-                return col < p.N && (MODE == RAGGED_M ? rl < ti.rows : ti.m0 + rl < p.M);
-            };
-            if constexpr (Epi::kPre && !DUAL) {
-                // every read of this slab in flight before the first is used
-                auto grow = [&](int rl) {
-                    return MODE == RAGGED_M ? ti.r0 + rl : (long)ti.m0 + rl;
-                };
-                typename Epi::Pre pre[NPS];
-#pragma unroll
-                for (int ps = 0; ps < NPS; ++ps)
-                    if (ok_of(row_of(ps))) pre[ps] = epi.pre8(ti.e, grow(row_of(ps)), col);
-#pragma unroll
-                for (int ps = 0; ps < NPS; ++ps) {
-                    const int rl = row_of(ps);
-                    const float* src = &slab[(ps * RPP + lane / LPR) * LDW + c0];
-                    float v[8];
-                    *reinterpret_cast<float4*>(v) = *reinterpret_cast<const float4*>(src);
-                    *reinterpret_cast<float4*>(v + 4) = *reinterpret_cast<const float4*>(src + 4);
-                    if (ok_of(rl)) epi.vec8p(ti.e, grow(rl), col, v, pre[ps]);
-                }
-            } else {
-#pragma unroll 1
-                for (int ps = 0; ps < NPS; ++ps) {
-                    const int rl = row_of(ps);
-                    const float* src = &slab[(ps * RPP + lane / LPR) * LDW + c0];
-                    float v[8];
-                    *reinterpret_cast<float4*>(v) = *reinterpret_cast<const float4*>(src);
-                    *reinterpret_cast<float4*>(v + 4) = *reinterpret_cast<const float4*>(src + 4);
-                    if (ok_of(rl)) {
-                        if constexpr (DUAL) {
-                            float v3[8];
-                            *reinterpret_cast<float4*>(v3) =
-                                *reinterpret_cast<const float4*>(src + SLAB);
-                            *reinterpret_cast<float4*>(v3 + 4) =
-                                *reinterpret_cast<const float4*>(src + SLAB + 4);
-                            epi.vec8(ti.e, ti.r0 + rl, col, v, v3);
-                        } else if (MODE == RAGGED_M) {
-                            epi.vec8(ti.e, ti.r0 + rl, col, v);
-                        } else {
-                            epi.vec8(ti.e, (long)ti.m0 + rl, col, v);
-                        }
-                    }
-                }
-            }
-            wave_lds_sync();
-        }
-    }
+    bf16_epilogue<BM, BN, WM, WN, NSTG, STAGE, MODE, DUAL>(ringbuf, ti, p, epi, acc, acc2);
 }
 
 // =====================================================================
@@ -1074,13 +1125,60 @@ __global__ __launch_bounds__(256) void ggemm_f32_kernel(GemmArgs<float> p, Epi e
 // planner: per-expert M-tile prefix and heaviest-first expert order
 // =====================================================================
 
+// Split of a weight-gradient segment (RAGGED_K) over its rows.  An expert
+// whose dW tiles are fewer than the compute units cannot fill the GPU, and
+// with a long segment its tiles set the whole product's critical path (one
+// expert with 39% of the rows, 64 tiles on 256 compute units).  Such a
+// segment (more than 2 * kSplitRows rows, fewer than kSplitTiles tiles) is
+// cut into chunks of kc = max(kSplitRows, rows / kSplitChunks rounded up to
+// 256) rows; each chunk's tiles store fp32 partial products and the reduce
+// kernel sums them in chunk order, so the split depends only on the
+// segment's length and the matrix shape and the sum order is fixed.
+constexpr int kSplitRows = 4096;
+constexpr int kSplitChunks = 64;
+constexpr int kSplitTiles = 256;
+
+__host__ __device__ inline int split_chunk_rows(int n) {
+    const int per = (n + kSplitChunks - 1) / kSplitChunks;
+    const int kc = (per + 255) / 256 * 256;
+    return kc > kSplitRows ? kc : kSplitRows;
+}
+
+// Bounds on the split plan of a product with R rows over E experts and
+// dw_tiles tiles per expert: partial slots (chunks of split segments) and
+// split segments.  A split segment has n > 2 kSplitRows rows and
+// ceil(n / kc) <= n / kSplitRows + 1 < 1.5 n / kSplitRows chunks.
+struct SplitBound {
+    long slots, splits;
+};
+inline SplitBound split_bound(long R, int E, int dw_tiles) {
+    if (dw_tiles >= kSplitTiles) return {0, 0};
+    const long splits = std::min<long>(E, R / (2L * kSplitRows + 1));
+    const long slots = std::min<long>((long)kSplitChunks * splits, 3 * R / (2L * kSplitRows) + 1);
+    return {splits > 0 ? slots : 0, splits};
+}
+
+// The tile plan of a call, from the segment offsets (one workgroup):
+//  tile_prefix[e] RAGGED_M row tiles of the experts before e (plus the total)
+//  full_prefix[e] the same for full 256-row tiles; part_list the experts with
+//                 a partial last tile (count at [E])
+//  order          experts by row count, heaviest first (ties: lower index)
+//  items          (dw_tiles > 0) the RAGGED_K work items in dealing order:
+//                 the chunks of split segments (heaviest expert first), then
+//                 the whole segments of the other experts in `order`;
+//                 counts[0] = items, counts[1] = split segments, whose
+//                 (expert, first slot, chunks) are listed in splits
 __global__ __launch_bounds__(1024) void ffn_plan_kernel(const int32_t* __restrict__ offsets,
-                                                        int E, int bm,
+                                                        int E, int bm, int dw_tiles,
                                                         int32_t* __restrict__ tile_prefix,
                                                         int32_t* __restrict__ order,
                                                         int32_t* __restrict__ full_prefix,
-                                                        int32_t* __restrict__ part_list) {
+                                                        int32_t* __restrict__ part_list,
+                                                        int4* __restrict__ items,
+                                                        int4* __restrict__ splits,
+                                                        int32_t* __restrict__ counts) {
     __shared__ int cnt[1024];
+    __shared__ int ord[1024];
     const int e = threadIdx.x;
     if (e < E) cnt[e] = offsets[e + 1] - offsets[e];
     __syncthreads();
@@ -1105,6 +1203,68 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(const int32_t* __restric
             rank += (cq > c) || (cq == c && q < e);
         }
         order[rank] = e;
+        ord[rank] = e;
+    }
+    __syncthreads();
+    if (items && e == 0) {
+        int ni = 0, ns = 0, slot = 0;
+        const bool may_split = dw_tiles < kSplitTiles;
+        for (int r = 0; r < E; ++r) {               // split segments, heaviest first
+            const int q = ord[r], n = cnt[q];
+            if (!may_split || n <= 2 * kSplitRows) break;   // the rest are shorter
+            const int kc = split_chunk_rows(n);
+            const int nc = (n + kc - 1) / kc;
+            for (int c = 0; c < nc; ++c)
+                items[ni++] = make_int4(q, offsets[q] + c * kc, min(kc, n - c * kc), slot + c);
+            splits[ns++] = make_int4(q, slot, nc, 0);
+            slot += nc;
+        }
+        for (int r = ns; r < E; ++r) {              // whole segments
+            const int q = ord[r];
+            items[ni++] = make_int4(q, offsets[q], cnt[q], -1);
+        }
+        counts[0] = ni;
+        counts[1] = ns;
+    }
+}
+
+// C_e (+)= the sum of a split segment's fp32 chunk products, in chunk order
+// (after the old value when accumulating), rounded once.  Block row j is the
+// j-th split segment; each thread finishes 8 consecutive elements of C_e.
+template <typename T>
+__global__ __launch_bounds__(256) void dw_split_reduce_kernel(
+    const int4* __restrict__ splits, const int32_t* __restrict__ counts,
+    const float* __restrict__ partial, long mn, T* __restrict__ C, long cstride,
+    int accumulate) {
+    const int j = blockIdx.y;
+    if (j >= counts[1]) return;
+    const long i0 = ((long)blockIdx.x * 256 + threadIdx.x) * 8;
+    if (i0 >= mn) return;
+    const int4 sp = splits[j];                      // expert, first slot, chunks
+    T* c = C + (long)sp.x * cstride + i0;
+    float acc[8];
+    if (accumulate) {
+        if constexpr (sizeof(T) == 2) {
+            Vec16<T>::ld(c, acc);
+        } else {
+            Vec16<T>::ld(c, acc);
+            Vec16<T>::ld(c + 4, acc + 4);
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+    }
+    for (int k = 0; k < sp.z; ++k) {
+        const float4* q = reinterpret_cast<const float4*>(partial + (long)(sp.y + k) * mn + i0);
+        const float4 a = q[0], b = q[1];
+        acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+        acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+    }
+    if constexpr (sizeof(T) == 2) {
+        Vec16<T>::st(c, acc);
+    } else {
+        Vec16<T>::st(c, acc);
+        Vec16<T>::st(c + 4, acc + 4);
     }
 }
 
@@ -1112,11 +1272,18 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(const int32_t* __restric
 
 constexpr int BM_BF16 = 256;
 
+// Workspace of an FFN call: the tile plan (forward and backward), then, for
+// the backward, dH and (bf16) the split plan of the dW products: work items,
+// split segments, their counts, and two fp32 partial regions (dW2 may run on
+// the side stream while dW1 / dW3 run on the caller's stream).
 struct FfnWs {
-    size_t prefix, order, full, part, dh, total;
+    size_t prefix, order, full, part, dh, items, splits, counts, part0, part1, total;
+    long item_max, split_max, slot_max;
 };
 
-FfnWs ffn_layout(int R, int E, int f, moe_act act, moe_dtype dt, int backward) {
+inline int dw_tiles_of(int d, int f) { return cdiv(d, 256) * cdiv(f, 256); }
+
+FfnWs ffn_layout(int R, int E, int d, int f, moe_act act, moe_dtype dt, int backward) {
     FfnWs w;
     w.prefix = 0;
     w.order = align_up(sizeof(int32_t) * (E + 1), 256);
@@ -1124,11 +1291,24 @@ FfnWs ffn_layout(int R, int E, int f, moe_act act, moe_dtype dt, int backward) {
     w.part = align_up(w.full + sizeof(int32_t) * (E + 1), 256);
     w.dh = align_up(w.part + sizeof(int32_t) * (E + 1), 256);
     size_t dh = 0;
+    w.item_max = w.split_max = w.slot_max = 0;
     if (backward) {
         const size_t es = dt == MOE_BF16 ? 2 : 4;
         dh = es * (size_t)R * f * (act == MOE_ACT_SWIGLU ? 2 : 1);
     }
-    w.total = align_up(w.dh + dh, 256);
+    w.items = align_up(w.dh + dh, 256);
+    if (backward && dt == MOE_BF16) {
+        const SplitBound sb = split_bound(R, E, dw_tiles_of(d, f));
+        w.slot_max = sb.slots;
+        w.split_max = sb.splits;
+        w.item_max = E + sb.slots;
+    }
+    w.splits = align_up(w.items + sizeof(int4) * w.item_max, 256);
+    w.counts = align_up(w.splits + sizeof(int4) * w.split_max, 256);
+    const size_t region = sizeof(float) * (size_t)w.slot_max * d * f;
+    w.part0 = align_up(w.counts + (w.item_max ? 2 * sizeof(int32_t) : 0), 256);
+    w.part1 = align_up(w.part0 + region, 256);
+    w.total = align_up(w.part1 + region, 256);
     return w;
 }
 
@@ -1146,7 +1326,7 @@ void launch_bf16(GemmArgs<bf16_t> p, Epi epi, int R, hipStream_t s, const char* 
         blocks = rt * p.nN;
     } else {
         p.nM = (p.M + BM - 1) / BM;
-        blocks = p.E * p.nM * p.nN;
+        blocks = (p.items ? p.item_max : p.E) * p.nM * p.nN;
     }
     if (blocks <= 0) return;
     if (p.xcd_run <= 0) p.xcd_run = MODE == RAGGED_M ? 32 : 8;
@@ -1200,6 +1380,11 @@ GemmArgs<T> base_args(const int32_t* offsets, const Plan& pl, int E) {
     p.xcd_run = 0;
     p.gather = nullptr;
     p.gather_rows = 0;
+    p.items = nullptr;
+    p.item_count = nullptr;
+    p.item_max = 0;
+    p.partial = nullptr;
+    p.partial_ld = 0;
     return p;
 }
 
@@ -1268,6 +1453,11 @@ struct Launch<bf16_t, Cfg> {
             // Split only when the product is a few rounds of workgroups:
             // with many rounds the one partially filled last round is a
             // small share, and the narrow slices cost more than they save.
+            // (Also with many small experts: on the 64-expert workload, where
+            // a fifth of the row tiles are an expert's mostly empty last
+            // tile, splitting the up and dA products made them 9% slower --
+            // a 64-row slice with one wave per SIMD runs its reduction at
+            // the same per-stage latency as a full tile.)
             const long tiles = (long)(cdiv(R, Cfg::BM) + E / 2) * cdiv(N, Cfg::BN);
             return tiles < (long)kSplitRounds * device_cus();
         }
@@ -1345,7 +1535,7 @@ moe_status ffn_fwd(const void* x_perm, const int32_t* offsets, int R, int E,
                    void* ws, hipStream_t s, const int32_t* gather = nullptr, long T_src = 0) {
     // gather != NULL: x_perm is the token-order input [T_src,d] and permuted row
     // r is its row gather[r] (the permute's row copy fused into GEMM1)
-    const FfnWs L = ffn_layout(R, E, f, act, MOE_F32, 0);
+    const FfnWs L = ffn_layout(R, E, d, f, act, sizeof(T) == 2 ? MOE_BF16 : MOE_F32, 0);
     char* base = static_cast<char*>(ws);
     int32_t* prefix = reinterpret_cast<int32_t*>(base + L.prefix);
     int32_t* order = reinterpret_cast<int32_t*>(base + L.order);
@@ -1353,8 +1543,9 @@ moe_status ffn_fwd(const void* x_perm, const int32_t* offsets, int R, int E,
     int32_t* part = reinterpret_cast<int32_t*>(base + L.part);
     const Plan pl{prefix, order, full, part};
     MOE_LAUNCH("ffn_plan", s,
-               ffn_plan_kernel<<<1, 1024, 0, s>>>(offsets, E, Launch<T, Cfg>::BM, prefix,
-                                                  order, full, part));
+               ffn_plan_kernel<<<1, 1024, 0, s>>>(offsets, E, Launch<T, Cfg>::BM, 0, prefix,
+                                                  order, full, part, nullptr, nullptr,
+                                                  nullptr));
 
     const T* xp = static_cast<const T*>(x_perm);
     T* H = static_cast<T*>(h_save);
@@ -1401,7 +1592,7 @@ moe_status ffn_bwd(const void* d_out, const void* x_perm, const void* h_save,
     // accumulate: dW1/dW2/dW3 += the products (fp32 sum, one rounding)
     // gather != NULL: x_perm is the token-order input [T_src,d]; dW1/dW3 read
     // permuted row r as its row gather[r]
-    const FfnWs L = ffn_layout(R, E, f, act, MOE_F32, 1);
+    const FfnWs L = ffn_layout(R, E, d, f, act, sizeof(T) == 2 ? MOE_BF16 : MOE_F32, 1);
     char* base = static_cast<char*>(ws);
     int32_t* prefix = reinterpret_cast<int32_t*>(base + L.prefix);
     int32_t* order = reinterpret_cast<int32_t*>(base + L.order);
@@ -1411,9 +1602,33 @@ moe_status ffn_bwd(const void* d_out, const void* x_perm, const void* h_save,
     T* dH = reinterpret_cast<T*>(base + L.dh);
     const bool sw = act == MOE_ACT_SWIGLU;
     const long ldh = sw ? 2L * f : (long)f;
+    // dW work items (bf16): whole segments and the chunks of split ones
+    int4* items = L.item_max ? reinterpret_cast<int4*>(base + L.items) : nullptr;
+    int4* splits = reinterpret_cast<int4*>(base + L.splits);
+    int32_t* counts = reinterpret_cast<int32_t*>(base + L.counts);
     MOE_LAUNCH("ffn_plan", s,
-               ffn_plan_kernel<<<1, 1024, 0, s>>>(offsets, E, Launch<T, Cfg>::BM, prefix,
-                                                  order, full, part));
+               ffn_plan_kernel<<<1, 1024, 0, s>>>(offsets, E, Launch<T, Cfg>::BM,
+                                                  dw_tiles_of(d, f), prefix, order, full,
+                                                  part, items, splits, counts));
+    // a dW product over the work items; part: its fp32 partial region
+    auto with_items = [&](GemmArgs<T>& p, size_t part_off) {
+        if (!items) return;
+        p.items = items;
+        p.item_count = counts;
+        p.item_max = (int)L.item_max;
+        p.partial = reinterpret_cast<float*>(base + part_off);
+        p.partial_ld = (long)d * f;
+    };
+    // the split segments' dW: their chunks summed in order, into C (+=)
+    auto reduce_splits = [&](void* C, size_t part_off, hipStream_t st, const char* name) {
+        if (!items || L.split_max == 0) return;
+        const long mn = (long)d * f;
+        const dim3 grid((unsigned)cdiv(mn, 256 * 8), (unsigned)L.split_max);
+        MOE_LAUNCH(name, st,
+                   dw_split_reduce_kernel<T><<<grid, 256, 0, st>>>(
+                       splits, counts, reinterpret_cast<const float*>(base + part_off), mn,
+                       static_cast<T*>(C), mn, accumulate ? 1 : 0));
+    };
 
     const T* dO = static_cast<const T*>(d_out);
     // Caller's stream: dA (full tiles) -> dX (full tiles) -> dW1, dW3.
@@ -1445,12 +1660,14 @@ moe_status ffn_bwd(const void* d_out, const void* x_perm, const void* h_save,
         GemmArgs<T> p = base_args<T>(offsets, pl, E);
         p.A = static_cast<const T*>(a_save); p.lda = f; p.M = f;
         p.B = dO; p.ldb = d; p.N = d;
+        with_items(p, L.part0);
         if (accumulate)
             Launch<T, Cfg>::template go<RAGGED_K, MNMAJ, MNMAJ, false, false>(
                 p, EpiAcc<T>{static_cast<T*>(dW2), d, (long)f * d}, R, ts, "gemm_dW2");
         else
             Launch<T, Cfg>::template go<RAGGED_K, MNMAJ, MNMAJ, false, false>(
                 p, EpiStore<T>{static_cast<T*>(dW2), d, (long)f * d}, R, ts, "gemm_dW2");
+        reduce_splits(dW2, L.part0, ts, "dw_split_reduce");
     }
     // dX = dH1 W1[e]^T (+ dH3 W3[e]^T)   [R, d]
     const bool dX_split = Launch<T, Cfg>::template splits<RAGGED_M, false>(R, E, d);
@@ -1485,6 +1702,7 @@ moe_status ffn_bwd(const void* d_out, const void* x_perm, const void* h_save,
         p.A = static_cast<const T*>(x_perm); p.lda = d; p.M = d;
         p.gather = gather; p.gather_rows = T_src;
         p.B = dH; p.ldb = ldh; p.N = f;
+        with_items(p, L.part1);
         auto dw = [&](void* C, const char* name) {
             if (accumulate)
                 Launch<T, Cfg>::template go<RAGGED_K, MNMAJ, MNMAJ, false, false, true>(
@@ -1492,6 +1710,7 @@ moe_status ffn_bwd(const void* d_out, const void* x_perm, const void* h_save,
             else
                 Launch<T, Cfg>::template go<RAGGED_K, MNMAJ, MNMAJ, false, false, true>(
                     p, EpiStore<T>{static_cast<T*>(C), f, (long)d * f}, R, s, name);
+            reduce_splits(C, L.part1, s, "dw_split_reduce");
         };
         dw(dW1, "gemm_dW1");
         if (sw) {
@@ -1549,7 +1768,7 @@ extern "C" {
 size_t moe_ffn_workspace_bytes(int R, int E, int d, int f, moe_act act,
                                moe_dtype dt, int backward) {
     if (ffn_check(R, E, d, f, act, dt) != MOE_OK) return 0;
-    return ffn_layout(R, E, f, act, dt, backward).total;
+    return ffn_layout(R, E, d, f, act, dt, backward).total;
 }
 
 moe_status moe_expert_ffn_fwd(const void* x_perm, const int32_t* offsets,

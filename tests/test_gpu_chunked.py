@@ -97,16 +97,17 @@ def test_chunking_bounds_the_activation_memory():
     assert peaks[1] < 0.5 * peaks[0], peaks
 
 
+@pytest.mark.parametrize("counts", [[300, 0, 17, 513, 64], [9000, 0, 20000, 64]])
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 @pytest.mark.parametrize("act", ["gelu", "swiglu"])
-def test_accumulate_entry_point_and_gemm1_only(act, dt):
+def test_accumulate_entry_point_and_gemm1_only(act, dt, counts):
     """moe_expert_ffn_bwd_accumulate adds to what dW holds (old + new in fp32,
-    one rounding); R = 0 leaves dW untouched; moe_expert_ffn_fwd with out_perm
-    = NULL writes the same saved state as the full call."""
+    one rounding; a segment split over its rows adds its chunks after the old
+    value); R = 0 leaves dW untouched; moe_expert_ffn_fwd with out_perm =
+    NULL writes the same saved state as the full call."""
     from moe_inputs import stage
     from _gpu import dev, dev_i32
-    banner("accumulate", act, dt)
-    counts = [300, 0, 17, 513, 64]
+    banner("accumulate", act, dt, counts)
     E, d, f = len(counts), 128, 192
     offsets = stage.counts_to_offsets(counts)
     R = int(offsets[-1])

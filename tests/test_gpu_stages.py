@@ -98,6 +98,9 @@ FFN_CASES = [  # counts per expert, d, f
     # than one row-tile group, and one expert with 8 full tiles + 130 rows
     ([64, 63, 65, 192, 257, 511, 320, 0, 1, 700, 130, 5], 128, 256),
     ([2178], 64, 128),
+    # dW split over rows: two experts above 8192 rows with one dW tile each
+    # (chunks of 4096 rows, fp32 partials summed in order), beside short ones
+    ([9000, 5, 20000, 0, 300], 128, 256),
 ]
 
 
