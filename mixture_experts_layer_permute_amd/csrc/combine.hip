@@ -6,6 +6,8 @@
 // kernel here is a gather keyed by dest[t,j] (one wave per token, 16-byte
 // lanes), so no two lanes ever write the same element and nothing depends on
 // the order of atomics: results are bit-identical run to run.
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
@@ -13,8 +15,9 @@ namespace {
 
 constexpr int U = 2;   // 16-byte vectors per lane in flight per slot
 
-// y[t] = sum_j w[t,j] * out_perm[dest[t,j]], fp32 in slot order.
-template <typename T>
+// y[t] = sum_j w[t,j] * out_perm[dest[t,j]], fp32 in slot order.  NT: the
+// rows bypass the caches (out_perm larger than the MALL).
+template <typename T, bool NT>
 __global__ __launch_bounds__(256) void combine_kernel(
     const T* __restrict__ out_perm, const int32_t* __restrict__ dest,
     const float* __restrict__ w, int Tn, int k, int d, T* __restrict__ y) {
@@ -40,7 +43,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
                 const int v = v0 + u * 64 + lane;
                 if (v < nvec) {
                     float o[V];
-                    Vec16<T>::ld(row + (long)v * V, o);
+                    Vec16s<T, NT>::ld(row + (long)v * V, o);
 #pragma unroll
                     for (int q = 0; q < V; ++q) acc[u][q] = fmaf(wj, o[q], acc[u][q]);
                 }
@@ -49,7 +52,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int v = v0 + u * 64 + lane;
-            if (v < nvec) Vec16<T>::st(y + t * d + (long)v * V, acc[u]);
+            if (v < nvec) Vec16s<T, NT>::st(y + t * d + (long)v * V, acc[u]);
         }
     }
 }
@@ -105,8 +108,9 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
     }
 }
 
-// dx[t] (+)= sum_j dx_perm[dest[t,j]], fp32 in slot order.
-template <typename T>
+// dx[t] (+)= sum_j dx_perm[dest[t,j]], fp32 in slot order.  NT: the rows
+// bypass the caches (dx_perm larger than the MALL).
+template <typename T, bool NT>
 __global__ __launch_bounds__(256) void unpermute_grad_kernel(
     const T* __restrict__ dxp, const int32_t* __restrict__ dest, int Tn, int k,
     int d, int accumulate, T* __restrict__ dx) {
@@ -142,7 +146,7 @@ __global__ __launch_bounds__(256) void unpermute_grad_kernel(
                 const int v = v0 + u * 64 + lane;
                 if (v < nvec) {
                     float o[V];
-                    Vec16<T>::ld(row + (long)v * V, o);
+                    Vec16s<T, NT>::ld(row + (long)v * V, o);
 #pragma unroll
                     for (int q = 0; q < V; ++q) sum[u][q] += o[q];
                 }
@@ -154,7 +158,7 @@ __global__ __launch_bounds__(256) void unpermute_grad_kernel(
             if (v < nvec) {
 #pragma unroll
                 for (int q = 0; q < V; ++q) acc[u][q] += sum[u][q];
-                Vec16<T>::st(dx + t * d + (long)v * V, acc[u]);
+                Vec16s<T, NT>::st(dx + t * d + (long)v * V, acc[u]);
             }
         }
     }
@@ -180,16 +184,18 @@ moe_status moe_combine(const void* out_perm, const int32_t* dest,
     MOE_CHECK_ARG(out_perm && dest && topk_w && y);
     MOE_CHECK_ARG(aligned16(out_perm) && aligned16(y));
     MOE_CHECK_DEVICE();
-    if (dt == MOE_BF16)
+    const bool nt = (long)T * k * d * (dt == MOE_BF16 ? 2 : 4) > kMallBytes;
+    auto go = [&](auto tag, auto ntc) {
+        using E = decltype(tag);
         MOE_LAUNCH("combine", stream,
-            combine_kernel<bf16_t><<<cdiv(T, 4), 256, 0, stream>>>(
-                static_cast<const bf16_t*>(out_perm), dest, topk_w, T, k, d,
-                static_cast<bf16_t*>(y)));
-    else
-        MOE_LAUNCH("combine", stream,
-            combine_kernel<float><<<cdiv(T, 4), 256, 0, stream>>>(
-                static_cast<const float*>(out_perm), dest, topk_w, T, k, d,
-                static_cast<float*>(y)));
+            (combine_kernel<E, decltype(ntc)::value><<<cdiv(T, 4), 256, 0, stream>>>(
+                static_cast<const E*>(out_perm), dest, topk_w, T, k, d, static_cast<E*>(y))));
+    };
+    if (dt == MOE_BF16) {
+        if (nt) go(bf16_t{}, std::true_type{}); else go(bf16_t{}, std::false_type{});
+    } else {
+        if (nt) go(float{}, std::true_type{}); else go(float{}, std::false_type{});
+    }
     return launch_status();
 }
 
@@ -225,16 +231,19 @@ moe_status moe_unpermute_grad(const void* dx_perm, const int32_t* dest, int T,
     MOE_CHECK_ARG(dx_perm && dest && dx);
     MOE_CHECK_ARG(aligned16(dx_perm) && aligned16(dx));
     MOE_CHECK_DEVICE();
-    if (dt == MOE_BF16)
+    const bool nt = (long)T * k * d * (dt == MOE_BF16 ? 2 : 4) > kMallBytes;
+    auto go = [&](auto tag, auto ntc) {
+        using E = decltype(tag);
         MOE_LAUNCH("unpermute_grad", stream,
-            unpermute_grad_kernel<bf16_t><<<cdiv(T, 4), 256, 0, stream>>>(
-                static_cast<const bf16_t*>(dx_perm), dest, T, k, d, accumulate,
-                static_cast<bf16_t*>(dx)));
-    else
-        MOE_LAUNCH("unpermute_grad", stream,
-            unpermute_grad_kernel<float><<<cdiv(T, 4), 256, 0, stream>>>(
-                static_cast<const float*>(dx_perm), dest, T, k, d, accumulate,
-                static_cast<float*>(dx)));
+            (unpermute_grad_kernel<E, decltype(ntc)::value><<<cdiv(T, 4), 256, 0, stream>>>(
+                static_cast<const E*>(dx_perm), dest, T, k, d, accumulate,
+                static_cast<E*>(dx))));
+    };
+    if (dt == MOE_BF16) {
+        if (nt) go(bf16_t{}, std::true_type{}); else go(bf16_t{}, std::false_type{});
+    } else {
+        if (nt) go(float{}, std::true_type{}); else go(float{}, std::false_type{});
+    }
     return launch_status();
 }
 
