@@ -34,9 +34,24 @@ PEAK_HBM_GBS = 8000.0
 # cold source in the same run (the summaries under profiles/ give commands
 # and factors).  Valid only for the kernel sources whose SHA-256 prefix is
 # TRAFFIC_SRC; null once they change.
-TRAFFIC_SRC = ""
+TRAFFIC_SRC = "26f590441f7b8b88"
 TRAFFIC_SOURCES = ("ggemm.hip", "common.h", "permute.hip", "combine.hip")
-TRAFFIC = {}
+TRAFFIC = {
+    # profiles/hbm_traffic_long_ctx_swiglu.md (fetch x 4.0, write x 2.0)
+    "long_ctx_swiglu": {
+        "perm_copy": 9672130961,
+        "gemm_up_swiglu": 680818343110,
+        "gemm_down": 230782054174,
+        "combine": 9680264046,
+        "combine_bwd": 18275468947,
+        "gemm_dA_swiglu": 429276980978,
+        "gemm_dW2": 379100553070,
+        "gemm_dW1": 379100553070,
+        "gemm_dW3": 379100553070,
+        "gemm_dX": 494575969609,
+        "unpermute_grad": 10745592667,
+    },
+}
 
 
 def source_hash():
