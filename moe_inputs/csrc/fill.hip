@@ -4,9 +4,10 @@
 // the NumPy version, so host and device produce identical bits.
 //
 // SplitMix64 (Steele, Lea, Flood, OOPSLA 2014): state = key + (c+1)*gamma,
-// output = finaliser(state).  The 64 output bits are cut into four 16-bit
-// integers; D = h0+h1+h2+h3 + 2 - 131072 is exact, z = fl32(fl32(D) * C0) *
-// scale with C0 = fl32(sqrt(3)/65536).
+// output = finaliser(state).  Element c takes the outputs at counters 3c,
+// 3c+1, 3c+2, each cut into four 16-bit integers; D = sum of the twelve + 6 -
+// 393216 is exact, z = fl32(D) * 2^-16 (exact: twelve uniforms minus 6),
+// value = fl32(z * scale).
 //
 // Test infrastructure (input generation); holds none of the MoE layer's
 // arithmetic.
@@ -23,11 +24,15 @@ __device__ __forceinline__ uint64_t splitmix64_at(uint64_t key, uint64_t c) {
 }
 
 __device__ __forceinline__ float deviate(uint64_t key, uint64_t c, float scale) {
-    const uint64_t h = splitmix64_at(key, c);
-    const int s = (int)(h & 0xFFFFu) + (int)((h >> 16) & 0xFFFFu) +
-                  (int)((h >> 32) & 0xFFFFu) + (int)(h >> 48);
-    const int dd = s + 2 - 131072;
-    const float z = (float)dd * __uint_as_float(0x37DDB3D7u);
+    int s = 0;
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+        const uint64_t h = splitmix64_at(key, 3 * c + q);
+        s += (int)(h & 0xFFFFu) + (int)((h >> 16) & 0xFFFFu) +
+             (int)((h >> 32) & 0xFFFFu) + (int)(h >> 48);
+    }
+    const int dd = s + 6 - 393216;
+    const float z = (float)dd * (1.0f / 65536.0f);
     return z * scale;
 }
 

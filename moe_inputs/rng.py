@@ -14,18 +14,20 @@ Definition (both sides implement exactly this):
   xor-shift 27, mul 0x94D049BB133111EB, xor-shift 31), all mod 2^64.
 * stream key of (seed, tensor, expert) = SplitMix64 output of state ``seed``
   at counter ``tensor * 65536 + expert``.
-* normal deviate (Irwin-Hall with 4 terms): the 64-bit output is cut into
-  four 16-bit integers h0..h3; D = h0+h1+h2+h3 + 2 - 131072 is the exact
-  integer 65536*(sum of the four uniforms (h+1/2)/65536 minus 2);
-  z = fl32(fl32(D) * C0) with C0 = fl32(sqrt(3)/65536) (bits 0x37DDB3D7) has
-  mean 0 and variance 1 and a bell shape bounded by +-2*sqrt(3).
+* normal deviate (Irwin-Hall with 12 terms, the sum of twelve uniforms
+  minus 6): element c takes the SplitMix64 outputs at counters 3c, 3c+1 and
+  3c+2, each cut into four 16-bit integers, twelve in all; D = sum(h) + 6 -
+  393216 is the exact integer 65536*(sum of the twelve uniforms (h+1/2)/65536
+  minus 6), and z = fl32(D) * 2^-16 is exact.  z has mean 0, variance 1,
+  kurtosis 2.9 (a Gaussian's is 3) and tails out to +-6.
 * value = fl32(z * scale), scale = fl32(std); bf16 tensors then round to
   nearest even.
 
 Only correctly rounded IEEE operations on exactly representable operands
-are used, so NumPy and the GPU agree bit for bit.  The four-term sum stands
-in for a Gaussian (N(0, std) in the workload statement); it has the stated
-mean and standard deviation.
+are used, so NumPy and the GPU agree bit for bit.  The twelve-term sum stands
+in for a Gaussian (N(0, std) in the workload statement): it has the stated
+mean and standard deviation, and only |z| > 6 (probability 2e-9 for a
+Gaussian) never occurs.
 
 Nothing here computes any part of the MoE layer.
 """
@@ -36,8 +38,8 @@ from .configs import MoEConfig
 GAMMA = np.uint64(0x9E3779B97F4A7C15)
 M1 = np.uint64(0xBF58476D1CE4E5B9)
 M2 = np.uint64(0x94D049BB133111EB)
-C0_BITS = 0x37DDB3D7
-C0 = np.array([C0_BITS], dtype=np.uint32).view(np.float32)[0]
+NTERM = 12                         # uniforms per deviate (3 outputs x 4)
+INV65536 = np.float32(1.0 / 65536.0)
 
 # tensor ids of the stream keys
 TID_X, TID_WG, TID_W1, TID_W3, TID_W2, TID_DY = 1, 2, 3, 4, 5, 6
@@ -64,11 +66,14 @@ def stream_key(seed: int, tensor: int, expert: int = 0) -> int:
 
 def _fill_chunk(out, key, start, lo, n, sc):
     mask = np.uint64(0xFFFF)
-    h = splitmix64_at(key, np.arange(start + lo, start + lo + n, dtype=np.uint64))
-    s = ((h & mask) + ((h >> np.uint64(16)) & mask)
-         + ((h >> np.uint64(32)) & mask) + (h >> np.uint64(48)))
-    dd = s.astype(np.int64) + 2 - 131072
-    z = dd.astype(np.float32) * C0
+    c = np.arange(start + lo, start + lo + n, dtype=np.uint64) * np.uint64(3)
+    s = np.zeros(n, dtype=np.uint64)
+    for q in range(3):
+        h = splitmix64_at(key, c + np.uint64(q))
+        s += ((h & mask) + ((h >> np.uint64(16)) & mask)
+              + ((h >> np.uint64(32)) & mask) + (h >> np.uint64(48)))
+    dd = s.astype(np.int64) + NTERM // 2 - NTERM * 32768
+    z = dd.astype(np.float32) * INV65536
     out[lo:lo + n] = z * sc
 
 

@@ -21,11 +21,19 @@ def test_normal_moments_and_support():
     z = rng.normal_f32(rng.stream_key(0, 1, 0), 0, 1 << 20, 1.0)
     assert abs(float(z.mean())) < 5e-3
     assert abs(float(z.std()) - 1.0) < 5e-3
-    # Irwin-Hall(4) support is +-2*sqrt(3)
-    assert float(np.abs(z).max()) <= 2 * np.sqrt(3) + 1e-6
-    # kurtosis of a 4-term uniform sum: 3 - 6/(5*4) = 2.7
+    # Irwin-Hall(12) support is +-6; a million draws reach past 4.5 sigma
+    # (a Gaussian does so with probability 6.8e-6 per draw)
+    assert float(np.abs(z).max()) <= 6.0
+    assert float(np.abs(z).max()) > 4.5
+    # kurtosis of a 12-term uniform sum: 3 - 6/(5*12) = 2.9
     k = float(((z.astype(np.float64)) ** 4).mean())
-    assert abs(k - 2.7) < 0.05
+    assert abs(k - 2.9) < 0.05
+    # element c is the twelve 16-bit pieces of outputs 3c .. 3c+2, exactly
+    key = rng.stream_key(0, 1, 0)
+    h = rng.splitmix64_at(key, np.arange(6))
+    parts = [int(v >> np.uint64(16 * q)) & 0xFFFF for v in h for q in range(4)]
+    want = [(sum(parts[12 * i:12 * i + 12]) + 6 - 393216) / 65536.0 for i in range(2)]
+    assert [float(v) for v in z[:2]] == want
 
 
 def test_counter_based_blocks_agree():
