@@ -82,6 +82,8 @@ struct GemmArgs {
     const int4* items;
     const int32_t* item_count;
     int item_max;        // host bound on the work items (grid size)
+    int k_grouped;       // RAGGED_K tile order inside an item: grouped (1) or
+                         // column by column (0), chosen by the launcher
     float* partial;
     long partial_ld;
 };
@@ -431,8 +433,18 @@ __device__ __forceinline__ TileInfo decode_tile(const GemmArgs<T>& p) {
     } else {
         const int per = p.nM * p.nN;
         const int es = L / per, rem = L % per;
-        ti.m0 = (rem % p.nM) * BM;
-        ti.n0 = (rem / p.nM) * BN;
+        if (p.k_grouped) {
+            // groups of GROUP_M row tiles, every column tile of a group, row
+            // tiles fastest: a run of 32 on one XCD is 8 row x 4 column tiles
+            const int first = (rem / (GROUP_M * p.nN)) * GROUP_M;
+            const int gm = min(GROUP_M, p.nM - first);
+            const int w = rem - first * p.nN;
+            ti.m0 = (first + w % gm) * BM;
+            ti.n0 = (w / gm) * BN;
+        } else {
+            ti.m0 = (rem % p.nM) * BM;
+            ti.n0 = (rem / p.nM) * BN;
+        }
         ti.r0 = 0;
         ti.rows = BM;
         if (p.items) {
@@ -1343,9 +1355,18 @@ void launch_bf16(GemmArgs<bf16_t> p, Epi epi, int R, hipStream_t s, const char* 
     } else {
         p.nM = (p.M + BM - 1) / BM;
         blocks = (p.items ? p.item_max : p.E) * p.nM * p.nN;
+        // Each XCD holds four runs of 8 consecutive tiles at once (32 compute
+        // units), runs 8 apart in the dealing order.  Column by column, those
+        // four runs share their row tiles (A panels) only when the row-tile
+        // count divides 64; otherwise (f = 14336: 56 row tiles of dW2) the
+        // tiles go in groups of 8 row tiles, runs of 32 (dW2 on the
+        // long-context shapes -11%; with a power-of-two row-tile count the
+        // column order was 1-4% faster)
+        p.k_grouped = 64 % p.nM != 0;
+        if (p.xcd_run <= 0) p.xcd_run = p.k_grouped ? 32 : 8;
     }
     if (blocks <= 0) return;
-    if (p.xcd_run <= 0) p.xcd_run = MODE == RAGGED_M ? 32 : 8;
+    if (p.xcd_run <= 0) p.xcd_run = 32;
     const int pad = NXCD * p.xcd_run;                      // whole XCD runs
     blocks = (blocks + pad - 1) / pad * pad;
     if constexpr (G) {
@@ -1399,6 +1420,7 @@ GemmArgs<T> base_args(const int32_t* offsets, const Plan& pl, int E) {
     p.items = nullptr;
     p.item_count = nullptr;
     p.item_max = 0;
+    p.k_grouped = 0;
     p.partial = nullptr;
     p.partial_ld = 0;
     return p;
