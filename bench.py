@@ -34,22 +34,48 @@ PEAK_HBM_GBS = 8000.0
 # cold source in the same run (the summaries under profiles/ give commands
 # and factors).  Valid only for the kernel sources whose SHA-256 prefix is
 # TRAFFIC_SRC; null once they change.
-TRAFFIC_SRC = "26f590441f7b8b88"
+TRAFFIC_SRC = "91099d581574c824"
 TRAFFIC_SOURCES = ("ggemm.hip", "common.h", "permute.hip", "combine.hip")
 TRAFFIC = {
-    # profiles/hbm_traffic_long_ctx_swiglu.md (fetch x 4.0, write x 2.0)
+    # profiles/hbm_traffic_long_ctx_swiglu.md
     "long_ctx_swiglu": {
-        "perm_copy": 9672130961,
-        "gemm_up_swiglu": 680818343110,
-        "gemm_down": 230782054174,
-        "combine": 9680264046,
-        "combine_bwd": 18275468947,
-        "gemm_dA_swiglu": 429276980978,
-        "gemm_dW2": 379100553070,
-        "gemm_dW1": 379100553070,
-        "gemm_dW3": 379100553070,
-        "gemm_dX": 494575969609,
-        "unpermute_grad": 10745592667,
+        "perm_copy": 9672121039,
+        "gemm_up_swiglu": 702329808976,
+        "gemm_down": 242468528824,
+        "combine": 9680258219,
+        "combine_bwd": 18275438271,
+        "gemm_dA_swiglu": 435644867427,
+        "gemm_dW2": 536196670993,
+        "gemm_dW1": 536196670993,
+        "gemm_dW3": 536196670993,
+        "gemm_dX": 522653542818,
+        "unpermute_grad": 10745595161,
+    },
+    # profiles/hbm_traffic_moe_s_like.md
+    "moe_s_like": {
+        "perm_copy": 101237882,
+        "gemm_up_gelu": 1186722060,
+        "gemm_down": 786328942,
+        "combine": 101776154,
+        "combine_bwd": 169111580,
+        "gemm_dA_gelu": 1186794142,
+        "gemm_dW2": 1141103149,
+        "gemm_dW1": 1141103149,
+        "gemm_dX": 784834135,
+        "unpermute_grad": 134812309,
+    },
+    # profiles/hbm_traffic_skewed_zipf1.2.md
+    "skewed_zipf1.2": {
+        "perm_copy": 403743092,
+        "gemm_up_gelu": 6970568121,
+        "gemm_down": 5434222771,
+        "combine": 404809816,
+        "combine_bwd": 673601428,
+        "gemm_dA_gelu": 6718727271,
+        "gemm_dW2": 4303421067,
+        "gemm_dW1": 4303421067,
+        "gemm_dX": 5466360092,
+        "unpermute_grad": 537981096,
     },
 }
 
