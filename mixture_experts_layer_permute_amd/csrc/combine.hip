@@ -13,11 +13,35 @@
 namespace moe {
 namespace {
 
-constexpr int U = 2;   // 16-byte vectors per lane in flight per slot
+constexpr int U = 2;   // 16-byte vectors per lane per slot in one batch of loads
+
+// The k slots of a token are taken KG at a time (KG = 1, 2, 4 or 8, the
+// launcher's smallest >= min(k, 8)): a lane issues the loads of all rows of a
+// group before it uses any of them, so that KG * U loads are in flight per
+// lane.  A slot past k or with an invalid row loads row 0 and is skipped.
+template <int KG>
+struct Slots {
+    long off[KG];        // element offset of the slot's row
+    float w[KG];         // the slot's gate weight (0 for a skipped slot; no weights: 0)
+    bool ok[KG];
+    __device__ __forceinline__ Slots(const int32_t* __restrict__ dest,
+                                     const float* __restrict__ wt, long t, int k, int jg,
+                                     int d, unsigned R) {
+#pragma unroll
+        for (int jj = 0; jj < KG; ++jj) {
+            const int j = jg + jj;
+            const long jc = t * k + min(j, k - 1);
+            const int r = dest[jc];
+            ok[jj] = j < k && (unsigned)r < R;
+            off[jj] = ok[jj] ? (long)r * d : 0;
+            w[jj] = wt && ok[jj] ? wt[jc] : 0.0f;
+        }
+    }
+};
 
 // y[t] = sum_j w[t,j] * out_perm[dest[t,j]], fp32 in slot order.  NT: the
 // rows bypass the caches (out_perm larger than the MALL).
-template <typename T, bool NT>
+template <typename T, bool NT, int KG>
 __global__ __launch_bounds__(256) void combine_kernel(
     const T* __restrict__ out_perm, const int32_t* __restrict__ dest,
     const float* __restrict__ w, int Tn, int k, int d, T* __restrict__ y) {
@@ -27,41 +51,49 @@ __global__ __launch_bounds__(256) void combine_kernel(
     const long t = (long)blockIdx.x * 4 + wv;
     if (t >= Tn) return;
     const int nvec = d / V;
+    const Slots<KG> s0(dest, w, t, k, 0, d, (unsigned)(Tn * k));   // the first group
     for (int v0 = 0; v0 < nvec; v0 += 64 * U) {
         float acc[U][V];
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int q = 0; q < V; ++q) acc[u][q] = 0.0f;
-        for (int j = 0; j < k; ++j) {
-            const int r = dest[t * k + j];
-            if ((unsigned)r >= (unsigned)(Tn * k)) continue;
-            const float wj = w[t * k + j];
-            const T* row = out_perm + (long)r * d;
+        for (int jg = 0; jg < k; jg += KG) {
+            const Slots<KG> sl = jg == 0 ? s0 : Slots<KG>(dest, w, t, k, jg, d, (unsigned)(Tn * k));
+            u32x4_t raw[KG][U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int v = v0 + u * 64 + lane;
-                if (v < nvec) {
+            for (int jj = 0; jj < KG; ++jj)
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    // out-of-row lanes load the row's last vector (never stored)
+                    const int v = min(v0 + u * 64 + lane, nvec - 1);
+                    raw[jj][u] = ld16<NT>(out_perm + sl.off[jj] + (long)v * V);
+                }
+#pragma unroll
+            for (int jj = 0; jj < KG; ++jj) {
+                if (!sl.ok[jj]) continue;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
                     float o[V];
-                    Vec16s<T, NT>::ld(row + (long)v * V, o);
+                    unpack16<T>(raw[jj][u], o);
 #pragma unroll
-                    for (int q = 0; q < V; ++q) acc[u][q] = fmaf(wj, o[q], acc[u][q]);
+                    for (int q = 0; q < V; ++q) acc[u][q] = fmaf(sl.w[jj], o[q], acc[u][q]);
                 }
             }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int v = v0 + u * 64 + lane;
-            if (v < nvec) Vec16s<T, NT>::st(y + t * d + (long)v * V, acc[u]);
+            if (v < nvec) st16<NT>(y + t * d + (long)v * V, pack16<T>(acc[u]));
         }
     }
 }
 
 // d_out_perm[dest[t,j]] = w[t,j] dy[t];  dw[t,j] = <dy[t], out_perm[dest[t,j]]>.
-// Slots are taken 8 at a time so dy is read once for k <= 8.
-constexpr int KG = 8;
-
-template <typename T>
+// dy is read once per group of KG slots (once for k <= 8); each lane takes
+// two of its vectors per batch of loads, in order, so each dot is the same
+// fp32 sequence over the lane's vectors as one at a time.
+template <typename T, int KG>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(
     const T* __restrict__ dy, const T* __restrict__ out_perm,
     const int32_t* __restrict__ dest, const float* __restrict__ w, int Tn,
@@ -73,28 +105,37 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
     if (t >= Tn) return;
     const int nvec = d / V;
     for (int jg = 0; jg < k; jg += KG) {
-        const int nj = min(KG, k - jg);
+        const Slots<KG> sl(dest, w, t, k, jg, d, (unsigned)(Tn * k));
         float dot[KG];
 #pragma unroll
         for (int jj = 0; jj < KG; ++jj) dot[jj] = 0.0f;
-        for (int v = lane; v < nvec; v += 64) {
-            float g[V];
-            Vec16<T>::ld(dy + t * d + (long)v * V, g);
+        for (int v0 = lane; v0 < nvec; v0 += 64 * U) {
+            u32x4_t graw[U], raw[KG][U];
 #pragma unroll
-            for (int jj = 0; jj < KG; ++jj) {
-                if (jj < nj) {
-                    const int j = jg + jj;
-                    const int r = dest[t * k + j];
-                    if ((unsigned)r >= (unsigned)(Tn * k)) continue;
-                    const float wj = w[t * k + j];
+            for (int u = 0; u < U; ++u) {
+                const int v = min(v0 + u * 64, nvec - 1);
+                graw[u] = ld16<false>(dy + t * d + (long)v * V);
+#pragma unroll
+                for (int jj = 0; jj < KG; ++jj)
+                    raw[jj][u] = ld16<false>(out_perm + sl.off[jj] + (long)v * V);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int v = v0 + u * 64;
+                if (v >= nvec) break;
+                float g[V];
+                unpack16<T>(graw[u], g);
+#pragma unroll
+                for (int jj = 0; jj < KG; ++jj) {
+                    if (!sl.ok[jj]) continue;
                     float o[V], s[V];
-                    Vec16<T>::ld(out_perm + (long)r * d + (long)v * V, o);
+                    unpack16<T>(raw[jj][u], o);
 #pragma unroll
                     for (int q = 0; q < V; ++q) {
                         dot[jj] = fmaf(g[q], o[q], dot[jj]);
-                        s[q] = wj * g[q];
+                        s[q] = sl.w[jj] * g[q];
                     }
-                    Vec16<T>::st(d_out + (long)r * d + (long)v * V, s);
+                    st16<false>(d_out + sl.off[jj] + (long)v * V, pack16<T>(s));
                 }
             }
         }
@@ -103,14 +144,14 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
             float v = dot[jj];
 #pragma unroll
             for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-            if (jj < nj && lane == 0) dw[t * k + jg + jj] = v;
+            if (jg + jj < k && lane == 0) dw[t * k + jg + jj] = v;
         }
     }
 }
 
 // dx[t] (+)= sum_j dx_perm[dest[t,j]], fp32 in slot order.  NT: the rows
 // bypass the caches (dx_perm larger than the MALL).
-template <typename T, bool NT>
+template <typename T, bool NT, int KG>
 __global__ __launch_bounds__(256) void unpermute_grad_kernel(
     const T* __restrict__ dxp, const int32_t* __restrict__ dest, int Tn, int k,
     int d, int accumulate, T* __restrict__ dx) {
@@ -120,16 +161,14 @@ __global__ __launch_bounds__(256) void unpermute_grad_kernel(
     const long t = (long)blockIdx.x * 4 + wv;
     if (t >= Tn) return;
     const int nvec = d / V;
+    const Slots<KG> s0(dest, nullptr, t, k, 0, d, (unsigned)(Tn * k));   // the first group
     for (int v0 = 0; v0 < nvec; v0 += 64 * U) {
-        float acc[U][V];
+        u32x4_t old[U];
+        if (accumulate) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int v = v0 + u * 64 + lane;
-            if (accumulate && v < nvec) {
-                Vec16<T>::ld(dx + t * d + (long)v * V, acc[u]);
-            } else {
-#pragma unroll
-                for (int q = 0; q < V; ++q) acc[u][q] = 0.0f;
+            for (int u = 0; u < U; ++u) {
+                const int v = min(v0 + u * 64 + lane, nvec - 1);
+                old[u] = ld16<false>(dx + t * d + (long)v * V);
             }
         }
         float sum[U][V];
@@ -137,16 +176,23 @@ __global__ __launch_bounds__(256) void unpermute_grad_kernel(
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int q = 0; q < V; ++q) sum[u][q] = 0.0f;
-        for (int j = 0; j < k; ++j) {
-            const int r = dest[t * k + j];
-            if ((unsigned)r >= (unsigned)(Tn * k)) continue;
-            const T* row = dxp + (long)r * d;
+        for (int jg = 0; jg < k; jg += KG) {
+            const Slots<KG> sl = jg == 0 ? s0 : Slots<KG>(dest, nullptr, t, k, jg, d, (unsigned)(Tn * k));
+            u32x4_t raw[KG][U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int v = v0 + u * 64 + lane;
-                if (v < nvec) {
+            for (int jj = 0; jj < KG; ++jj)
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int v = min(v0 + u * 64 + lane, nvec - 1);
+                    raw[jj][u] = ld16<NT>(dxp + sl.off[jj] + (long)v * V);
+                }
+#pragma unroll
+            for (int jj = 0; jj < KG; ++jj) {
+                if (!sl.ok[jj]) continue;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
                     float o[V];
-                    Vec16s<T, NT>::ld(row + (long)v * V, o);
+                    unpack16<T>(raw[jj][u], o);
 #pragma unroll
                     for (int q = 0; q < V; ++q) sum[u][q] += o[q];
                 }
@@ -156,12 +202,28 @@ __global__ __launch_bounds__(256) void unpermute_grad_kernel(
         for (int u = 0; u < U; ++u) {
             const int v = v0 + u * 64 + lane;
             if (v < nvec) {
+                float acc[V];
+                if (accumulate) {
+                    unpack16<T>(old[u], acc);
+                } else {
 #pragma unroll
-                for (int q = 0; q < V; ++q) acc[u][q] += sum[u][q];
-                Vec16s<T, NT>::st(dx + t * d + (long)v * V, acc[u]);
+                    for (int q = 0; q < V; ++q) acc[q] = 0.0f;
+                }
+#pragma unroll
+                for (int q = 0; q < V; ++q) acc[q] += sum[u][q];
+                st16<NT>(dx + t * d + (long)v * V, pack16<T>(acc));
             }
         }
     }
+}
+
+// Calls f(std::integral_constant<int, KG>) for the slot group of k.
+template <class F>
+void with_kg(int k, F&& f) {
+    if (k <= 1) f(std::integral_constant<int, 1>{});
+    else if (k <= 2) f(std::integral_constant<int, 2>{});
+    else if (k <= 4) f(std::integral_constant<int, 4>{});
+    else f(std::integral_constant<int, 8>{});
 }
 
 bool rows_ok(moe_dtype dt, int d) {
@@ -187,9 +249,12 @@ moe_status moe_combine(const void* out_perm, const int32_t* dest,
     const bool nt = (long)T * k * d * (dt == MOE_BF16 ? 2 : 4) > kMallBytes;
     auto go = [&](auto tag, auto ntc) {
         using E = decltype(tag);
-        MOE_LAUNCH("combine", stream,
-            (combine_kernel<E, decltype(ntc)::value><<<cdiv(T, 4), 256, 0, stream>>>(
-                static_cast<const E*>(out_perm), dest, topk_w, T, k, d, static_cast<E*>(y))));
+        with_kg(k, [&](auto kg) {
+            MOE_LAUNCH("combine", stream,
+                (combine_kernel<E, decltype(ntc)::value, decltype(kg)::value>
+                 <<<cdiv(T, 4), 256, 0, stream>>>(static_cast<const E*>(out_perm), dest, topk_w,
+                                                  T, k, d, static_cast<E*>(y))));
+        });
     };
     if (dt == MOE_BF16) {
         if (nt) go(bf16_t{}, std::true_type{}); else go(bf16_t{}, std::false_type{});
@@ -209,16 +274,16 @@ moe_status moe_combine_bwd(const void* dy, const void* out_perm,
     MOE_CHECK_ARG(dy && out_perm && dest && topk_w && d_out_perm && d_topk_w);
     MOE_CHECK_ARG(aligned16(dy) && aligned16(out_perm) && aligned16(d_out_perm));
     MOE_CHECK_DEVICE();
-    if (dt == MOE_BF16)
-        MOE_LAUNCH("combine_bwd", stream,
-            combine_bwd_kernel<bf16_t><<<cdiv(T, 4), 256, 0, stream>>>(
-                static_cast<const bf16_t*>(dy), static_cast<const bf16_t*>(out_perm),
-                dest, topk_w, T, k, d, static_cast<bf16_t*>(d_out_perm), d_topk_w));
-    else
-        MOE_LAUNCH("combine_bwd", stream,
-            combine_bwd_kernel<float><<<cdiv(T, 4), 256, 0, stream>>>(
-                static_cast<const float*>(dy), static_cast<const float*>(out_perm),
-                dest, topk_w, T, k, d, static_cast<float*>(d_out_perm), d_topk_w));
+    auto go = [&](auto tag) {
+        using E = decltype(tag);
+        with_kg(k, [&](auto kg) {
+            MOE_LAUNCH("combine_bwd", stream,
+                (combine_bwd_kernel<E, decltype(kg)::value><<<cdiv(T, 4), 256, 0, stream>>>(
+                    static_cast<const E*>(dy), static_cast<const E*>(out_perm), dest, topk_w, T,
+                    k, d, static_cast<E*>(d_out_perm), d_topk_w)));
+        });
+    };
+    if (dt == MOE_BF16) go(bf16_t{}); else go(float{});
     return launch_status();
 }
 
@@ -234,10 +299,12 @@ moe_status moe_unpermute_grad(const void* dx_perm, const int32_t* dest, int T,
     const bool nt = (long)T * k * d * (dt == MOE_BF16 ? 2 : 4) > kMallBytes;
     auto go = [&](auto tag, auto ntc) {
         using E = decltype(tag);
-        MOE_LAUNCH("unpermute_grad", stream,
-            (unpermute_grad_kernel<E, decltype(ntc)::value><<<cdiv(T, 4), 256, 0, stream>>>(
-                static_cast<const E*>(dx_perm), dest, T, k, d, accumulate,
-                static_cast<E*>(dx))));
+        with_kg(k, [&](auto kg) {
+            MOE_LAUNCH("unpermute_grad", stream,
+                (unpermute_grad_kernel<E, decltype(ntc)::value, decltype(kg)::value>
+                 <<<cdiv(T, 4), 256, 0, stream>>>(static_cast<const E*>(dx_perm), dest, T, k, d,
+                                                  accumulate, static_cast<E*>(dx))));
+        });
     };
     if (dt == MOE_BF16) {
         if (nt) go(bf16_t{}, std::true_type{}); else go(bf16_t{}, std::false_type{});

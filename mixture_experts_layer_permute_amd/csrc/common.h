@@ -84,41 +84,51 @@ template <> struct Vec16<bf16_t> {
     }
 };
 
-// 16-byte vector access that does not keep the line in the caches
-// (nontemporal).  Streaming row kernels whose rows exceed the 256 MB MALL use
-// it: the rows are touched once, and keeping them only evicts other data.
+// A 16-byte vector of a row as raw bits, loaded or stored plainly or
+// nontemporally (NT: the line is not kept in the caches; streaming row
+// kernels whose rows exceed the 256 MB MALL use it, since the rows are touched
+// once and keeping them only evicts other data).  unpack16 / pack16 convert
+// between the bits and the vector's V floats.
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-template <typename T, bool NT> struct Vec16s;
-template <typename T> struct Vec16s<T, false> {
-    static __device__ __forceinline__ void ld(const T* p, float* o) { Vec16<T>::ld(p, o); }
-    static __device__ __forceinline__ void st(T* p, const float* o) { Vec16<T>::st(p, o); }
-};
-template <typename T> struct Vec16s<T, true> {
-    static __device__ __forceinline__ void ld(const T* p, float* o) {
-        const u32x4_t w = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-        if constexpr (sizeof(T) == 2) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                o[2 * i] = __uint_as_float(w[i] << 16);
-                o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] = __uint_as_float(w[i]);
-        }
-    }
-    static __device__ __forceinline__ void st(T* p, const float* o) {
-        u32x4_t w;
-        if constexpr (sizeof(T) == 2) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(o[2 * i], o[2 * i + 1]);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) w[i] = __float_as_uint(o[i]);
-        }
+template <bool NT>
+__device__ __forceinline__ u32x4_t ld16(const void* p) {
+    if constexpr (NT)
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    else
+        return *reinterpret_cast<const u32x4_t*>(p);
+}
+template <bool NT>
+__device__ __forceinline__ void st16(void* p, u32x4_t w) {
+    if constexpr (NT)
         __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
+    else
+        *reinterpret_cast<u32x4_t*>(p) = w;
+}
+template <typename T>
+__device__ __forceinline__ void unpack16(u32x4_t w, float* o) {
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            o[2 * i] = __uint_as_float(w[i] << 16);
+            o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = __uint_as_float(w[i]);
     }
-};
+}
+template <typename T>
+__device__ __forceinline__ u32x4_t pack16(const float* o) {
+    u32x4_t w;
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(o[2 * i], o[2 * i + 1]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = __float_as_uint(o[i]);
+    }
+    return w;
+}
 constexpr long kMallBytes = 256l << 20;
 
 // ------------------------------------------------------------ host side
