@@ -34,48 +34,48 @@ PEAK_HBM_GBS = 8000.0
 # cold source in the same run (the summaries under profiles/ give commands
 # and factors).  Valid only for the kernel sources whose SHA-256 prefix is
 # TRAFFIC_SRC; null once they change.
-TRAFFIC_SRC = "91099d581574c824"
+TRAFFIC_SRC = "a797fa149aed167d"
 TRAFFIC_SOURCES = ("ggemm.hip", "common.h", "permute.hip", "combine.hip")
 TRAFFIC = {
     # profiles/hbm_traffic_long_ctx_swiglu.md
     "long_ctx_swiglu": {
-        "perm_copy": 9672121039,
-        "gemm_up_swiglu": 702329808976,
-        "gemm_down": 242468528824,
-        "combine": 9680258219,
-        "combine_bwd": 18275438271,
-        "gemm_dA_swiglu": 435644867427,
-        "gemm_dW2": 536196670993,
-        "gemm_dW1": 536196670993,
-        "gemm_dW3": 536196670993,
-        "gemm_dX": 522653542818,
-        "unpermute_grad": 10745595161,
+        "perm_copy": 9672121672,
+        "gemm_up_swiglu": 704386564743,
+        "gemm_down": 235027195230,
+        "combine": 9680330649,
+        "combine_bwd": 18275054337,
+        "gemm_dA_swiglu": 462354667185,
+        "gemm_dW2": 542665044463,
+        "gemm_dW1": 542665044463,
+        "gemm_dW3": 542665044463,
+        "gemm_dX": 502824473624,
+        "unpermute_grad": 10745674319,
     },
     # profiles/hbm_traffic_moe_s_like.md
     "moe_s_like": {
-        "perm_copy": 101237882,
-        "gemm_up_gelu": 1186722060,
-        "gemm_down": 786328942,
-        "combine": 101776154,
-        "combine_bwd": 169111580,
-        "gemm_dA_gelu": 1186794142,
-        "gemm_dW2": 1141103149,
-        "gemm_dW1": 1141103149,
-        "gemm_dX": 784834135,
-        "unpermute_grad": 134812309,
+        "perm_copy": 101243301,
+        "gemm_up_gelu": 1186665309,
+        "gemm_down": 785601616,
+        "combine": 101795146,
+        "combine_bwd": 169050873,
+        "gemm_dA_gelu": 1187262076,
+        "gemm_dW2": 1141104061,
+        "gemm_dW1": 1141104061,
+        "gemm_dX": 784834373,
+        "unpermute_grad": 134847727,
     },
     # profiles/hbm_traffic_skewed_zipf1.2.md
     "skewed_zipf1.2": {
-        "perm_copy": 403743092,
-        "gemm_up_gelu": 6970568121,
-        "gemm_down": 5434222771,
-        "combine": 404809816,
-        "combine_bwd": 673601428,
-        "gemm_dA_gelu": 6718727271,
-        "gemm_dW2": 4303421067,
-        "gemm_dW1": 4303421067,
-        "gemm_dX": 5466360092,
-        "unpermute_grad": 537981096,
+        "perm_copy": 403743014,
+        "gemm_up_gelu": 6893505786,
+        "gemm_down": 5436096535,
+        "combine": 404829005,
+        "combine_bwd": 673548276,
+        "gemm_dA_gelu": 6664836637,
+        "gemm_dW2": 4300262551,
+        "gemm_dW1": 4300262551,
+        "gemm_dX": 5461043045,
+        "unpermute_grad": 538016151,
     },
 }
 
