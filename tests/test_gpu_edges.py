@@ -201,3 +201,47 @@ def test_permute_skips_invalid_expert_ids():
     assert_equal_i(dest, want_dest.reshape(T, k), "dest")
     assert_equal_i(host_i(src)[:nv], order[:nv] // k, "src")
     assert np.array_equal(host(xp[:nv]), x.astype(np.float64)[order[:nv] // k]), "x_perm"
+
+
+@pytest.mark.parametrize("k", [3, 8, 11])
+def test_row_kernels_skip_invalid_slots(k):
+    """dest = -1 (a pair whose expert id was invalid) contributes nothing: the
+    combine sums the other slots, its backward writes no row and a zero gate
+    gradient for the slot, the unpermute adds nothing.  The oracle sees the
+    same slots pointed at an extra all-zero row with weight 0."""
+    g = np.random.default_rng(7 + k)
+    T, d, E = 211, 128, 16
+    idx = np.stack([g.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    _, _, dest, _ = oracle.permute(idx, E)
+    bad = g.choice(T * k, size=T // 3, replace=False)
+    R = T * k
+    gdest = dest.reshape(-1).copy()
+    gdest[bad] = -1
+    odest = dest.reshape(-1).copy()
+    odest[bad] = R                               # the extra zero row
+    gdest, odest = gdest.reshape(T, k), odest.reshape(T, k)
+    out = stage.normal(71, (R, d), 1.0, "bf16")
+    dxp = stage.normal(72, (R, d), 1.0, "bf16")
+    dy = stage.normal(73, (T, d), 1.0, "bf16")
+    w = np.abs(stage.normal(74, (T, k), 1.0, "f32"))
+    ow = w.copy()
+    ow.reshape(-1)[bad] = 0.0
+    out1 = np.concatenate([out, np.zeros((1, d), out.dtype)])
+    dxp1 = np.concatenate([dxp, np.zeros((1, d), dxp.dtype)])
+    banner("row kernels with dest = -1", T, k)
+    g_out, g_dest, g_w = dev(out, "bf16"), dev_i32(gdest), dev(w)
+    y = M.moe_combine(g_out, g_dest, g_w)
+    # rows no slot maps to are not written: start them at zero
+    d_out = torch.zeros_like(g_out)
+    dw = torch.empty(T, k, dtype=torch.float32, device=g_out.device)
+    d_out, dw = M.moe_combine_bwd(dev(dy, "bf16"), g_out, g_dest, g_w, out=(d_out, dw))
+    dx = M.moe_unpermute_grad(dev(dxp, "bf16"), g_dest)
+    torch.cuda.synchronize()
+    assert_close(y, oracle.combine(out1, odest, ow), "bf16", "y")
+    rd_out, rdw = oracle.combine_bwd(dy, out1, odest, ow)
+    assert_close(d_out, rd_out[:R], "bf16", "d_out_perm")
+    dwh = dw.cpu().numpy()
+    assert np.all(dwh.reshape(-1)[bad] == 0.0), "d_topk_w of skipped slots"
+    assert_close(dw, rdw, "bf16", "d_topk_w")
+    assert_close(dx, oracle.unpermute_grad(dxp1, odest), "bf16", "dx")
+

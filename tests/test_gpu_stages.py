@@ -172,7 +172,10 @@ def test_expert_ffn_bwd(case, act, dt):
 # ------------------------------------------------- combine / unpermute
 
 ROW_CASES = [(1000, 8, 2, 128), (333, 16, 4, 64), (64, 128, 8, 512), (1, 4, 1, 64),
-             (2049, 64, 2, 1024)]
+             (2049, 64, 2, 1024),
+             # slot groups of 4 and 8 with padded slots (k = 3, 6), two and
+             # three groups of 8 (k = 12, 20)
+             (257, 16, 3, 192), (130, 32, 6, 320), (77, 64, 12, 256), (50, 40, 20, 128)]
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
