@@ -165,14 +165,17 @@ def parse():
     return ap.parse_args()
 
 
-def mfma_loop_tflops(torch, L, s, stream, iters=50000, reps=3):
+def mfma_loop_tflops(torch, L, s, stream, iters=50000, reps=3, random=False):
     """Attainable bf16 matrix-instruction rate: moe_mfma_loop on two
     workgroups of 4 waves per compute unit (two waves per SIMD), register
-    operands only, timed with events on the step's stream."""
+    operands only, timed with events on the step's stream.  random: the
+    operands change with every instruction (moe_mfma_loop_random), the
+    ceiling for GEMMs on random data (the rate depends on the data)."""
     from mixture_experts_layer_permute_amd import _lib
     blocks = 2 * torch.cuda.get_device_properties(0).multi_processor_count
     out = torch.empty(blocks * 4, dtype=torch.float32, device="cuda")
-    run = lambda: _lib.check(L.moe_mfma_loop(blocks, iters, out.data_ptr(), out.numel(), s),
+    fn = L.moe_mfma_loop_random if random else L.moe_mfma_loop
+    run = lambda: _lib.check(fn(blocks, iters, out.data_ptr(), out.numel(), s),
                              "moe_mfma_loop")
     run()
     torch.cuda.synchronize()
@@ -561,6 +564,7 @@ def main():
         torch.cuda.empty_cache()
     copy_gbs = stream_copy_gbs(torch)
     mfma_tf = mfma_loop_tflops(torch, L, s, stream)
+    mfma_rand_tf = mfma_loop_tflops(torch, L, s, stream, iters=20000, random=True)
     work = kernel_work(cfg)
     kernels = {}
     for name, v in per.items():
@@ -598,6 +602,7 @@ def main():
             ent["frac_of_peak"] = round(ent["tflops"] / PEAK_BF16_TFLOPS, 4)
             if cfg.dtype == "bf16":
                 ent["frac_of_mfma_loop"] = round(ent["tflops"] / mfma_tf, 4)
+                ent["frac_of_mfma_random"] = round(ent["tflops"] / mfma_rand_tf, 4)
             gemm_ms += per_call * calls
         else:
             ent["gbs"] = round(amt / (per_call * 1e-3) / 1e9, 1)
@@ -658,7 +663,10 @@ def main():
         "value_at_median_step": round(cfg.T / (pct(0.5) * 1e-3), 1),
         "stream_copy_gbs": round(copy_gbs, 1),
         "mfma_loop_tflops": round(mfma_tf, 1),
+        "mfma_loop_random_tflops": round(mfma_rand_tf, 1),
         "gemm_frac_of_mfma_loop": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / mfma_tf, 4)
+        if gemm_ms and cfg.dtype == "bf16" else None,
+        "gemm_frac_of_mfma_random": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / mfma_rand_tf, 4)
         if gemm_ms and cfg.dtype == "bf16" else None,
         "roofline": roof,
         "graph_replay": graph,

@@ -378,6 +378,21 @@ moe_status moe_profile_get(int i, const char **name, float *ms);
 moe_status moe_mfma_loop(int blocks, int iters, float *out, size_t out_floats,
                          hipStream_t stream);
 
+/*
+ * moe_mfma_loop_random -- benchmark support: moe_mfma_loop on operands that
+ * change with every instruction.  Each wave cycles through eight A and eight
+ * B fragments of random bf16 values (|v| < 1, random mantissas), so the
+ * matrix cores see operand bits toggle as in a GEMM on random data.  The
+ * sustained rate of the matrix instructions depends on the data (power and
+ * clock), and this is the ceiling that applies to GEMMs on such inputs.
+ *   iters: a positive multiple of 8 (rounds of four instructions per wave).
+ *   out: as for moe_mfma_loop.
+ *   Errors: MOE_ERR_INVALID_ARG for blocks < 1, iters not a positive
+ *   multiple of 8, out NULL or out_floats < blocks * 4.
+ */
+moe_status moe_mfma_loop_random(int blocks, int iters, float *out, size_t out_floats,
+                                hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

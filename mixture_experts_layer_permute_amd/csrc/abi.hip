@@ -159,6 +159,54 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, float* __rest
         for (int v = 0; v < 16; ++v) s += acc[c][v];
     if (lane == 0) out[blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6)] = s;
 }
+// The same loop on operands that change with every instruction: each wave
+// holds eight A and eight B fragments of random bf16 values (a counter hash
+// of block, wave, lane and slot, |v| < 1) and cycles through them, so the
+// matrix cores see operand bits toggle as in a GEMM on random data.  On this
+// part the matrix instructions' sustained rate depends on the data (power
+// and clock): constant operands run faster than random ones.
+__device__ __forceinline__ uint32_t mix32(uint32_t h) {
+    h ^= h >> 16;
+    h *= 0x7feb352du;
+    h ^= h >> 15;
+    h *= 0x846ca68bu;
+    h ^= h >> 16;
+    return h;
+}
+__global__ __launch_bounds__(256) void mfma_loop_random_kernel(int rounds, float* __restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    const uint32_t seed = ((uint32_t)blockIdx.x * 256u + threadIdx.x) * 256u;
+    bf16x8 a[8], b[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            // a float in (-1, 1): random mantissa bits, exponents of 2^-1 .. 2^-8
+            const uint32_t ha = mix32(seed + (uint32_t)(s * 16 + q));
+            const uint32_t hb = mix32(seed + (uint32_t)(s * 16 + 8 + q) + 0x9e3779b9u);
+            a[s][q] = (__bf16)__uint_as_float((ha & 0x807fffffu) | ((126u - (ha >> 28 & 7u)) << 23));
+            b[s][q] = (__bf16)__uint_as_float((hb & 0x807fffffu) | ((126u - (hb >> 28 & 7u)) << 23));
+        }
+    f32x16 acc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[c][v] = 0.0f;
+    for (int i = 0; i < rounds; ++i) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[(u + c) & 7], b[(u + 3 * c + 1) & 7],
+                                                                acc[c], 0, 0, 0);
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s += acc[c][v];
+    if (lane == 0) out[blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6)] = s;
+}
 
 }  // namespace moe
 
@@ -172,6 +220,17 @@ moe_status moe_mfma_loop(int blocks, int iters, float* out, size_t out_floats,
     MOE_CHECK_DEVICE();
     MOE_LAUNCH("mfma_loop", stream,
                mfma_loop_kernel<<<blocks, 256, 0, stream>>>(iters, out));
+    return launch_status();
+}
+
+moe_status moe_mfma_loop_random(int blocks, int iters, float* out, size_t out_floats,
+                                hipStream_t stream) {
+    using namespace moe;
+    MOE_CHECK_ARG(blocks >= 1 && iters >= 8 && iters % 8 == 0 && out);
+    MOE_CHECK_ARG(out_floats >= (size_t)blocks * 4);
+    MOE_CHECK_DEVICE();
+    MOE_LAUNCH("mfma_loop_random", stream,
+               mfma_loop_random_kernel<<<blocks, 256, 0, stream>>>(iters / 8, out));
     return launch_status();
 }
 
@@ -236,7 +295,7 @@ const char* moe_status_string(moe_status s) {
     return "unknown status";
 }
 
-int moe_abi_version(void) { return 6; }
+int moe_abi_version(void) { return 7; }
 
 moe_status moe_set_overlap(int enable) {
     moe::g_overlap.store(enable != 0 ? 1 : 0, std::memory_order_relaxed);

@@ -50,7 +50,7 @@ def test_binding_names_match_c_names():
 
 
 def test_status_strings_and_version(lib):
-    assert lib.moe_abi_version() == 6
+    assert lib.moe_abi_version() == 7
     for s in (0, -1, -2, -3, -4):
         assert lib.moe_status_string(s)
 
@@ -170,3 +170,7 @@ def test_mfma_loop_rejects_bad_arguments(lib):
     assert lib.moe_mfma_loop(0, 10, None, 0, None) == INV          # no blocks, no buffer
     assert lib.moe_mfma_loop(4, 0, 16, 16, None) == INV            # no iterations
     assert lib.moe_mfma_loop(4, 10, 16, 15, None) == INV           # buffer under blocks * 4
+    assert lib.moe_mfma_loop_random(0, 16, None, 0, None) == INV   # no blocks, no buffer
+    assert lib.moe_mfma_loop_random(4, 12, 16, 16, None) == INV    # not a multiple of 8
+    assert lib.moe_mfma_loop_random(4, 0, 16, 16, None) == INV     # no iterations
+    assert lib.moe_mfma_loop_random(4, 16, 16, 15, None) == INV    # buffer under blocks * 4
