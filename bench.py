@@ -133,10 +133,10 @@ def parse():
                          "per-kernel pass is always serial")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU work for the oracle baseline")
-    ap.add_argument("--cpu-tokens", type=int, default=8192,
+    ap.add_argument("--cpu-tokens", type=int, default=32768,
                     help="sampled oracle baseline of a large workload: tokens "
                          "routed and carried through the row steps")
-    ap.add_argument("--cpu-rows", type=int, default=320,
+    ap.add_argument("--cpu-rows", type=int, default=800,
                     help="sampled oracle baseline: rows of each of the four "
                          "seeded experts carried through the FFN")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
