@@ -34,48 +34,48 @@ PEAK_HBM_GBS = 8000.0
 # cold source in the same run (the summaries under profiles/ give commands
 # and factors).  Valid only for the kernel sources whose SHA-256 prefix is
 # TRAFFIC_SRC; null once they change.
-TRAFFIC_SRC = "a797fa149aed167d"
+TRAFFIC_SRC = "9a61a67b337d3195"
 TRAFFIC_SOURCES = ("ggemm.hip", "common.h", "permute.hip", "combine.hip")
 TRAFFIC = {
     # profiles/hbm_traffic_long_ctx_swiglu.md
     "long_ctx_swiglu": {
-        "perm_copy": 9672121672,
-        "gemm_up_swiglu": 704386564743,
-        "gemm_down": 235027195230,
-        "combine": 9680330649,
-        "combine_bwd": 18275054337,
-        "gemm_dA_swiglu": 462354667185,
-        "gemm_dW2": 542665044463,
-        "gemm_dW1": 542665044463,
-        "gemm_dW3": 542665044463,
-        "gemm_dX": 502824473624,
-        "unpermute_grad": 10745674319,
+        "perm_copy": 9672120588,
+        "gemm_up_swiglu": 675371618163,
+        "gemm_down": 250493368193,
+        "combine": 9680336226,
+        "combine_bwd": 18275051498,
+        "gemm_dA_swiglu": 434819912311,
+        "gemm_dW2": 547860914315,
+        "gemm_dW1": 547860914315,
+        "gemm_dW3": 547860914315,
+        "gemm_dX": 505702222537,
+        "unpermute_grad": 10745678739,
     },
     # profiles/hbm_traffic_moe_s_like.md
     "moe_s_like": {
-        "perm_copy": 101243301,
-        "gemm_up_gelu": 1186665309,
-        "gemm_down": 785601616,
-        "combine": 101795146,
-        "combine_bwd": 169050873,
-        "gemm_dA_gelu": 1187262076,
-        "gemm_dW2": 1141104061,
-        "gemm_dW1": 1141104061,
-        "gemm_dX": 784834373,
-        "unpermute_grad": 134847727,
+        "perm_copy": 101237260,
+        "gemm_up_gelu": 1186836927,
+        "gemm_down": 787437457,
+        "combine": 101795537,
+        "combine_bwd": 169050782,
+        "gemm_dA_gelu": 1187139072,
+        "gemm_dW2": 1141103332,
+        "gemm_dW1": 1141103332,
+        "gemm_dX": 784823713,
+        "unpermute_grad": 134847709,
     },
     # profiles/hbm_traffic_skewed_zipf1.2.md
     "skewed_zipf1.2": {
-        "perm_copy": 403743014,
-        "gemm_up_gelu": 6893505786,
-        "gemm_down": 5436096535,
-        "combine": 404829005,
-        "combine_bwd": 673548276,
-        "gemm_dA_gelu": 6664836637,
-        "gemm_dW2": 4300262551,
-        "gemm_dW1": 4300262551,
-        "gemm_dX": 5461043045,
-        "unpermute_grad": 538016151,
+        "perm_copy": 403743052,
+        "gemm_up_gelu": 7044032188,
+        "gemm_down": 5440844010,
+        "combine": 404828641,
+        "combine_bwd": 673548452,
+        "gemm_dA_gelu": 6704877733,
+        "gemm_dW2": 4303758137,
+        "gemm_dW1": 4303758137,
+        "gemm_dX": 5486885433,
+        "unpermute_grad": 538016044,
     },
 }
 
