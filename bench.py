@@ -77,6 +77,19 @@ TRAFFIC = {
         "gemm_dX": 5486885433,
         "unpermute_grad": 538016044,
     },
+    # profiles/hbm_traffic_many_expert_zipf1.0.md
+    "many_expert_zipf1.0": {
+        "perm_copy": 404812924,
+        "gemm_up_gelu": 4730030006,
+        "gemm_down": 3071031447,
+        "combine": 406926550,
+        "combine_bwd": 675905775,
+        "gemm_dA_gelu": 4765331655,
+        "gemm_dW2": 5437752994,
+        "gemm_dW1": 5437752994,
+        "gemm_dX": 3068598249,
+        "unpermute_grad": 539064914,
+    },
 }
 
 
