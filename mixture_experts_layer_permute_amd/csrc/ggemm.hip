@@ -715,10 +715,15 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // Wait until at most N direct-to-LDS loads of this wave are in flight and
-// its LDS reads have returned, then meet the other waves of the block.
+// its LDS reads have returned, then meet the other waves of the block.  The
+// compiler does not read the wait inside the asm; the lgkmcnt(0) after it
+// (which then costs nothing) tells it that no LDS read is outstanding, so
+// its own waits for the next fragments count only the reads issued after
+// the barrier instead of draining them all (dW products 2-3% faster).
 template <int N>
 __device__ __forceinline__ void stage_barrier() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);                // lgkmcnt(0), no vmcnt wait
 }
 // stage_barrier with `ahead` (0..MAXA, wave-uniform) later stages of NL loads
 // each allowed to stay in flight
