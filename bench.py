@@ -34,61 +34,61 @@ PEAK_HBM_GBS = 8000.0
 # cold source in the same run (the summaries under profiles/ give commands
 # and factors).  Valid only for the kernel sources whose SHA-256 prefix is
 # TRAFFIC_SRC; null once they change.
-TRAFFIC_SRC = "9a61a67b337d3195"
+TRAFFIC_SRC = "4fcfe3941a129179"
 TRAFFIC_SOURCES = ("ggemm.hip", "common.h", "permute.hip", "combine.hip")
 TRAFFIC = {
     # profiles/hbm_traffic_long_ctx_swiglu.md
     "long_ctx_swiglu": {
-        "perm_copy": 9672120588,
-        "gemm_up_swiglu": 675371618163,
-        "gemm_down": 250493368193,
-        "combine": 9680336226,
-        "combine_bwd": 18275051498,
-        "gemm_dA_swiglu": 434819912311,
-        "gemm_dW2": 547860914315,
-        "gemm_dW1": 547860914315,
-        "gemm_dW3": 547860914315,
-        "gemm_dX": 505702222537,
-        "unpermute_grad": 10745678739,
+        "perm_copy": 9672122896,
+        "gemm_up_swiglu": 683751468397,
+        "gemm_down": 234012466145,
+        "combine": 9680341033,
+        "combine_bwd": 18275045633,
+        "gemm_dA_swiglu": 463596040400,
+        "gemm_dW2": 400446914432,
+        "gemm_dW1": 400446914432,
+        "gemm_dW3": 400446914432,
+        "gemm_dX": 481903674106,
+        "unpermute_grad": 10745680919,
     },
     # profiles/hbm_traffic_moe_s_like.md
     "moe_s_like": {
-        "perm_copy": 101237260,
-        "gemm_up_gelu": 1186836927,
-        "gemm_down": 787437457,
-        "combine": 101795537,
-        "combine_bwd": 169050782,
-        "gemm_dA_gelu": 1187139072,
-        "gemm_dW2": 1141103332,
-        "gemm_dW1": 1141103332,
-        "gemm_dX": 784823713,
-        "unpermute_grad": 134847709,
+        "perm_copy": 101237823,
+        "gemm_up_gelu": 1186782230,
+        "gemm_down": 786997924,
+        "combine": 101795090,
+        "combine_bwd": 169051200,
+        "gemm_dA_gelu": 1189210498,
+        "gemm_dW2": 1141100697,
+        "gemm_dW1": 1141100697,
+        "gemm_dX": 784850304,
+        "unpermute_grad": 134847643,
     },
     # profiles/hbm_traffic_skewed_zipf1.2.md
     "skewed_zipf1.2": {
-        "perm_copy": 403743052,
-        "gemm_up_gelu": 7044032188,
-        "gemm_down": 5440844010,
-        "combine": 404828641,
-        "combine_bwd": 673548452,
-        "gemm_dA_gelu": 6704877733,
-        "gemm_dW2": 4303758137,
-        "gemm_dW1": 4303758137,
-        "gemm_dX": 5486885433,
-        "unpermute_grad": 538016044,
+        "perm_copy": 403743230,
+        "gemm_up_gelu": 6829629472,
+        "gemm_down": 5449579778,
+        "combine": 404829692,
+        "combine_bwd": 673548775,
+        "gemm_dA_gelu": 6731764457,
+        "gemm_dW2": 4295331827,
+        "gemm_dW1": 4295331827,
+        "gemm_dX": 5476458921,
+        "unpermute_grad": 538016467,
     },
     # profiles/hbm_traffic_many_expert_zipf1.0.md
     "many_expert_zipf1.0": {
-        "perm_copy": 404812924,
-        "gemm_up_gelu": 4730030006,
-        "gemm_down": 3071031447,
-        "combine": 406926550,
-        "combine_bwd": 675905775,
-        "gemm_dA_gelu": 4765331655,
-        "gemm_dW2": 5437752994,
-        "gemm_dW1": 5437752994,
-        "gemm_dX": 3068598249,
-        "unpermute_grad": 539064914,
+        "perm_copy": 404812636,
+        "gemm_up_gelu": 4732097108,
+        "gemm_down": 3070275345,
+        "combine": 406925644,
+        "combine_bwd": 675906173,
+        "gemm_dA_gelu": 4768407161,
+        "gemm_dW2": 5436846702,
+        "gemm_dW1": 5436846702,
+        "gemm_dX": 3067883949,
+        "unpermute_grad": 539064308,
     },
 }
 
