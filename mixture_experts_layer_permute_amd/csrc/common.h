@@ -131,6 +131,48 @@ __device__ __forceinline__ u32x4_t pack16(const float* o) {
 }
 constexpr long kMallBytes = 256l << 20;
 
+// ------------------------------------------------------- wave/block scans
+
+// Inclusive prefix sum of v over the 64 lanes of a wave, with DPP moves (no
+// LDS): lanes i-1, i-2, i-4, i-8 of the same 16-lane row are added in turn
+// (a source lane outside the row reads 0), which scans each row; then lane
+// 15 of rows 0 and 2 is added to rows 1 and 3 (row_bcast:15), and lane 31
+// (the sum of rows 0-1) to rows 2 and 3 (row_bcast:31).  Every lane of the
+// wave must be active.  Integer sums, so the result does not depend on the
+// order of the additions.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return v;
+}
+
+// Exclusive prefix sum of v over the NT threads of a block (NT a multiple of
+// 64, at most 1024), and the block's total in *total.  sh holds NT/64 ints
+// of LDS.  Every thread of the block must call it (it has block barriers).
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int* sh, int* total) {
+    static_assert(NT % 64 == 0 && NT <= 1024, "whole waves");
+    constexpr int NW = NT / 64;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int inc = wave_incl_scan(v);
+    if (lane == 63) sh[w] = inc;
+    __syncthreads();
+    int base = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const int t = sh[i];
+        base += i < w ? t : 0;
+        tot += t;
+    }
+    __syncthreads();                         // sh may be reused after this
+    *total = tot;
+    return base + inc - v;
+}
+
 // ------------------------------------------------------------ host side
 
 // Checks (once per device) that the current device is gfx950 and returns

@@ -1230,21 +1230,26 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(const int32_t* __restric
                                                         int32_t* __restrict__ counts) {
     __shared__ int cnt[1024];
     __shared__ int ord[1024];
+    __shared__ int sh[16];
     const int e = threadIdx.x;
-    if (e < E) cnt[e] = offsets[e + 1] - offsets[e];
-    __syncthreads();
+    const int c_e = e < E ? offsets[e + 1] - offsets[e] : 0;
+    if (e < E) cnt[e] = c_e;
+    // per-expert prefixes of the row tiles, of the full row tiles and of the
+    // experts with a partial last tile (block scans; experts in index order)
+    int tot_tiles, tot_full, tot_part;
+    const int p_tiles = block_excl_scan<1024>((c_e + bm - 1) / bm, sh, &tot_tiles);
+    const int p_full = block_excl_scan<1024>(c_e / bm, sh, &tot_full);
+    const int has_part = e < E && c_e % bm != 0;
+    const int p_part = block_excl_scan<1024>(has_part, sh, &tot_part);
+    if (e < E) {
+        tile_prefix[e] = p_tiles;
+        full_prefix[e] = p_full;
+        if (has_part) part_list[p_part] = e;
+    }
     if (e == 0) {
-        int run = 0, full = 0, np = 0;
-        for (int q = 0; q < E; ++q) {
-            tile_prefix[q] = run;
-            full_prefix[q] = full;
-            run += (cnt[q] + bm - 1) / bm;
-            full += cnt[q] / bm;
-            if (cnt[q] % bm) part_list[np++] = q;
-        }
-        tile_prefix[E] = run;
-        full_prefix[E] = full;
-        part_list[E] = np;
+        tile_prefix[E] = tot_tiles;
+        full_prefix[E] = tot_full;
+        part_list[E] = tot_part;
     }
     if (e < E) {
         const int c = cnt[e];
@@ -1257,10 +1262,15 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(const int32_t* __restric
         ord[rank] = e;
     }
     __syncthreads();
-    if (items && e == 0) {
+    if (!items) return;
+    // dW work items: the chunks of the split segments (heaviest first), then
+    // the whole segments in rank order.  Only the heaviest experts can split,
+    // so the first loop is short; its counts reach the other threads in LDS.
+    __shared__ int nsplit[2];
+    if (e == 0) {
         int ni = 0, ns = 0, slot = 0;
         const bool may_split = dw_tiles < kSplitTiles;
-        for (int r = 0; r < E; ++r) {               // split segments, heaviest first
+        for (int r = 0; r < E; ++r) {
             const int q = ord[r], n = cnt[q];
             if (!may_split || n <= 2 * kSplitRows) break;   // the rest are shorter
             const int kc = split_chunk_rows(n);
@@ -1270,12 +1280,16 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(const int32_t* __restric
             splits[ns++] = make_int4(q, slot, nc, 0);
             slot += nc;
         }
-        for (int r = ns; r < E; ++r) {              // whole segments
-            const int q = ord[r];
-            items[ni++] = make_int4(q, offsets[q], cnt[q], -1);
-        }
-        counts[0] = ni;
+        nsplit[0] = ni;
+        nsplit[1] = ns;
+        counts[0] = ni + (E - ns);
         counts[1] = ns;
+    }
+    __syncthreads();
+    const int ni = nsplit[0], ns = nsplit[1];
+    if (e >= ns && e < E) {                         // whole segments
+        const int q = ord[e];
+        items[ni + (e - ns)] = make_int4(q, offsets[q], cnt[q], -1);
     }
 }
 

@@ -47,7 +47,7 @@ __global__ __launch_bounds__(256) void perm_hist_kernel(
 __global__ __launch_bounds__(256) void perm_scan_kernel(
     const int32_t* __restrict__ block_counts, int nblk,
     int32_t* __restrict__ block_base, int32_t* __restrict__ counts) {
-    __shared__ int part[256];
+    __shared__ int sh[4];
     const int e = blockIdx.x;
     const int32_t* in = block_counts + (long)e * nblk;
     int32_t* out = block_base + (long)e * nblk;
@@ -55,19 +55,9 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(
     const int lo = threadIdx.x * per, hi = min(nblk, lo + per);
     int s = 0;
     for (int i = lo; i < hi; ++i) s += in[i];
-    part[threadIdx.x] = s;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int run = 0;
-        for (int i = 0; i < 256; ++i) {
-            const int v = part[i];
-            part[i] = run;
-            run += v;
-        }
-        counts[e] = run;
-    }
-    __syncthreads();
-    int run = part[threadIdx.x];
+    int total;
+    int run = block_excl_scan<256>(s, sh, &total);   // DPP wave scans, then the 4 wave sums
+    if (threadIdx.x == 0) counts[e] = total;
     for (int i = lo; i < hi; ++i) {
         const int v = in[i];
         out[i] = run;
@@ -99,14 +89,21 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int b = blockIdx.x;
 
-    // expert offsets: exclusive scan of counts (one thread, E <= 1024)
-    if (tid == 0) {
-        int run = 0;
-        for (int e = 0; e < E; ++e) {
+    // expert offsets: exclusive scan of counts (E <= 1024: up to 4
+    // consecutive experts per thread, then a block scan of the threads' sums)
+    {
+        __shared__ int sh[4];
+        const int per = (E + 255) / 256;
+        const int lo = min(E, tid * per), hi = min(E, lo + per);
+        int s = 0;
+        for (int e = lo; e < hi; ++e) s += counts[e];
+        int total;
+        int run = block_excl_scan<256>(s, sh, &total);
+        for (int e = lo; e < hi; ++e) {
             offs[e] = run;
             run += counts[e];
         }
-        offs[E] = run;
+        if (tid == 0) offs[E] = total;
     }
     for (int q = tid; q < 4 * E; q += 256) wcnt[q] = 0;
     __syncthreads();
