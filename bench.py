@@ -34,61 +34,61 @@ PEAK_HBM_GBS = 8000.0
 # cold source in the same run (the summaries under profiles/ give commands
 # and factors).  Valid only for the kernel sources whose SHA-256 prefix is
 # TRAFFIC_SRC; null once they change.
-TRAFFIC_SRC = "4fcfe3941a129179"
+TRAFFIC_SRC = "589c5b7c6cc90e77"
 TRAFFIC_SOURCES = ("ggemm.hip", "common.h", "permute.hip", "combine.hip")
 TRAFFIC = {
     # profiles/hbm_traffic_long_ctx_swiglu.md
     "long_ctx_swiglu": {
-        "perm_copy": 9672122896,
-        "gemm_up_swiglu": 683751468397,
-        "gemm_down": 234012466145,
-        "combine": 9680341033,
-        "combine_bwd": 18275045633,
-        "gemm_dA_swiglu": 463596040400,
-        "gemm_dW2": 400446914432,
-        "gemm_dW1": 400446914432,
-        "gemm_dW3": 400446914432,
-        "gemm_dX": 481903674106,
-        "unpermute_grad": 10745680919,
+        "perm_copy": 9672123353,
+        "gemm_up_swiglu": 689820602202,
+        "gemm_down": 242334014921,
+        "combine": 9680413048,
+        "combine_bwd": 18275136241,
+        "gemm_dA_swiglu": 448708358544,
+        "gemm_dW2": 404789088976,
+        "gemm_dW1": 404789088976,
+        "gemm_dW3": 404789088976,
+        "gemm_dX": 533224621498,
+        "unpermute_grad": 10745768156,
     },
     # profiles/hbm_traffic_moe_s_like.md
     "moe_s_like": {
-        "perm_copy": 101237823,
-        "gemm_up_gelu": 1186782230,
-        "gemm_down": 786997924,
-        "combine": 101795090,
-        "combine_bwd": 169051200,
-        "gemm_dA_gelu": 1189210498,
-        "gemm_dW2": 1141100697,
-        "gemm_dW1": 1141100697,
-        "gemm_dX": 784850304,
-        "unpermute_grad": 134847643,
+        "perm_copy": 101236421,
+        "gemm_up_gelu": 1186694454,
+        "gemm_down": 787036658,
+        "combine": 101795431,
+        "combine_bwd": 169050742,
+        "gemm_dA_gelu": 1187759393,
+        "gemm_dW2": 1141096171,
+        "gemm_dW1": 1141096171,
+        "gemm_dX": 784843139,
+        "unpermute_grad": 134847824,
     },
     # profiles/hbm_traffic_skewed_zipf1.2.md
     "skewed_zipf1.2": {
-        "perm_copy": 403743230,
-        "gemm_up_gelu": 6829629472,
-        "gemm_down": 5449579778,
-        "combine": 404829692,
-        "combine_bwd": 673548775,
-        "gemm_dA_gelu": 6731764457,
-        "gemm_dW2": 4295331827,
-        "gemm_dW1": 4295331827,
-        "gemm_dX": 5476458921,
-        "unpermute_grad": 538016467,
+        "perm_copy": 403735378,
+        "gemm_up_gelu": 6878476489,
+        "gemm_down": 5452075064,
+        "combine": 404830042,
+        "combine_bwd": 673549345,
+        "gemm_dA_gelu": 6699742448,
+        "gemm_dW2": 4296819579,
+        "gemm_dW1": 4296819579,
+        "gemm_dX": 5564916419,
+        "unpermute_grad": 538017373,
     },
     # profiles/hbm_traffic_many_expert_zipf1.0.md
     "many_expert_zipf1.0": {
-        "perm_copy": 404812636,
-        "gemm_up_gelu": 4732097108,
-        "gemm_down": 3070275345,
-        "combine": 406925644,
-        "combine_bwd": 675906173,
-        "gemm_dA_gelu": 4768407161,
-        "gemm_dW2": 5436846702,
-        "gemm_dW1": 5436846702,
-        "gemm_dX": 3067883949,
-        "unpermute_grad": 539064308,
+        "perm_copy": 404798751,
+        "gemm_up_gelu": 4728235491,
+        "gemm_down": 3069672756,
+        "combine": 406925596,
+        "combine_bwd": 675904938,
+        "gemm_dA_gelu": 4764497193,
+        "gemm_dW2": 5436864361,
+        "gemm_dW1": 5436864361,
+        "gemm_dX": 3068233610,
+        "unpermute_grad": 539064416,
     },
 }
 
