@@ -22,6 +22,10 @@ GATE_CASES = [  # T, d, E, k, bias, renorm
     (300, 64, 4, 1, False, 1), (200, 64, 100, 3, True, 1),
     (64, 128, 128, 8, True, 0), (33, 64, 5, 5, False, 1),
     (40, 64, 1, 1, False, 1), (1, 64, 64, 4, True, 1), (16, 72, 1024, 3, False, 1),
+    # grids of at least two blocks per compute unit take the logits kernel's
+    # 2-token x 8-expert form: ragged tokens and experts, a partial feature
+    # chunk (136 = 2 x 64 + 8), and the threshold itself (512 blocks)
+    (20000, 136, 100, 3, True, 1), (32768, 64, 64, 2, False, 1),
 ]
 
 
