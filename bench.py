@@ -172,6 +172,10 @@ def parse():
                          "in pinned host memory, uploaded this many experts at a time "
                          "beside the GEMMs (OffloadedMoELayer); reported as "
                          "'offloaded', never as the value (it includes PCIe)")
+    ap.add_argument("--pin-frac", type=float, default=0.0,
+                    help="with --offload-experts: keep this fraction of the experts, "
+                         "the most routed in the headline step, on the GPU (expert "
+                         "pinning); their weights are not moved each step")
     ap.add_argument("--flush-mall", action="store_true",
                     help="add a per-kernel pass that reads a 512 MiB buffer before "
                          "every entry point, so memory kernels read from HBM")
@@ -723,14 +727,16 @@ def main():
         del fl
         layer = None
     if args.offload_experts and not args.chunk_tokens:
+        counts = None
         if layer is not None:             # the headline layer's buffers out of HBM
             y0 = layer.y.clone()
+            counts = layer.counts.cpu()
             del layer
-        out["offloaded"] = offloaded_pass(args, cfg, t, y0, s, stream)
+        out["offloaded"] = offloaded_pass(args, cfg, t, y0, s, stream, counts)
     print(json.dumps(out), flush=True)
 
 
-def offloaded_pass(args, cfg, t, y0, s, stream):
+def offloaded_pass(args, cfg, t, y0, s, stream, counts=None):
     """The same step with the expert weights in pinned host memory
     (OffloadedMoELayer): the weights of G experts at a time are uploaded
     beside the GEMMs, the weight gradients downloaded.  The device copies of
@@ -751,8 +757,11 @@ def offloaded_pass(args, cfg, t, y0, s, stream):
     torch.cuda.empty_cache()
     torch.cuda.reset_peak_memory_stats()
     G = args.offload_experts
+    pinned = (M.OffloadedMoELayer.most_routed(counts, args.pin_frac)
+              if args.pin_frac > 0 and counts is not None else [])
     lay = M.OffloadedMoELayer(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.act,
-                              device.torch_dtype(cfg), cfg.renorm, group_experts=G)
+                              device.torch_dtype(cfg), cfg.renorm, group_experts=G,
+                              pinned=pinned)
     lay.bind(t["x"], t["Wg"], W1, W2, W3, t["bias"], t["dy"])
     for _ in range(args.warmup):
         lay.step(s)
@@ -769,16 +778,20 @@ def offloaded_pass(args, cfg, t, y0, s, stream):
     b = 2 if cfg.dtype == "bf16" else 4
     per_expert = cfg.d * cfg.f * (3 if cfg.swiglu else 2) * b
     n = len(lay.groups)
-    # uploads: every group in the forward, all but the last two again in the
-    # backward; downloads: every expert's weight gradients
-    up = (cfg.E + sum(ne for _, ne in lay.groups[:max(0, n - 2)])) * per_expert
-    down = cfg.E * per_expert
-    return {"experts_per_group": lay.G, "ms_per_step": round(ms, 5),
+    off_experts = cfg.E - len(pinned)
+    # uploads: every offloaded group in the forward, all but the last two
+    # again in the backward; downloads: every offloaded expert's weight
+    # gradients (pinned experts' weights and gradients stay on the GPU)
+    up = (off_experts + sum(ne for _, ne in lay.groups[:max(0, n - 2)])) * per_expert
+    down = off_experts * per_expert
+    return {"experts_per_group": lay.G, "pinned_experts": len(pinned),
+            "ms_per_step": round(ms, 5),
             "value": round(cfg.T / (ms * 1e-3), 1), "unit": "tokens/s",
             "pcie_bytes_per_step": up + down,
             "pcie_gbs": round((up + down) / (ms * 1e-3) / 1e9, 1),
             "hbm_peak_bytes": torch.cuda.max_memory_allocated(),
             "expert_weight_bytes_on_host": cfg.E * per_expert,
+            "pinned_weight_bytes_on_gpu": len(pinned) * per_expert,
             "y_bit_identical": bool(torch.equal(y0, lay.y))}
 
 

@@ -5,6 +5,8 @@ forward:  moe_gate_topk -> moe_permute -> moe_expert_ffn_fwd -> moe_combine
 backward: moe_combine_bwd -> (moe_gate_topk_bwd on a second stream, writes
           dx) and moe_expert_ffn_bwd -> moe_unpermute_grad (adds to dx)
 """
+import math
+
 import torch
 
 from ._lib import MOE_ACT_GELU, MOE_ACT_SWIGLU, MOE_BF16, MOE_F32, check, load
@@ -349,6 +351,28 @@ class ChunkedMoELayer:
         self.backward(stream)
 
 
+def offload_groups(E, G, pinned):
+    """The expert calls of OffloadedMoELayer: offloaded groups (e0, ne), runs
+    of unpinned experts cut into at most G, and resident runs (e0, ne, p0),
+    maximal runs of consecutive pinned experts whose weights are rows
+    p0 .. p0+ne-1 of the pinned tensors (pinned: increasing expert ids)."""
+    pin = {e: j for j, e in enumerate(pinned)}
+    groups, resident = [], []
+    e = 0
+    while e < E:
+        e1 = e + 1
+        if e in pin:
+            while e1 < E and e1 in pin:
+                e1 += 1
+            resident.append((e, e1 - e, pin[e]))
+        else:
+            while e1 < E and e1 not in pin and e1 - e < G:
+                e1 += 1
+            groups.append((e, e1 - e))
+        e = e1
+    return groups, resident
+
+
 class OffloadedMoELayer:
     """The layer step with the expert weights in pinned host memory and only
     the weights (and weight gradients) of G experts on the GPU at a time:
@@ -371,6 +395,24 @@ class OffloadedMoELayer:
     A group call passes offsets + e0 and the group's expert count; rows stay
     absolute, so every tile is the same fixed-order sum as in MoELayer and
     every output (y, dx, dWg, dW1, dW2, dW3) is bit-identical to it.
+
+    Expert pinning (ES-MoE review, 三 技术架构 / 自适应卸载: the most
+    frequently routed quarter of the experts is kept on the GPU to cut the
+    transfers): the experts listed in `pinned` are copied to the GPU once, at
+    bind(), into W1p/W2p/W3p [P, ...] (pinned order), and their weight
+    gradients go to dW1p/dW2p/dW3p on the GPU (in the step's stream order;
+    grads_ready covers the host gradients only); those two sets are the
+    pinned experts' weights and gradients from then on (the host tensors'
+    rows of pinned experts are neither read again nor written).  Runs of
+    consecutive pinned experts are one call each.  They run first in the
+    forward, while both staging slots fill, and right after the first
+    offloaded group in the backward, while the slot that group frees is
+    refilled: the most routed experts carry the most compute, and it hides
+    those transfers.  (Dealing them in shares between all the groups was
+    slower: skewed workload, 4 of 16 pinned, 40.6-44.4 against 32.6 ms.)
+    The other experts form the offloaded groups of at most G.  Grouping
+    changes no bits: every expert's rows are the same tiles in any call.
+    most_routed(counts, frac) picks such a list from a routing histogram.
     Inputs: x, Wg, logit_bias, dy on the GPU; W1, W2, W3 as pinned host
     tensors (bind).  dW1, dW2, dW3 are pinned host tensors, final once the
     event grads_ready has completed (grads_ready.synchronize(), a stream that
@@ -382,7 +424,7 @@ class OffloadedMoELayer:
     """
 
     def __init__(self, T, d, f, E, k, act="gelu", dtype=torch.bfloat16, renorm=1,
-                 device="cuda", group_experts=4):
+                 device="cuda", group_experts=4, pinned=()):
         self.T, self.d, self.f, self.E, self.k = T, d, f, E, k
         self.act = MOE_ACT_SWIGLU if act == "swiglu" else MOE_ACT_GELU
         self.dtype = dtype
@@ -390,7 +432,10 @@ class OffloadedMoELayer:
         self.renorm = renorm
         self.device = torch.device(device)
         self.G = G = max(1, min(int(group_experts), E))
-        self.groups = [(e0, min(G, E - e0)) for e0 in range(0, E, G)]
+        self.pinned = sorted({int(e) for e in pinned})
+        assert all(0 <= e < E for e in self.pinned), "pinned experts out of range"
+        self.groups, self.resident = offload_groups(E, G, self.pinned)
+        gmax = max([ne for _, ne in self.groups] + [ne for _, ne, _ in self.resident])
         L = self.lib = load()
         R = self.R = T * k
         dev = self.device
@@ -416,6 +461,14 @@ class OffloadedMoELayer:
         self.dx_perm = e(R, d)
         self.dx = e(T, d)
         self.dWg = e(d, E)
+        # the pinned experts' weights and weight gradients, on the GPU
+        P = len(self.pinned)
+        self.W1p = e(P, d, f) if P else None
+        self.W2p = e(P, f, d) if P else None
+        self.W3p = e(P, d, f) if P and sw else None
+        self.dW1p = e(P, d, f) if P else None
+        self.dW2p = e(P, f, d) if P else None
+        self.dW3p = e(P, d, f) if P and sw else None
         # two staging slots of G experts' weights and weight gradients
         self.W1s = [e(G, d, f) for _ in range(2)]
         self.W2s = [e(G, f, d) for _ in range(2)]
@@ -429,17 +482,26 @@ class OffloadedMoELayer:
         self.dW3 = h(E, d, f) if sw else None
         ws = lambda n: torch.empty(max(int(n), 1), dtype=torch.uint8, device=dev)
         self.ws_perm = ws(L.moe_permute_workspace_bytes(T, E, k))
-        self.ws_ffn_f = ws(L.moe_ffn_workspace_bytes(R, G, d, f, self.act, self.dt, 0))
-        self.ws_ffn_b = ws(L.moe_ffn_workspace_bytes(R, G, d, f, self.act, self.dt, 1))
+        self.ws_ffn_f = ws(L.moe_ffn_workspace_bytes(R, gmax, d, f, self.act, self.dt, 0))
+        self.ws_ffn_b = ws(L.moe_ffn_workspace_bytes(R, gmax, d, f, self.act, self.dt, 1))
         self.ws_gate = ws(L.moe_gate_bwd_workspace_bytes(T, d, E))
         self._up_stream = torch.cuda.Stream(device=dev)
         self._dn_stream = torch.cuda.Stream(device=dev)
         ev = lambda: [torch.cuda.Event(), torch.cuda.Event()]
         self._up, self._free, self._dl = ev(), ev(), ev()
         self._slot = [-1, -1]          # group whose weights each slot holds
+        self._pin_ready = torch.cuda.Event()
         # recorded on the download stream once a backward's weight gradients
         # are all on the host
         self.grads_ready = torch.cuda.Event()
+
+    @staticmethod
+    def most_routed(counts, frac=0.25):
+        """The ceil(frac * E) experts with the most rows in a routing
+        histogram (ties: lower index first), in increasing order."""
+        c = [int(v) for v in torch.as_tensor(counts).detach().cpu().tolist()]
+        n = min(len(c), math.ceil(frac * len(c)))
+        return sorted(sorted(range(len(c)), key=lambda e: (-c[e], e))[:n])
 
     def bind(self, x, Wg, W1, W2, W3=None, logit_bias=None, dy=None):
         """x, Wg, logit_bias, dy on the GPU; W1 [E,d,f], W2 [E,f,d], W3 as
@@ -455,6 +517,15 @@ class OffloadedMoELayer:
         self.x, self.Wg, self.bias, self.dy = x, Wg, logit_bias, dy
         self.W1h, self.W2h, self.W3h = W1, W2, W3
         self._slot = [-1, -1]
+        if self.pinned:                # the pinned experts' weights, once
+            us = self._up_stream
+            with torch.cuda.stream(us):
+                for j, e in enumerate(self.pinned):
+                    self.W1p[j].copy_(W1[e], non_blocking=True)
+                    self.W2p[j].copy_(W2[e], non_blocking=True)
+                    if W3 is not None:
+                        self.W3p[j].copy_(W3[e], non_blocking=True)
+            self._pin_ready.record(us)
         return self
 
     def _upload(self, g):
@@ -489,7 +560,20 @@ class OffloadedMoELayer:
         n = len(self.groups)
         # the host weights may have changed since the last step: upload all
         self._slot = [-1, -1]
-        self._upload(0)
+        for g in range(min(n, 2)):     # both slots before any compute
+            self._upload(g)
+        if self.resident:
+            ms.wait_event(self._pin_ready)
+
+        def pinned_fwd(runs):
+            for e0, ne, p0 in runs:
+                check(L.moe_expert_ffn_fwd(p(self.x_perm), p(self.offsets) + 4 * e0, R, ne, d,
+                                           f, a, dt, p(self.W1p[p0]),
+                                           p(self.W3p[p0]) if self.W3p is not None else None,
+                                           p(self.W2p[p0]), p(self.h_save), p(self.a_save),
+                                           p(self.out_perm), p(self.ws_ffn_f),
+                                           self.ws_ffn_f.numel(), s), "moe_expert_ffn_fwd")
+        pinned_fwd(self.resident)
         for g, (e0, ne) in enumerate(self.groups):
             b = g % 2
             if g + 1 < n:
@@ -519,8 +603,20 @@ class OffloadedMoELayer:
                                   p(self.topk_w), p(self.d_topk_w), T, d, E, k, self.renorm,
                                   dt, p(self.dx), 0, p(self.dWg), p(self.ws_gate),
                                   self.ws_gate.numel(), s), "moe_gate_topk_bwd")
-        order = list(range(len(self.groups)))[::-1]   # the forward's last groups are resident
-        self._upload(order[0])
+        order = list(range(len(self.groups)))[::-1]   # the forward's last groups are staged
+        if order:
+            self._upload(order[0])
+
+        def pinned_bwd(runs):          # pinned experts: gradients stay on the GPU
+            for e0, ne, p0 in runs:
+                check(L.moe_expert_ffn_bwd(p(self.d_out_perm), p(self.x_perm), p(self.h_save),
+                                           p(self.a_save), p(self.offsets) + 4 * e0, R, ne, d,
+                                           f, a, dt, p(self.W1p[p0]),
+                                           p(self.W3p[p0]) if self.W3p is not None else None,
+                                           p(self.W2p[p0]), p(self.dx_perm), p(self.dW1p[p0]),
+                                           p(self.dW3p[p0]) if self.dW3p is not None else None,
+                                           p(self.dW2p[p0]), p(self.ws_ffn_b),
+                                           self.ws_ffn_b.numel(), s), "moe_expert_ffn_bwd")
         pending = [None, None]                # group whose dW a slot holds, not yet downloaded
         for i, g in enumerate(order):
             e0, ne = self.groups[g]
@@ -540,6 +636,10 @@ class OffloadedMoELayer:
                                        self.ws_ffn_b.numel(), s), "moe_expert_ffn_bwd")
             self._free[b].record(ms)
             pending[b] = g
+            if i == 0:                 # beside the refill of the slot just freed
+                pinned_bwd(self.resident)
+        if not order:
+            pinned_bwd(self.resident)
         check(L.moe_unpermute_grad(p(self.dx_perm), p(self.dest), T, k, d, dt, p(self.dx), 1,
                                    s), "moe_unpermute_grad")
         # the last groups' gradients go out after the step's GEMMs: downloads

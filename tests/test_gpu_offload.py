@@ -41,9 +41,10 @@ def whole_step(cfg, t, x=None, dy=None):
     return L
 
 
-def offloaded(cfg, t, G):
+def offloaded(cfg, t, G, pinned=()):
     L = M.OffloadedMoELayer(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.act,
-                            device.torch_dtype(cfg), cfg.renorm, group_experts=G)
+                            device.torch_dtype(cfg), cfg.renorm, group_experts=G,
+                            pinned=pinned)
     W3 = host_pinned(t["W3"]) if t["W3"] is not None else None
     L.bind(t["x"], t["Wg"], host_pinned(t["W1"]), host_pinned(t["W2"]), W3, t["bias"],
            t["dy"])
@@ -134,3 +135,41 @@ def test_offloaded_against_oracle():
     assert_close(off.dWg, gr["dWg"], dt, "dWg")
     for n in ("dW1", "dW2", "dW3"):
         assert_close(host(getattr(off, n)), gr[n], dt, n)
+
+
+PIN_CASES = [  # workload, overrides, experts per group, pinned (None: the most-routed quarter)
+    ("many_expert_zipf1.0", dict(T=1200, d=128, f=256, E=32, k=2), 6, None),
+    ("moe_s_like", dict(T=1000, d=256, f=512, E=10, k=2), 3, [0, 3, 4, 9]),
+    ("moe_s_like", dict(T=1000, d=256, f=512, E=10, k=2), 2, [2, 3, 4, 5, 6]),  # run > G
+    ("long_ctx_swiglu", dict(T=777, d=128, f=256, E=16, k=4), 5, None),
+    ("moe_s_like", dict(T=1000, d=256, f=512, E=8, k=2), 3, list(range(8))),    # all pinned
+    ("tiny_fp32", {}, 2, [1]),
+]
+
+
+@pytest.mark.parametrize("case", PIN_CASES)
+def test_pinned_experts_match_resident_layer(case):
+    """Pinned experts (weights copied to the GPU once, gradients kept there)
+    beside offloaded groups: every output bit-identical to MoELayer's, the
+    pinned experts' gradients in dW1p/dW2p/dW3p, the others' on the host."""
+    name, kw, G, pinned = case
+    cfg = small_variant(name, **kw)
+    t = device.gen_all(cfg)
+    ref = whole_step(cfg, t)
+    if pinned is None:
+        pinned = M.OffloadedMoELayer.most_routed(ref.counts, 0.25)
+    banner("offload pinned", cfg.short(), G, pinned)
+    off = offloaded(cfg, t, G, pinned)
+    for _ in range(2):                   # the second step reuses the pinned copies
+        off.step()
+    off.grads_ready.synchronize()
+    torch.cuda.synchronize()
+    for n in OUT:
+        assert torch.equal(getattr(off, n), getattr(ref, n)), n
+    rest = [e for e in range(cfg.E) if e not in pinned]
+    for n in ["dW1", "dW2"] + (["dW3"] if cfg.swiglu else []):
+        want = getattr(ref, n)
+        if rest:
+            assert torch.equal(getattr(off, n)[rest], want.cpu()[rest]), n
+        if pinned:
+            assert torch.equal(getattr(off, n + "p"), want[pinned]), n + "p"
