@@ -518,6 +518,8 @@ class OffloadedMoELayer:
         self.W1h, self.W2h, self.W3h = W1, W2, W3
         self._slot = [-1, -1]
         if self.pinned:                # the pinned experts' weights, once
+            # a step still in flight may read the pinned copies: let it finish
+            torch.cuda.synchronize(self.device)
             us = self._up_stream
             with torch.cuda.stream(us):
                 for j, e in enumerate(self.pinned):
