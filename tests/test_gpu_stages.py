@@ -26,6 +26,8 @@ GATE_CASES = [  # T, d, E, k, bias, renorm
     # 2-token x 8-expert form: ragged tokens and experts, a partial feature
     # chunk (136 = 2 x 64 + 8), and the threshold itself (512 blocks)
     (20000, 136, 100, 3, True, 1), (32768, 64, 64, 2, False, 1),
+    # and with 9-16 experts the 2-expert form
+    (16384, 64, 12, 2, True, 1), (20001, 264, 16, 3, False, 1),
 ]
 
 
