@@ -39,56 +39,56 @@ TRAFFIC_SOURCES = ("ggemm.hip", "common.h", "permute.hip", "combine.hip")
 TRAFFIC = {
     # profiles/hbm_traffic_long_ctx_swiglu.md
     "long_ctx_swiglu": {
-        "perm_copy": 9672123353,
-        "gemm_up_swiglu": 689820602202,
-        "gemm_down": 242334014921,
-        "combine": 9680413048,
-        "combine_bwd": 18275136241,
-        "gemm_dA_swiglu": 448708358544,
-        "gemm_dW2": 404789088976,
-        "gemm_dW1": 404789088976,
-        "gemm_dW3": 404789088976,
-        "gemm_dX": 533224621498,
-        "unpermute_grad": 10745768156,
+        "perm_copy": 9672113488,
+        "gemm_up_swiglu": 675337367104,
+        "gemm_down": 244399126200,
+        "combine": 9680338536,
+        "combine_bwd": 18275055792,
+        "gemm_dA_swiglu": 437912088844,
+        "gemm_dW2": 433428591098,
+        "gemm_dW1": 433428591098,
+        "gemm_dW3": 433428591098,
+        "gemm_dX": 537143830558,
+        "unpermute_grad": 10745682902,
     },
     # profiles/hbm_traffic_moe_s_like.md
     "moe_s_like": {
-        "perm_copy": 101236421,
-        "gemm_up_gelu": 1186694454,
-        "gemm_down": 787036658,
-        "combine": 101795431,
-        "combine_bwd": 169050742,
-        "gemm_dA_gelu": 1187759393,
-        "gemm_dW2": 1141096171,
-        "gemm_dW1": 1141096171,
-        "gemm_dX": 784843139,
-        "unpermute_grad": 134847824,
+        "perm_copy": 101234731,
+        "gemm_up_gelu": 1187248445,
+        "gemm_down": 787969826,
+        "combine": 101795049,
+        "combine_bwd": 169051084,
+        "gemm_dA_gelu": 1187034134,
+        "gemm_dW2": 1141094887,
+        "gemm_dW1": 1141094887,
+        "gemm_dX": 784842527,
+        "unpermute_grad": 134847691,
     },
     # profiles/hbm_traffic_skewed_zipf1.2.md
     "skewed_zipf1.2": {
-        "perm_copy": 403735378,
-        "gemm_up_gelu": 6878476489,
-        "gemm_down": 5452075064,
-        "combine": 404830042,
-        "combine_bwd": 673549345,
-        "gemm_dA_gelu": 6699742448,
-        "gemm_dW2": 4296819579,
-        "gemm_dW1": 4296819579,
-        "gemm_dX": 5564916419,
-        "unpermute_grad": 538017373,
+        "perm_copy": 403734895,
+        "gemm_up_gelu": 6883957853,
+        "gemm_down": 5444213871,
+        "combine": 404829698,
+        "combine_bwd": 673549588,
+        "gemm_dA_gelu": 6742331323,
+        "gemm_dW2": 4295596651,
+        "gemm_dW1": 4295596651,
+        "gemm_dX": 5525499427,
+        "unpermute_grad": 538017023,
     },
     # profiles/hbm_traffic_many_expert_zipf1.0.md
     "many_expert_zipf1.0": {
-        "perm_copy": 404798751,
-        "gemm_up_gelu": 4728235491,
-        "gemm_down": 3069672756,
-        "combine": 406925596,
-        "combine_bwd": 675904938,
-        "gemm_dA_gelu": 4764497193,
-        "gemm_dW2": 5436864361,
-        "gemm_dW1": 5436864361,
-        "gemm_dX": 3068233610,
-        "unpermute_grad": 539064416,
+        "perm_copy": 404799853,
+        "gemm_up_gelu": 4727341723,
+        "gemm_down": 3070802362,
+        "combine": 406925494,
+        "combine_bwd": 675905170,
+        "gemm_dA_gelu": 4763172657,
+        "gemm_dW2": 5436847951,
+        "gemm_dW1": 5436847951,
+        "gemm_dX": 3068617148,
+        "unpermute_grad": 539064210,
     },
 }
 

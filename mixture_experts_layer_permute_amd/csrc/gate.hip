@@ -510,8 +510,9 @@ moe_status launch_logits(const void* x, const void* Wg, const float* bias,
                                    logits, s);
     else if (E <= 16 && (long)cdiv(Tn, 32) * cdiv(E, 16) >= 2L * max(device_cus(), 1))
         // 2 experts per thread: 5 LDS bytes per multiply-add instead of 6
-        // (16 experts, 16384 tokens, d 2048: 51 -> 43 us), while the grid
-        // still gives every compute unit two blocks
+        // (16 experts, 16384 tokens, d 2048, x in the MALL: 51 -> 43 us; with
+        // x read from HBM, as in a layer step, about the same), while the
+        // grid still gives every compute unit two blocks
         logits_go<T, 16, 2, 1, 256>(dim3(cdiv(Tn, 32), cdiv(E, 16)), xp, wp, bias, Tn, d, E,
                                     logits, s);
     else if (E <= 16)
