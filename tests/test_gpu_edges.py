@@ -5,6 +5,7 @@ gate/permute cases, all against the oracle on the host copy of the inputs.
 * Every token routed to one expert (a large logit bias on it).
 * k = E: every token visits every expert.
 * T = 1 and a token count that is no multiple of any tile.
+* About a thousand experts of a few rows each, some of them empty.
 * Two runs of the same step give identical bits (no float atomics, fixed
   reduction orders), with side-stream overlap on.
 * Randomized (T, d, E, k, skew) for the gate and the permute, bit-exact
@@ -106,6 +107,21 @@ def test_k_equals_e(act):
     banner("edge k=E", act)
     layer, _ = layer_case(cfg)
     assert np.all(layer.counts.cpu().numpy() == cfg.T)
+
+
+@pytest.mark.parametrize("dt,zipf", [("bf16", 1.0), ("f32", None)])
+def test_many_small_experts(dt, zipf):
+    """About a thousand experts of a few rows each, some empty: the tile plan's
+    block scans over its 1024 threads, a partial tile for almost every
+    expert, and exact zero weight gradients for the empty ones."""
+    cfg = small(E=1000, k=4, T=1500, d=64, f=128, dtype=dt, zipf_s=zipf)
+    banner("edge many small experts", dt, zipf)
+    layer, _ = layer_case(cfg)
+    counts = layer.counts.cpu().numpy()
+    assert counts.sum() == cfg.T * cfg.k and (counts == 0).any()
+    for e in np.flatnonzero(counts == 0)[:50]:
+        assert float(layer.dW1[e].abs().max()) == 0.0
+        assert float(layer.dW2[e].abs().max()) == 0.0
 
 
 @pytest.mark.parametrize("T", [1, 17, 1031])
