@@ -32,9 +32,10 @@ PEAK_HBM_GBS = 8000.0
 # launches together) per workload, from rocprofv3 --pmc FETCH_SIZE and
 # WRITE_SIZE runs scaled by the readings of a plain 4 GiB device copy with a
 # cold source in the same run (the summaries under profiles/ give commands
-# and factors).  Valid only for the kernel sources whose SHA-256 prefix is
-# TRAFFIC_SRC; null once they change.
-TRAFFIC_SRC = "589c5b7c6cc90e77"
+# and factors).  Valid only for the kernel sources whose code (comments and
+# blank lines aside, see source_hash) has the SHA-256 prefix TRAFFIC_SRC;
+# null once it changes.
+TRAFFIC_SRC = "f29407460134209b"
 TRAFFIC_SOURCES = ("ggemm.hip", "common.h", "permute.hip", "combine.hip")
 TRAFFIC = {
     # profiles/hbm_traffic_long_ctx_swiglu.md
@@ -94,12 +95,17 @@ TRAFFIC = {
 
 
 def source_hash():
+    """SHA-256 prefix of the kernel sources' code: // comments and blank
+    lines are left out, so that a comment edit keeps the measured traffic."""
     import hashlib
     h = hashlib.sha256()
     for f in TRAFFIC_SOURCES:
         with open(os.path.join(ROOT, "mixture_experts_layer_permute_amd", "csrc", f),
-                  "rb") as fh:
-            h.update(fh.read())
+                  encoding="utf-8") as fh:
+            for line in fh:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

@@ -1026,8 +1026,9 @@ __global__ __launch_bounds__(64 * WM * WN, 2) void ggemm_bf16_dma_kernel(GemmArg
         const int qn = qc + 1 == NSTG ? 0 : qc + 1;    // slot of stage j+1
         const int qf = qc == 0 ? NSTG - 1 : qc - 1;    // slot of stage j-1 = j+NSTG-1
         const bool more = (NP < NSTG || j > 0) && j + NSTG - 1 < nj;
-        // a gathered issue waits on LDS (its row indices), so it goes behind
-        // the first MFMAs of the stage, whose fragments it waits for anyway
+        // a gathered issue (row indices read from LDS a stage ahead) goes
+        // behind the first k-step's MFMAs: at the top of the stage it was 2%
+        // slower on the long-context dW shapes (60.5 against 59.2-59.5 ms)
         if (!KGATHER && more) issue(ring(qf), j + NSTG - 1);
 #pragma unroll
         for (int ks = 0; ks + 1 < KS; ++ks) {
