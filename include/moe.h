@@ -34,9 +34,11 @@
  *  - Bit-reproducible: no float atomics; every reduction has a fixed order.
  *  - Limits: 1 <= k <= E <= 1024; T*k < 2^31; d a multiple of 8 for the gate
  *    and the permute, of 64 for the FFN, combine and unpermute; f a multiple
- *    of 64; device pointers to rows 16-byte aligned.  T = 0 is accepted and
- *    launches nothing, except that the gate backward still writes its dWg
- *    (all zeros).
+ *    of 64; device pointers to rows 16-byte aligned.  T = 0 (R = 0) is
+ *    accepted: nothing of the tokens is read and their pointers may be NULL;
+ *    outputs with entries are still written: the permute's counts and
+ *    offsets, the FFN backward's dW and the gate backward's dWg (all zeros;
+ *    dW unchanged by the accumulating FFN backward).
  *  - Threads: entry points are reentrant; concurrent calls on different
  *    streams must not share output or workspace buffers.
  */

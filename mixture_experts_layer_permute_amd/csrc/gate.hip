@@ -666,9 +666,11 @@ moe_status moe_gate_topk_bwd(const void* x, const void* Wg, const float* logits,
     MOE_CHECK_ARG(dt == MOE_F32 || dt == MOE_BF16);
     const int vec = dt == MOE_BF16 ? 8 : 4;
     MOE_CHECK_ARG(d % vec == 0);
-    MOE_CHECK_ARG(x && Wg && logits && topk_idx && topk_w && d_topk_w && dWg);
+    MOE_CHECK_ARG(Wg && dWg);
+    // T = 0: nothing of the tokens is read (empty tensors may have null
+    // pointers); dWg is still written (zeros)
+    MOE_CHECK_ARG(T == 0 || (x && logits && topk_idx && topk_w && d_topk_w && dx));
     MOE_CHECK_ARG(aligned16(x));
-    MOE_CHECK_ARG(T == 0 || dx);
     MOE_CHECK_ARG(dx == nullptr || aligned16(dx));
     if (ws_bytes < moe_gate_bwd_workspace_bytes(T, d, E) || !ws) return MOE_ERR_WORKSPACE;
     MOE_CHECK_DEVICE();

@@ -124,6 +124,25 @@ def test_no_gpu_means_error_not_fallback(lib):
     assert lib.moe_init(0) in (_lib.MOE_ERR_HIP, _lib.MOE_ERR_UNSUPPORTED)
 
 
+def test_empty_gate_backward_needs_no_token_pointers(lib):
+    """T = 0: the gate backward accepts NULL token pointers (empty tensors)
+    and gets past its argument checks to the device check (which fails here,
+    with no GPU); it still needs Wg and dWg, which it writes."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("GPU present")
+    N = None
+    buf = ctypes.create_string_buffer(1 << 16)
+    p = ctypes.addressof(buf) + (-ctypes.addressof(buf)) % 16
+    wsb = lib.moe_gate_bwd_workspace_bytes(0, 64, 4)
+    wbuf = ctypes.create_string_buffer(max(wsb, 16) + 16)
+    wp = ctypes.addressof(wbuf) + (-ctypes.addressof(wbuf)) % 16
+    args = lambda Wg, dWg: (N, Wg, N, N, N, N, 0, 64, 4, 2, 1, 1, N, 0, dWg, wp, wsb, N)
+    assert lib.moe_gate_topk_bwd(*args(p, p)) in (_lib.MOE_ERR_HIP, _lib.MOE_ERR_UNSUPPORTED)
+    assert lib.moe_gate_topk_bwd(*args(N, p)) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_gate_topk_bwd(*args(p, N)) == _lib.MOE_ERR_INVALID_ARG
+
+
 def _ctype_of(decl):
     """ctypes kind of one C parameter or return type in include/moe.h."""
     decl = decl.strip()

@@ -124,6 +124,38 @@ def test_many_small_experts(dt, zipf):
         assert float(layer.dW2[e].abs().max()) == 0.0
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_empty_input_through_every_entry_point(dt):
+    """T = 0 (so R = 0) through the layer's eight calls: every call succeeds,
+    counts and offsets are zeros, and the weight gradients that the calls
+    still write (dW1, dW2 and dWg) are exact zeros, over buffers that held
+    other values."""
+    E, k, d, f = 8, 2, 64, 128
+    banner("edge T=0", dt)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    x = torch.empty(0, d, dtype=tdt, device="cuda")
+    Wg = torch.randn(d, E, device="cuda").to(tdt)
+    logits, idx, w = M.moe_gate_topk(x, Wg, k)
+    counts, offsets, dest, src, xp = M.moe_permute(idx, x, E)
+    W1 = torch.randn(E, d, f, device="cuda").to(tdt)
+    W2 = torch.randn(E, f, d, device="cuda").to(tdt)
+    h, a, o = M.moe_expert_ffn_fwd(xp, offsets, W1, W2, None, "gelu")
+    y = M.moe_combine(o, dest, w)
+    dy = torch.empty(0, d, dtype=tdt, device="cuda")
+    d_out, dw = M.moe_combine_bwd(dy, o, dest, w)
+    dW1, dW2 = torch.ones_like(W1), torch.ones_like(W2)
+    dxp = torch.empty(0, d, dtype=tdt, device="cuda")
+    M.moe_expert_ffn_bwd(d_out, xp, h, a, offsets, W1, W2, None, "gelu",
+                         out=(dxp, dW1, None, dW2))
+    dx = M.moe_unpermute_grad(dxp, dest)
+    dWg = M.moe_gate_topk_bwd(x, Wg, logits, idx, w, dw, dx, dWg=torch.ones_like(Wg))
+    torch.cuda.synchronize()
+    assert y.shape == (0, d) and dx.shape == (0, d)
+    assert int(counts.abs().sum()) == 0 and int(offsets.abs().sum()) == 0
+    for n, g in (("dW1", dW1), ("dW2", dW2), ("dWg", dWg)):
+        assert float(g.float().abs().max()) == 0.0, n
+
+
 @pytest.mark.parametrize("T", [1, 17, 1031])
 def test_token_counts(T):
     cfg = small(T=T, E=6, k=2, dtype="bf16")
