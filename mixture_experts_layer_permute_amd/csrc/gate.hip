@@ -32,6 +32,11 @@ __device__ __forceinline__ void static_for(F&& f) {
     static_for_seq(f, std::make_integer_sequence<int, N>{});
 }
 
+// Top-k order: larger logit first, the lower expert index on a tie.
+__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
+    return va > vb || (va == vb && ia < ib);
+}
+
 // ------------------------------------------------------------ logits
 // Block: 256 threads.  TE experts per block column, EPT of them per thread
 // (experts tx, tx + TX, ...: rows a TX apart keep the LDS reads spread);
@@ -43,11 +48,15 @@ __device__ __forceinline__ void static_for(F&& f) {
 // consecutive features of one expert; the next NPF chunks are fetched into
 // registers while the current one is consumed.  With few experts a thread
 // has a single chain, so the chunk is long (256 features).
-template <typename T, int TE, int EPT, int MT, int GKC, int NPF>
+//
+// FUSE (E <= TE, one block column): the block holds every expert of its
+// tokens, so it also takes each token's top-k and gate weights (below).
+template <typename T, int TE, int EPT, int MT, int GKC, int NPF, bool FUSE>
 __global__ __launch_bounds__(256) void gate_logits_kernel(
     const T* __restrict__ x, const T* __restrict__ Wg,
     const float* __restrict__ bias, int Tn, int d, int E,
-    float* __restrict__ logits) {
+    float* __restrict__ logits, int k, int renorm, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w) {
 #pragma clang fp contract(off)
     constexpr int GWP = GKC + 4;               // padded LDS row of a gate column
     constexpr int TX = TE / EPT;               // threads across experts
@@ -180,15 +189,79 @@ __global__ __launch_bounds__(256) void gate_logits_kernel(
             logits[t * E + e] = v;
         }
     }
+    if constexpr (FUSE) {
+        // A token's experts sit in the TX consecutive lanes of its row (lane
+        // tx holds experts tx, tx + TX, ...; e0 = 0).  k rounds of a
+        // segmented wave arg-max on (value desc, index asc) pick the experts
+        // in order, the winner taken out of its lane, as in topk_kernel; the
+        // weights are the softmax of the k picked logits (renorm = 1) or of
+        // all E, then picked (renorm = 0).  Every lane takes part (the
+        // shuffles); tokens past Tn are not stored.
+        static_assert(64 % TX == 0 && EPT <= 32, "token rows within a wave");
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const long t = t0 + ty * MT + m;
+            const bool store = tx == 0 && t < Tn;
+            float v[EPT];
+            uint32_t live = 0;
+#pragma unroll
+            for (int b = 0; b < EPT; ++b) {
+                const int e = tx + TX * b;
+                float lv = acc[m][b];
+                if (bias && e < E) lv = lv + bias[e];
+                v[b] = lv;
+                if (e < E) live |= 1u << b;
+            }
+            float best0 = 0.0f, den = 0.0f;
+            for (int j = 0; j < k; ++j) {
+                float bv = -FLT_MAX;
+                int bi = 0x7fffffff;
+#pragma unroll
+                for (int b = 0; b < EPT; ++b) {
+                    const int e = tx + TX * b;
+                    if (((live >> b) & 1u) && (bi == 0x7fffffff || better(v[b], e, bv, bi))) {
+                        bv = v[b];
+                        bi = e;
+                    }
+                }
+#pragma unroll
+                for (int off = TX / 2; off > 0; off >>= 1) {
+                    const float ov = __shfl_xor(bv, off);
+                    const int oi = __shfl_xor(bi, off);
+                    if (oi != 0x7fffffff && (bi == 0x7fffffff || better(ov, oi, bv, bi))) {
+                        bv = ov;
+                        bi = oi;
+                    }
+                }
+                if (bi % TX == tx) live &= ~(1u << (bi / TX));
+                if (j == 0) best0 = bv;
+                const float ex = expf(bv - best0);
+                if (renorm) den = den + ex;
+                if (store) {
+                    topk_idx[t * k + j] = bi;
+                    topk_w[t * k + j] = ex;        // scaled below
+                }
+            }
+            if (!renorm) {
+                float sum = 0.0f;
+#pragma unroll
+                for (int b = 0; b < EPT; ++b)
+                    if (tx + TX * b < E) sum = sum + expf(v[b] - best0);
+#pragma unroll
+                for (int off = TX / 2; off > 0; off >>= 1) sum = sum + __shfl_xor(sum, off);
+                den = sum;
+            }
+            const float inv = 1.0f / den;
+            if (store)
+                for (int j = 0; j < k; ++j) topk_w[t * k + j] = topk_w[t * k + j] * inv;
+        }
+    }
 }
 
 // ------------------------------------------------------------- top-k
 // One wave per token.  Lane l holds experts l, l+64, ...  Each of the k
 // rounds is a wave arg-max on (value desc, index asc); the winner is taken
 // out of its lane.  Selected logits wait in LDS for the weight pass.
-__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
-    return va > vb || (va == vb && ia < ib);
-}
 
 template <int NV>
 __global__ __launch_bounds__(256) void topk_kernel(
@@ -485,54 +558,80 @@ __global__ __launch_bounds__(256) void gate_dx_kernel(
 // the fetch with other blocks and keeps its registers for occupancy.
 constexpr int kNpfFew = 4, kNpfMany = 1;
 
-template <typename T, int TE, int EPT, int MT, int GKC>
+// The top-k arguments of a FUSE launch; unused otherwise.
+struct TopkOut {
+    int k, renorm;
+    int32_t* idx;
+    float* w;
+};
+
+template <typename T, int TE, int EPT, int MT, int GKC, bool FUSE>
 void logits_go(dim3 g, const T* xp, const T* wp, const float* bias, int Tn, int d, int E,
-               float* logits, hipStream_t s) {
+               float* logits, const TopkOut& o, hipStream_t s) {
     if ((long)g.x * g.y <= 2L * max(device_cus(), 1))
         MOE_LAUNCH("gate_logits", s,
-            gate_logits_kernel<T, TE, EPT, MT, GKC, kNpfFew><<<g, 256, 0, s>>>(
-                xp, wp, bias, Tn, d, E, logits));
+            gate_logits_kernel<T, TE, EPT, MT, GKC, kNpfFew, FUSE><<<g, 256, 0, s>>>(
+                xp, wp, bias, Tn, d, E, logits, o.k, o.renorm, o.idx, o.w));
     else
         MOE_LAUNCH("gate_logits", s,
-            gate_logits_kernel<T, TE, EPT, MT, GKC, kNpfMany><<<g, 256, 0, s>>>(
-                xp, wp, bias, Tn, d, E, logits));
+            gate_logits_kernel<T, TE, EPT, MT, GKC, kNpfMany, FUSE><<<g, 256, 0, s>>>(
+                xp, wp, bias, Tn, d, E, logits, o.k, o.renorm, o.idx, o.w));
 }
 
+// The logits, and with E <= 64 (every expert of a token in one block) the
+// top-k and gate weights in the same launch; with more experts those come
+// from topk_kernel.
 template <typename T>
 moe_status launch_logits(const void* x, const void* Wg, const float* bias,
-                         int Tn, int d, int E, float* logits, hipStream_t s) {
+                         int Tn, int d, int E, float* logits, const TopkOut& o,
+                         hipStream_t s) {
     const T* xp = static_cast<const T*>(x);
     const T* wp = static_cast<const T*>(Wg);
     // tokens per block = MT * 256 / (TE / EPT); one expert per thread for
     // small E keeps the grid at Tn/32 or more blocks
     if (E <= 8)
-        logits_go<T, 8, 1, 1, 256>(dim3(cdiv(Tn, 32), cdiv(E, 8)), xp, wp, bias, Tn, d, E,
-                                   logits, s);
-    else if (E <= 16 && (long)cdiv(Tn, 32) * cdiv(E, 16) >= 2L * max(device_cus(), 1))
-        // 2 experts per thread: 5 LDS bytes per multiply-add instead of 6
-        // (16 experts, 16384 tokens, d 2048, x in the MALL: 51 -> 43 us; with
-        // x read from HBM, as in a layer step, about the same), while the
-        // grid still gives every compute unit two blocks
-        logits_go<T, 16, 2, 1, 256>(dim3(cdiv(Tn, 32), cdiv(E, 16)), xp, wp, bias, Tn, d, E,
-                                    logits, s);
-    else if (E <= 16)
-        logits_go<T, 16, 1, 1, 256>(dim3(cdiv(Tn, 16), cdiv(E, 16)), xp, wp, bias, Tn, d, E,
-                                    logits, s);
+        logits_go<T, 8, 1, 1, 256, true>(dim3(cdiv(Tn, 32), cdiv(E, 8)), xp, wp, bias, Tn, d,
+                                         E, logits, o, s);
+    else if (E <= 16) {
+        // bf16: 2 experts per thread, 5 LDS bytes per multiply-add instead of
+        // 6 (16 experts, 16384 tokens, d 2048, x in the MALL: 51 -> 43 us;
+        // with x read from HBM, as in a layer step, about the same), while
+        // the grid still gives every compute unit two blocks.  (fp32 rows
+        // would take more registers than there are.)
+        if constexpr (sizeof(T) == 2) {
+            if ((long)cdiv(Tn, 32) * cdiv(E, 16) >= 2L * max(device_cus(), 1)) {
+                logits_go<T, 16, 2, 1, 256, true>(dim3(cdiv(Tn, 32), cdiv(E, 16)), xp, wp, bias,
+                                                  Tn, d, E, logits, o, s);
+                return launch_status();
+            }
+        }
+        logits_go<T, 16, 1, 1, 256, true>(dim3(cdiv(Tn, 16), cdiv(E, 16)), xp, wp, bias, Tn, d,
+                                          E, logits, o, s);
+    }
     else if (E <= 32)
-        logits_go<T, 32, 2, 1, 128>(dim3(cdiv(Tn, 16), cdiv(E, 32)), xp, wp, bias, Tn, d, E,
-                                    logits, s);
-    else if ((long)cdiv(Tn, 64) * cdiv(E, 64) >= 2L * max(device_cus(), 1))
+        logits_go<T, 32, 2, 1, 128, true>(dim3(cdiv(Tn, 16), cdiv(E, 32)), xp, wp, bias, Tn, d,
+                                          E, logits, o, s);
+    else if ((long)cdiv(Tn, 64) * cdiv(E, 64) >= 2L * max(device_cus(), 1)) {
         // 2 tokens x 8 experts per thread: per 16-byte slice of features a
         // thread reads 2 token vectors and 8 gate vectors for 16 chains,
         // 2.25 LDS bytes per multiply-add instead of 4.5 with 1 x 4 (the
         // kernel was bound by those reads: 64 experts 142 -> 94 us, 128
         // experts at d 4096 1.85 -> 1.15 ms), while the grid still gives
         // every compute unit two blocks
-        logits_go<T, 64, 8, 2, 64>(dim3(cdiv(Tn, 64), cdiv(E, 64)), xp, wp, bias, Tn, d, E,
-                                   logits, s);
-    else
-        logits_go<T, 64, 4, 1, 64>(dim3(cdiv(Tn, 16), cdiv(E, 64)), xp, wp, bias, Tn, d, E,
-                                   logits, s);
+        if (E <= 64) {
+            logits_go<T, 64, 8, 2, 64, true>(dim3(cdiv(Tn, 64), 1), xp, wp, bias, Tn, d, E,
+                                             logits, o, s);
+        } else {
+            logits_go<T, 64, 8, 2, 64, false>(dim3(cdiv(Tn, 64), cdiv(E, 64)), xp, wp, bias, Tn,
+                                              d, E, logits, o, s);
+        }
+    } else if (E <= 64) {
+        logits_go<T, 64, 4, 1, 64, true>(dim3(cdiv(Tn, 16), 1), xp, wp, bias, Tn, d, E, logits,
+                                         o, s);
+    } else {
+        logits_go<T, 64, 4, 1, 64, false>(dim3(cdiv(Tn, 16), cdiv(E, 64)), xp, wp, bias, Tn, d,
+                                          E, logits, o, s);
+    }
     return launch_status();
 }
 
@@ -644,10 +743,11 @@ moe_status moe_gate_topk(const void* x, const void* Wg, const float* logit_bias,
     MOE_CHECK_ARG(x && Wg && logits && topk_idx && topk_w);
     MOE_CHECK_ARG(aligned16(x));
     MOE_CHECK_DEVICE();
+    const TopkOut o{k, renorm, topk_idx, topk_w};
     moe_status st = dt == MOE_BF16
-        ? launch_logits<bf16_t>(x, Wg, logit_bias, T, d, E, logits, stream)
-        : launch_logits<float>(x, Wg, logit_bias, T, d, E, logits, stream);
-    if (st != MOE_OK) return st;
+        ? launch_logits<bf16_t>(x, Wg, logit_bias, T, d, E, logits, o, stream)
+        : launch_logits<float>(x, Wg, logit_bias, T, d, E, logits, o, stream);
+    if (st != MOE_OK || E <= 64) return st;    // E <= 64: top-k in the logits launch
     return launch_topk(logits, T, E, k, renorm, topk_idx, topk_w, stream);
 }
 
