@@ -54,42 +54,42 @@ TRAFFIC = {
     },
     # profiles/hbm_traffic_moe_s_like.md
     "moe_s_like": {
-        "perm_copy": 101234731,
-        "gemm_up_gelu": 1187248445,
-        "gemm_down": 787969826,
-        "combine": 101795049,
-        "combine_bwd": 169051084,
-        "gemm_dA_gelu": 1187034134,
-        "gemm_dW2": 1141094887,
-        "gemm_dW1": 1141094887,
-        "gemm_dX": 784842527,
-        "unpermute_grad": 134847691,
+        "perm_copy": 101231696,
+        "gemm_up_gelu": 1186687675,
+        "gemm_down": 790532035,
+        "combine": 101795671,
+        "combine_bwd": 169050645,
+        "gemm_dA_gelu": 1187235528,
+        "gemm_dW2": 1141093898,
+        "gemm_dW1": 1141093898,
+        "gemm_dX": 784841648,
+        "unpermute_grad": 134847875,
     },
     # profiles/hbm_traffic_skewed_zipf1.2.md
     "skewed_zipf1.2": {
-        "perm_copy": 403734895,
-        "gemm_up_gelu": 6883957853,
-        "gemm_down": 5444213871,
-        "combine": 404829698,
-        "combine_bwd": 673549588,
-        "gemm_dA_gelu": 6742331323,
-        "gemm_dW2": 4295596651,
-        "gemm_dW1": 4295596651,
-        "gemm_dX": 5525499427,
-        "unpermute_grad": 538017023,
+        "perm_copy": 403734722,
+        "gemm_up_gelu": 6829894633,
+        "gemm_down": 5449847459,
+        "combine": 404828658,
+        "combine_bwd": 673549146,
+        "gemm_dA_gelu": 6691146937,
+        "gemm_dW2": 4295314282,
+        "gemm_dW1": 4295314282,
+        "gemm_dX": 5500490813,
+        "unpermute_grad": 538015961,
     },
     # profiles/hbm_traffic_many_expert_zipf1.0.md
     "many_expert_zipf1.0": {
-        "perm_copy": 404799853,
-        "gemm_up_gelu": 4727341723,
-        "gemm_down": 3070802362,
-        "combine": 406925494,
-        "combine_bwd": 675905170,
-        "gemm_dA_gelu": 4763172657,
-        "gemm_dW2": 5436847951,
-        "gemm_dW1": 5436847951,
-        "gemm_dX": 3068617148,
-        "unpermute_grad": 539064210,
+        "perm_copy": 404799174,
+        "gemm_up_gelu": 4728851991,
+        "gemm_down": 3071081458,
+        "combine": 406925636,
+        "combine_bwd": 675904088,
+        "gemm_dA_gelu": 4761867641,
+        "gemm_dW2": 5436720038,
+        "gemm_dW1": 5436720038,
+        "gemm_dX": 3074217197,
+        "unpermute_grad": 539063351,
     },
 }
 
