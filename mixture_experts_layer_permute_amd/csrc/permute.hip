@@ -10,6 +10,7 @@
 // Four kernels:
 //   hist    per block of tokens, count pairs per expert (LDS counters)
 //   scan    per expert, exclusive scan of the block counts -> block bases
+//           (with at most kFuseScanBlocks blocks the scatter sums them itself)
 //   scatter per block, stable ranks inside the block from wave ballots
 //           (ranks never depend on the order atomics land in), dest and src
 //   copy    x_perm[dest[t,j]] = x[t]: each token row is read once and
@@ -22,6 +23,7 @@ namespace moe {
 namespace {
 
 constexpr int PERM_ENT = 1024;    // target (token, slot) pairs per block
+constexpr int kFuseScanBlocks = 64;
 
 inline int tokens_per_block(int k) { return k >= PERM_ENT ? 1 : PERM_ENT / k; }
 
@@ -78,17 +80,40 @@ __device__ __forceinline__ uint64_t match_peers(int e, bool valid, int nbits) {
     return peers;
 }
 
+// FUSED (at most kFuseScanBlocks blocks): no perm_scan launch; each block
+// sums the block counts itself, all of them for counts[e] (block 0 stores
+// those) and those of the blocks before it for its own bases.  Integer sums,
+// so the result is the same as through perm_scan.
+template <bool FUSED>
 __global__ __launch_bounds__(256) void perm_scatter_kernel(
-    const int32_t* __restrict__ idx, const int32_t* __restrict__ counts,
-    const int32_t* __restrict__ block_base, int Tn, int E, int k, int tpb,
-    int nblk, int nbits, int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ idx, int32_t* __restrict__ counts,
+    const int32_t* __restrict__ block_counts, const int32_t* __restrict__ block_base,
+    int Tn, int E, int k, int tpb, int nblk, int nbits, int32_t* __restrict__ offsets,
     int32_t* __restrict__ dest, int32_t* __restrict__ src) {
     extern __shared__ int sm[];
     int* offs = sm;                  // [E+1]
     int* wcnt = sm + E + 1;          // [4][E]
+    int* cnt_l = sm + 5 * E + 1;     // FUSED: [E] counts, [E] this block's bases
+    int* base_l = cnt_l + E;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int b = blockIdx.x;
 
+    if constexpr (FUSED) {
+        for (int e = tid; e < E; e += 256) {
+            const int32_t* bc = block_counts + (long)e * nblk;
+            int before = 0, all = 0;
+            for (int q = 0; q < nblk; ++q) {
+                const int v = bc[q];
+                before += q < b ? v : 0;
+                all += v;
+            }
+            cnt_l[e] = all;
+            base_l[e] = before;
+            if (b == 0) counts[e] = all;
+        }
+        __syncthreads();
+    }
+    const int32_t* cnt = FUSED ? cnt_l : counts;
     // expert offsets: exclusive scan of counts (E <= 1024: up to 4
     // consecutive experts per thread, then a block scan of the threads' sums)
     {
@@ -96,12 +121,12 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(
         const int per = (E + 255) / 256;
         const int lo = min(E, tid * per), hi = min(E, lo + per);
         int s = 0;
-        for (int e = lo; e < hi; ++e) s += counts[e];
+        for (int e = lo; e < hi; ++e) s += cnt[e];
         int total;
         int run = block_excl_scan<256>(s, sh, &total);
         for (int e = lo; e < hi; ++e) {
             offs[e] = run;
-            run += counts[e];
+            run += cnt[e];
         }
         if (tid == 0) offs[E] = total;
     }
@@ -145,7 +170,7 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(
         const bool valid = e >= 0 && e < E;
         const uint64_t peers = match_peers(valid ? e : 0, valid, nbits);
         if (valid) {
-            const int pos = offs[e] + block_base[(long)e * nblk + b] +
+            const int pos = offs[e] + (FUSED ? base_l[e] : block_base[(long)e * nblk + b]) +
                             wcnt[w * E + e] + popc64(peers & lt);
             dest[i] = pos;
             src[pos] = (int)(i / k);
@@ -245,23 +270,27 @@ moe_status moe_permute(const int32_t* topk_idx, const void* x, int T, int d,
     while ((1 << nbits) < E) ++nbits;
 
     if (T == 0) {
-        // empty input: counts = 0, offsets = 0 (a tiny scatter launch with no
-        // blocks would do nothing, so write them with the scan kernel form)
-        MOE_LAUNCH("perm_scan", stream,
-            perm_scan_kernel<<<E, 256, 0, stream>>>(bcounts, 0, bbase, counts));
+        // empty input: counts = 0, offsets = 0, from one scatter block that
+        // sums no block counts and ranks no pairs
         MOE_LAUNCH("perm_scatter", stream,
-            perm_scatter_kernel<<<1, 256, sizeof(int) * (5 * (size_t)E + 1), stream>>>(
-                topk_idx, counts, bbase, 0, E, k, tpb, 1, nbits, offsets, dest, src));
+            perm_scatter_kernel<true><<<1, 256, sizeof(int) * (7 * (size_t)E + 1), stream>>>(
+                topk_idx, counts, bcounts, bbase, 0, E, k, tpb, 0, nbits, offsets, dest, src));
         return launch_status();
     }
     MOE_LAUNCH("perm_hist", stream,
         perm_hist_kernel<<<nblk, 256, sizeof(int) * (size_t)E, stream>>>(
             topk_idx, T, E, k, tpb, nblk, bcounts));
-    MOE_LAUNCH("perm_scan", stream,
-        perm_scan_kernel<<<E, 256, 0, stream>>>(bcounts, nblk, bbase, counts));
-    MOE_LAUNCH("perm_scatter", stream,
-        perm_scatter_kernel<<<nblk, 256, sizeof(int) * (5 * (size_t)E + 1), stream>>>(
-            topk_idx, counts, bbase, T, E, k, tpb, nblk, nbits, offsets, dest, src));
+    if (nblk <= kFuseScanBlocks) {
+        MOE_LAUNCH("perm_scatter", stream,
+            perm_scatter_kernel<true><<<nblk, 256, sizeof(int) * (7 * (size_t)E + 1), stream>>>(
+                topk_idx, counts, bcounts, bbase, T, E, k, tpb, nblk, nbits, offsets, dest, src));
+    } else {
+        MOE_LAUNCH("perm_scan", stream,
+            perm_scan_kernel<<<E, 256, 0, stream>>>(bcounts, nblk, bbase, counts));
+        MOE_LAUNCH("perm_scatter", stream,
+            perm_scatter_kernel<false><<<nblk, 256, sizeof(int) * (5 * (size_t)E + 1), stream>>>(
+                topk_idx, counts, bcounts, bbase, T, E, k, tpb, nblk, nbits, offsets, dest, src));
+    }
     if (!x_perm) return launch_status();
     if (dt == MOE_BF16)
         MOE_LAUNCH("perm_copy", stream,

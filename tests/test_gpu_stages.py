@@ -67,6 +67,10 @@ PERM_CASES = [  # T, E, k, hot, hot_frac, dead
     (777, 64, 8, 0, 0.5, tuple(range(40, 64))), (5, 4, 4, None, 0.0, ()),
     (1, 3, 1, None, 0.0, ()), (3000, 1, 1, None, 0.0, ()),
     (1500, 1024, 3, 5, 0.7, ()), (4097, 128, 8, 127, 0.95, (0, 1, 2)),
+    # 64 blocks (the scatter sums the block counts itself), 65 blocks and
+    # 157 blocks (through the separate scan)
+    (32768, 16, 2, 4, 0.5, ()), (32769, 16, 2, 4, 0.5, (9,)),
+    (20000, 64, 8, 3, 0.6, (60, 61)),
 ]
 
 
