@@ -759,87 +759,102 @@ __device__ __forceinline__ void bf16_epilogue(uint8_t* ringbuf, const TileInfo& 
     float* slab = reinterpret_cast<float*>(home) + (wv % WPS) * SLAB * NBT;
     constexpr int LPR = WTN / 8;
     constexpr int RPP = 64 / LPR;
+    constexpr int NPS = 16 / RPP;                         // sub-passes of a slab
+    const int c0 = (lane % LPR) * 8;
+    const int col = ti.n0 + wn * WTN + c0;
+    // slab q = 2i + h holds rows i*32 + h*16 .. +15 of the wave's tile
+    auto row_of = [&](int q, int ps) {
+        return wm * WTM + (q >> 1) * 32 + (q & 1) * 16 + ps * RPP + lane / LPR;
+    };
+    auto ok_of = [&](int rl) {
+        return col < p.N && (MODE == RAGGED_M ? rl < ti.rows : ti.m0 + rl < p.M);
+    };
+    auto grow = [&](int rl) { return MODE == RAGGED_M ? ti.r0 + rl : (long)ti.m0 + rl; };
+    // a chunk of a split dW segment: its fp32 partial product, summed
+    // with the segment's other chunks (in order) by the reduce kernel
+    const bool split = MODE == RAGGED_K && ti.pslot >= 0;
+    auto to_partial = [&](int rl, const float* v) {
+        float* q = p.partial + (long)ti.pslot * p.partial_ld + ((long)ti.m0 + rl) * p.N + col;
+        *reinterpret_cast<float4*>(q) = *reinterpret_cast<const float4*>(v);
+        *reinterpret_cast<float4*>(q + 4) = *reinterpret_cast<const float4*>(v + 4);
+    };
+    // Epilogues that read memory: the reads of slab q + 1 are issued before
+    // slab q is consumed and stored, so each slab waits for its reads at most
+    // as long as the previous slab takes (the reads of slab 0 go out before
+    // its accumulators are staged); stores count in the same in-order
+    // counter, so a read issued after a slab's stores would also wait for them.
+    constexpr bool PRE = Epi::kPre && !DUAL;
+    typedef typename Epi::Pre Pre;
+    // The reads are not predicated: a lane whose row or column is outside
+    // the product reads the tile's first row at column 0 instead (always in
+    // bounds) and drops the data, so no branch hides a read from the
+    // compiler's count of reads in flight (a branch around them makes it
+    // wait for all of them).  A chunk of a split dW segment reads no C.
+    auto issue = [&](int q, Pre (&pre)[NPS]) {
+        if (split) return;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+        for (int ps = 0; ps < NPS; ++ps) {
+            const int rl = row_of(q, ps);
+            const bool in = ok_of(rl);
+            pre[ps] = epi.pre8(ti.e, grow(in ? rl : 0), in ? col : 0);
+        }
+    };
+    Pre pre[2 * FM][NPS];                                 // one set per slab: no copies
+    if constexpr (PRE) issue(0, pre[0]);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+    for (int q = 0; q < 2 * FM; ++q) {
+        const int i = q >> 1, h = q & 1;
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-                for (int vv = 0; vv < 8; ++vv) {
-                    const int v = h * 8 + vv;
-                    const int r = (vv >> 2) * 8 + (lane >> 5) * 4 + (vv & 3);
-                    slab[r * LDW + j * 32 + (lane & 31)] = acc[i][j][v];
-                    if constexpr (DUAL)
-                        slab[SLAB + r * LDW + j * 32 + (lane & 31)] = acc2[i][j][v];
+            for (int vv = 0; vv < 8; ++vv) {
+                const int v = h * 8 + vv;
+                const int r = (vv >> 2) * 8 + (lane >> 5) * 4 + (vv & 3);
+                slab[r * LDW + j * 32 + (lane & 31)] = acc[i][j][v];
+                if constexpr (DUAL)
+                    slab[SLAB + r * LDW + j * 32 + (lane & 31)] = acc2[i][j][v];
+            }
+        wave_lds_sync();
+        if constexpr (PRE) {
+            if (q + 1 < 2 * FM) issue(q + 1, pre[q + 1]);
+#pragma unroll
+            for (int ps = 0; ps < NPS; ++ps) {
+                const int rl = row_of(q, ps);
+                const float* src = &slab[(ps * RPP + lane / LPR) * LDW + c0];
+                float v[8];
+                *reinterpret_cast<float4*>(v) = *reinterpret_cast<const float4*>(src);
+                *reinterpret_cast<float4*>(v + 4) = *reinterpret_cast<const float4*>(src + 4);
+                if (ok_of(rl)) {
+                    if (split) to_partial(rl, v);
+                    else epi.vec8p(ti.e, grow(rl), col, v, pre[q][ps]);
                 }
-            wave_lds_sync();
-            constexpr int NPS = 16 / RPP;                 // sub-passes of this slab
-            auto row_of = [&](int ps) { return wm * WTM + i * 32 + h * 16 + ps * RPP + lane / LPR; };
-            const int c0 = (lane % LPR) * 8;
-            const int col = ti.n0 + wn * WTN + c0;
-            auto ok_of = [&](int rl) {
-                return col < p.N && (MODE == RAGGED_M ? rl < ti.rows : ti.m0 + rl < p.M);
-            };
-            // a chunk of a split dW segment: its fp32 partial product, summed
-            // with the segment's other chunks (in order) by the reduce kernel
-            const bool split = MODE == RAGGED_K && ti.pslot >= 0;
-            auto to_partial = [&](int rl, const float* v) {
-                float* q = p.partial + (long)ti.pslot * p.partial_ld +
-                           ((long)ti.m0 + rl) * p.N + col;
-                *reinterpret_cast<float4*>(q) = *reinterpret_cast<const float4*>(v);
-                *reinterpret_cast<float4*>(q + 4) = *reinterpret_cast<const float4*>(v + 4);
-            };
-            if constexpr (Epi::kPre && !DUAL) {
-                // every read of this slab in flight before the first is used
-                auto grow = [&](int rl) {
-                    return MODE == RAGGED_M ? ti.r0 + rl : (long)ti.m0 + rl;
-                };
-                typename Epi::Pre pre[NPS];
-#pragma unroll
-                for (int ps = 0; ps < NPS; ++ps)
-                    if (!split && ok_of(row_of(ps)))
-                        pre[ps] = epi.pre8(ti.e, grow(row_of(ps)), col);
-#pragma unroll
-                for (int ps = 0; ps < NPS; ++ps) {
-                    const int rl = row_of(ps);
-                    const float* src = &slab[(ps * RPP + lane / LPR) * LDW + c0];
-                    float v[8];
-                    *reinterpret_cast<float4*>(v) = *reinterpret_cast<const float4*>(src);
-                    *reinterpret_cast<float4*>(v + 4) = *reinterpret_cast<const float4*>(src + 4);
-                    if (ok_of(rl)) {
-                        if (split) to_partial(rl, v);
-                        else epi.vec8p(ti.e, grow(rl), col, v, pre[ps]);
-                    }
-                }
-            } else {
+            }
+        } else {
 #pragma unroll 1
-                for (int ps = 0; ps < NPS; ++ps) {
-                    const int rl = row_of(ps);
-                    const float* src = &slab[(ps * RPP + lane / LPR) * LDW + c0];
-                    float v[8];
-                    *reinterpret_cast<float4*>(v) = *reinterpret_cast<const float4*>(src);
-                    *reinterpret_cast<float4*>(v + 4) = *reinterpret_cast<const float4*>(src + 4);
-                    if (ok_of(rl)) {
-                        if constexpr (DUAL) {
-                            float v3[8];
-                            *reinterpret_cast<float4*>(v3) =
-                                *reinterpret_cast<const float4*>(src + SLAB);
-                            *reinterpret_cast<float4*>(v3 + 4) =
-                                *reinterpret_cast<const float4*>(src + SLAB + 4);
-                            epi.vec8(ti.e, ti.r0 + rl, col, v, v3);
-                        } else if (MODE == RAGGED_M) {
-                            epi.vec8(ti.e, ti.r0 + rl, col, v);
-                        } else if (split) {
-                            to_partial(rl, v);
-                        } else {
-                            epi.vec8(ti.e, (long)ti.m0 + rl, col, v);
-                        }
+            for (int ps = 0; ps < NPS; ++ps) {
+                const int rl = row_of(q, ps);
+                const float* src = &slab[(ps * RPP + lane / LPR) * LDW + c0];
+                float v[8];
+                *reinterpret_cast<float4*>(v) = *reinterpret_cast<const float4*>(src);
+                *reinterpret_cast<float4*>(v + 4) = *reinterpret_cast<const float4*>(src + 4);
+                if (ok_of(rl)) {
+                    if constexpr (DUAL) {
+                        float v3[8];
+                        *reinterpret_cast<float4*>(v3) = *reinterpret_cast<const float4*>(src + SLAB);
+                        *reinterpret_cast<float4*>(v3 + 4) =
+                            *reinterpret_cast<const float4*>(src + SLAB + 4);
+                        epi.vec8(ti.e, ti.r0 + rl, col, v, v3);
+                    } else if (MODE == RAGGED_M) {
+                        epi.vec8(ti.e, ti.r0 + rl, col, v);
+                    } else if (split) {
+                        to_partial(rl, v);
+                    } else {
+                        epi.vec8(ti.e, (long)ti.m0 + rl, col, v);
                     }
                 }
             }
-            wave_lds_sync();
         }
+        wave_lds_sync();
     }
 }
 
