@@ -9,8 +9,10 @@
 // The logits decide integer routing, so they are summed in one fixed fp32
 // order: increasing feature index i, each product and each sum rounded.
 // This file is compiled with -ffp-contract=off so no multiply-add is fused
-// for fp32 inputs; for bf16 inputs the fp32 product is exact and an explicit
-// fused multiply-add gives the same bits.
+// for fp32 inputs; for bf16 inputs the fp32 product of two 8-bit
+// significands is exact (while it stays in fp32's normal range: at or above
+// 2^-126 and below overflow) and an explicit fused multiply-add gives the
+// same bits.
 #include <float.h>
 
 #include <type_traits>

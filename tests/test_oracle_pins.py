@@ -66,6 +66,14 @@ def test_gate_bf16_inputs_products_exact():
         assert np.array_equal(p64.astype(np.float32).astype(np.float64), p64)
         acc = (acc.astype(np.float64) + p64).astype(np.float32)
     assert np.array_equal(acc, l)
+    # The exactness needs the product inside fp32's normal range: two bf16
+    # values (8-bit significands) whose product lies below 2^-126 lose bits
+    # to fp32's subnormal spacing, so there an FMA and a rounded product can
+    # differ.  The gate's inputs stay far from that range.
+    a = np.float32(np.ldexp(1.0078125, -70))      # 1 + 2^-7, a bf16 value
+    assert np.float32(a).view(np.uint32) & 0xffff == 0
+    exact = np.float64(a) * np.float64(a)
+    assert np.float64(np.float32(exact)) != exact
 
 
 def test_topk_brute_force_and_ties():
