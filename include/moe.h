@@ -395,6 +395,34 @@ moe_status moe_mfma_loop(int blocks, int iters, float *out, size_t out_floats,
 moe_status moe_mfma_loop_random(int blocks, int iters, float *out, size_t out_floats,
                                 hipStream_t stream);
 
+/*
+ * moe_lds_probe -- benchmark support: the rates of the LDS paths the grouped
+ * GEMM's main loop uses, alone and side by side.  `blocks` workgroups of 4
+ * waves each run `iters` rounds; per round each wave does, for every set bit
+ * of `mode`:
+ *   1: eight 16-byte-per-lane LDS reads (ds_read_b128, 1 KB per wave each),
+ *   2: sixteen 8-byte-per-lane transposing LDS reads (ds_read_b64_tr_b16,
+ *      512 B per wave each), the read of M/N-contiguous operand fragments,
+ *   4: eight direct-to-LDS buffer loads of 16 bytes per lane
+ *      (buffer_load_dwordx4 ... lds, 1 KB per wave each) from `src`, cycling
+ *      through its src_bytes bytes (size it under the L2 to time L2-to-LDS
+ *      loads), then a wait for them,
+ *   8: the reads of bits 1 and 2 three times (the ratio of fragment reads to
+ *      ring loads of the GEMM's 256 x 256 tile),
+ * so each kind moves 32 KB per workgroup and round (reads 96 KB with bit 8).  Each workgroup holds
+ * 64 KB of LDS (two per compute unit).  Timed by the caller on `stream`.
+ *   src: device buffer, 16-byte aligned, read only when bit 4 is set (may be
+ *   NULL otherwise); src_bytes a power of two from 8 KB to 1 GB.
+ *   out: device buffer of at least blocks * 4 floats (one value per wave,
+ *   meaningless; written so that the work is not optimised away).
+ *   Errors: MOE_ERR_INVALID_ARG for mode outside 1..15 or with none of
+ *   bits 1, 2, 4 set, blocks < 1,
+ *   iters < 1, out NULL or out_floats < blocks * 4, or, with bit 4 set, src
+ *   NULL or unaligned or src_bytes not a power of two in [8 KB, 1 GB].
+ */
+moe_status moe_lds_probe(int mode, int blocks, int iters, const void *src, size_t src_bytes,
+                         float *out, size_t out_floats, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

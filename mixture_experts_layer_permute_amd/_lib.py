@@ -46,6 +46,7 @@ SIGNATURES = {
                                _P, _P, _Z, _P]),
     "moe_mfma_loop": (_I, [_I, _I, _P, _Z, _P]),
     "moe_mfma_loop_random": (_I, [_I, _I, _P, _Z, _P]),
+    "moe_lds_probe": (_I, [_I, _I, _I, _P, _Z, _P, _Z, _P]),
     "moe_profile_enable": (_I, [_I]),
     "moe_profile_disable": (None, []),
     "moe_profile_reset": (None, []),

@@ -1844,6 +1844,68 @@ moe_status scratch_address(void** out) {
     return MOE_OK;
 }
 
+// ------------------------------------------------------------ LDS probe
+// The rates of the LDS paths of the main loop, alone and side by side
+// (moe_lds_probe).  Bits of MODE: 1 plain 16-byte fragment reads
+// (ds_read_b128), 2 transposing 8-byte reads of M/N-contiguous operands
+// (ds_read_b64_tr_b16), 4 direct-to-LDS buffer loads of the ring
+// (buffer_load_dwordx4 ... lds, lds_dma16) from a source window of
+// win_mask + 1 bytes; 8: the reads three times per round, the ratio of
+// fragment reads to ring loads of a 256 x 256 tile.  Each wave reads its own
+// 8 KB and loads into another 8 KB; lanes take consecutive 16- (8-) byte
+// slots, so a read touches every bank once per phase.  Every kind moves 8 KB
+// per wave and round (the reads 24 KB with bit 8).
+constexpr int PROBE_WAVE_LDS = 8192;
+
+template <int MODE>
+__global__ __launch_bounds__(256) void lds_probe_kernel(const bf16_t* src, uint32_t win_mask,
+                                                        int iters, float* __restrict__ out) {
+    __shared__ __attribute__((aligned(16))) uint8_t rd[4 * PROBE_WAVE_LDS];
+    __shared__ __attribute__((aligned(16))) uint8_t dm[4 * PROBE_WAVE_LDS];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    uint8_t* my = rd + w * PROBE_WAVE_LDS;
+    for (int i = lane; i < PROBE_WAVE_LDS / 16; i += 64)
+        reinterpret_cast<uint4*>(my)[i] = make_uint4(i, lane, w, blockIdx.x);
+    wave_lds_sync();
+    uint32_t acc = 0;
+    const uint32_t gw = blockIdx.x * 4 + w;
+    const uint32_t ldm = lds_addr(dm + w * PROBE_WAVE_LDS);
+    for (int it = 0; it < iters; ++it) {
+        asm volatile("" ::: "memory");       // the reads are issued again every round
+        if constexpr ((MODE & 4) != 0) {
+            const i32x4_t rs = rsrc_words(src, (long)win_mask + 1);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t o = ((gw * 8 + j + (uint32_t)it * 8) * 1024 + lane * 16) & win_mask;
+                lds_dma16(rs, o, ldm + j * 1024);
+            }
+        }
+        constexpr int NR = (MODE & 8) != 0 ? 3 : 1;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            if (r > 0) asm volatile("" ::: "memory");   // read again, not reuse
+            if constexpr ((MODE & 1) != 0) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const uint4 v = *reinterpret_cast<const uint4*>(my + j * 1024 + lane * 16);
+                    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+                }
+            }
+            if constexpr ((MODE & 2) != 0) {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_v4i16_t*)(my + j * 512 + lane * 8));
+                    acc ^= (uint32_t)(uint16_t)v[0] ^ ((uint32_t)(uint16_t)v[1] << 16) ^
+                           (uint32_t)(uint16_t)v[2] ^ ((uint32_t)(uint16_t)v[3] << 16);
+                }
+            }
+        }
+        if constexpr ((MODE & 4) != 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    if (lane == 0) out[gw] = (float)acc;
+}
+
 moe_status ffn_check(int R, int E, int d, int f, moe_act act, moe_dtype dt) {
     if (R < 0 || E < 1 || E > 1024 || d < 64 || f < 64) return MOE_ERR_INVALID_ARG;
     if (d % 64 != 0 || f % 64 != 0) return MOE_ERR_INVALID_ARG;
@@ -2021,6 +2083,34 @@ moe_status moe_expert_ffn_bwd_gather(const void* d_out_perm, const void* x,
                                W3, W2, dx_perm, dW1, dW3, dW2, ws, stream, src, T);
     return ffn_bwd<float>(d_out_perm, x, h_save, a_save, offsets, R, E, d, f, act, W1, W3,
                           W2, dx_perm, dW1, dW3, dW2, ws, stream, src, T);
+}
+
+
+moe_status moe_lds_probe(int mode, int blocks, int iters, const void* src, size_t src_bytes,
+                         float* out, size_t out_floats, hipStream_t stream) {
+    MOE_CHECK_ARG(mode >= 1 && mode <= 15 && (mode & 7) != 0);
+    MOE_CHECK_ARG(blocks >= 1 && iters >= 1 && out);
+    MOE_CHECK_ARG(out_floats >= (size_t)blocks * 4);
+    if (mode & 4) {
+        MOE_CHECK_ARG(src && aligned16(src));
+        MOE_CHECK_ARG(src_bytes >= 8192 && src_bytes <= (1u << 30) &&
+                      (src_bytes & (src_bytes - 1)) == 0);
+    }
+    MOE_CHECK_DEVICE();
+    const bf16_t* sp = static_cast<const bf16_t*>(src);
+    const uint32_t wm = (mode & 4) ? (uint32_t)(src_bytes - 1) : 0u;
+    switch (mode) {
+#define PROBE_CASE(M)                                                                    \
+    case M:                                                                              \
+        MOE_LAUNCH("lds_probe", stream,                                                  \
+                   lds_probe_kernel<M><<<blocks, 256, 0, stream>>>(sp, wm, iters, out)); \
+        break;
+        PROBE_CASE(1) PROBE_CASE(2) PROBE_CASE(3) PROBE_CASE(4) PROBE_CASE(5) PROBE_CASE(6)
+        PROBE_CASE(7) PROBE_CASE(9) PROBE_CASE(10) PROBE_CASE(11) PROBE_CASE(12)
+        PROBE_CASE(13) PROBE_CASE(14) PROBE_CASE(15)
+#undef PROBE_CASE
+    }
+    return launch_status();
 }
 
 }  // extern "C"

@@ -184,7 +184,7 @@ def test_binding_types_match_the_header():
         assert kind.get(res) == rk, (name, res, rk)
 
 
-def test_mfma_loop_rejects_bad_arguments(lib):
+def test_benchmark_probes_reject_bad_arguments(lib):
     INV = _lib.MOE_ERR_INVALID_ARG
     assert lib.moe_mfma_loop(0, 10, None, 0, None) == INV          # no blocks, no buffer
     assert lib.moe_mfma_loop(4, 0, 16, 16, None) == INV            # no iterations
@@ -192,4 +192,13 @@ def test_mfma_loop_rejects_bad_arguments(lib):
     assert lib.moe_mfma_loop_random(0, 16, None, 0, None) == INV   # no blocks, no buffer
     assert lib.moe_mfma_loop_random(4, 12, 16, 16, None) == INV    # not a multiple of 8
     assert lib.moe_mfma_loop_random(4, 0, 16, 16, None) == INV     # no iterations
+    assert lib.moe_lds_probe(0, 4, 10, None, 0, 16, 16, None) == INV       # no kind
+    assert lib.moe_lds_probe(8, 4, 10, None, 0, 16, 16, None) == INV       # multiplier only
+    assert lib.moe_lds_probe(16, 4, 10, None, 0, 16, 16, None) == INV      # unknown bit
+    assert lib.moe_lds_probe(1, 4, 10, None, 0, 16, 15, None) == INV       # buffer short
+    assert lib.moe_lds_probe(3, 0, 10, None, 0, 16, 16, None) == INV       # no blocks
+    assert lib.moe_lds_probe(4, 4, 10, None, 1 << 20, 16, 16, None) == INV  # loads, no source
+    assert lib.moe_lds_probe(4, 4, 10, 256, 3 << 20, 16, 16, None) == INV   # not a power of two
+    assert lib.moe_lds_probe(5, 4, 10, 256, 4096, 16, 16, None) == INV      # under 8 KB
+    assert lib.moe_lds_probe(6, 4, 10, 8, 1 << 20, 16, 16, None) == INV     # unaligned source
     assert lib.moe_mfma_loop_random(4, 16, 16, 15, None) == INV    # buffer under blocks * 4
