@@ -1517,10 +1517,21 @@ struct TileCfg {
 // RAGGED_M main and wide-tail tiles: two 64-deep stages (half the barriers
 // of 32-deep ones; the next stage is issued at the top of the current one).  dW
 // products, whose reduction is a segment that may be short, keep four
-// 32-deep stages.  The narrow tail (64x128 slices, few MFMAs per stage)
-// takes 64-deep stages in a 5-stage ring, three in flight.
+// 32-deep stages, unless the segments are long (LongKCfg).  The narrow tail
+// (64x128 slices, few MFMAs per stage) takes 64-deep stages in a 5-stage
+// ring, three in flight.
 using DefaultCfg = TileCfg<256, 256, 4, 2, 128, 4, 2, 64, 256, 1, 4, 128, 4, Ring<2, 64>,
                            Ring<2, 64>, Ring<5, 64>, Ring<4, 32>>;
+// dW products over segments of kLongSegmentRows rows or more on average
+// (R >= kLongSegmentRows * E): two 64-deep stages, half the barriers of four
+// 32-deep ones (the long-context step 1.9% faster; with 2048-row segments,
+// MoE-S-like, they were 0.4% slower, so shorter segments keep the 32-deep
+// ring).  Same summation order: the outputs do not change.
+template <class C>
+using LongKCfg = TileCfg<C::BM, C::BN, C::WM, C::WN, C::BND, C::WMD, C::WND, C::BMT, C::BNT,
+                         C::WMT, C::WNT, C::BNN, C::WNN, typename C::RM, typename C::RT,
+                         typename C::RN, Ring<2, 64>>;
+constexpr long kLongSegmentRows = 4096;
 
 // Wave quantisation.  A RAGGED_M product has between ceil(R/BM) and
 // ceil(R/BM) + E - 1 row tiles, since each expert's last tile is usually
@@ -1629,6 +1640,19 @@ struct Launch<float, Cfg> {
 // steps were 3% and 1% faster with everything on the caller's stream.
 inline bool side_stream_pays(int d, int f) { return (long)d * f <= (8L << 20); }
 
+// One dW product (RAGGED_K), with the ring that suits the segment length.
+template <typename T, class Cfg, bool G, class Epi>
+void dw_go(bool long_k, const GemmArgs<T>& p, Epi epi, int R, hipStream_t s, const char* name) {
+    if constexpr (sizeof(T) == 2) {
+        if (long_k) {
+            Launch<T, LongKCfg<Cfg>>::template go<RAGGED_K, MNMAJ, MNMAJ, false, false, G>(
+                p, epi, R, s, name);
+            return;
+        }
+    }
+    Launch<T, Cfg>::template go<RAGGED_K, MNMAJ, MNMAJ, false, false, G>(p, epi, R, s, name);
+}
+
 template <typename T, class Cfg = DefaultCfg>
 moe_status ffn_fwd(const void* x_perm, const int32_t* offsets, int R, int E,
                    int d, int f, moe_act act, const void* W1, const void* W3,
@@ -1694,6 +1718,7 @@ moe_status ffn_bwd(const void* d_out, const void* x_perm, const void* h_save,
     // gather != NULL: x_perm is the token-order input [T_src,d]; dW1/dW3 read
     // permuted row r as its row gather[r]
     const FfnWs L = ffn_layout(R, E, d, f, act, sizeof(T) == 2 ? MOE_BF16 : MOE_F32, 1);
+    const bool long_k = (long)R >= kLongSegmentRows * E;     // ring of the dW products
     char* base = static_cast<char*>(ws);
     int32_t* prefix = reinterpret_cast<int32_t*>(base + L.prefix);
     int32_t* order = reinterpret_cast<int32_t*>(base + L.order);
@@ -1763,11 +1788,11 @@ moe_status ffn_bwd(const void* d_out, const void* x_perm, const void* h_save,
         p.B = dO; p.ldb = d; p.N = d;
         with_items(p, L.part0);
         if (accumulate)
-            Launch<T, Cfg>::template go<RAGGED_K, MNMAJ, MNMAJ, false, false>(
-                p, EpiAcc<T>{static_cast<T*>(dW2), d, (long)f * d}, R, ts, "gemm_dW2");
+            dw_go<T, Cfg, false>(long_k, p, EpiAcc<T>{static_cast<T*>(dW2), d, (long)f * d}, R,
+                                 ts, "gemm_dW2");
         else
-            Launch<T, Cfg>::template go<RAGGED_K, MNMAJ, MNMAJ, false, false>(
-                p, EpiStore<T>{static_cast<T*>(dW2), d, (long)f * d}, R, ts, "gemm_dW2");
+            dw_go<T, Cfg, false>(long_k, p, EpiStore<T>{static_cast<T*>(dW2), d, (long)f * d},
+                                 R, ts, "gemm_dW2");
         reduce_splits(dW2, L.part0, ts, "dw_split_reduce");
     }
     // dX = dH1 W1[e]^T (+ dH3 W3[e]^T)   [R, d]
@@ -1806,11 +1831,11 @@ moe_status ffn_bwd(const void* d_out, const void* x_perm, const void* h_save,
         with_items(p, L.part1);
         auto dw = [&](void* C, const char* name) {
             if (accumulate)
-                Launch<T, Cfg>::template go<RAGGED_K, MNMAJ, MNMAJ, false, false, true>(
-                    p, EpiAcc<T>{static_cast<T*>(C), f, (long)d * f}, R, s, name);
+                dw_go<T, Cfg, true>(long_k, p, EpiAcc<T>{static_cast<T*>(C), f, (long)d * f}, R,
+                                    s, name);
             else
-                Launch<T, Cfg>::template go<RAGGED_K, MNMAJ, MNMAJ, false, false, true>(
-                    p, EpiStore<T>{static_cast<T*>(C), f, (long)d * f}, R, s, name);
+                dw_go<T, Cfg, true>(long_k, p, EpiStore<T>{static_cast<T*>(C), f, (long)d * f},
+                                    R, s, name);
             reduce_splits(C, L.part1, s, "dw_split_reduce");
         };
         dw(dW1, "gemm_dW1");

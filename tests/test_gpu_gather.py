@@ -23,6 +23,7 @@ CASES = [  # T, E, k, d, f, hot expert (every token's first choice) or None
     (257, 4, 1, 64, 128, None),
     (1, 3, 2, 64, 64, None),
     (9000, 6, 2, 64, 128, 4),      # expert 4 gets 9000 rows: three map chunks
+    (12500, 3, 2, 64, 128, 1),     # 8333 rows per expert: the dW products' 64-deep ring
 ]
 
 

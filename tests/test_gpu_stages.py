@@ -110,7 +110,12 @@ FFN_CASES = [  # counts per expert, d, f
     ([2178], 64, 128),
     # dW split over rows: two experts above 8192 rows with one dW tile each
     # (chunks of 4096 rows, fp32 partials summed in order), beside short ones
+    # (segments of 5861 rows on average: the dW products' 64-deep ring)
     ([9000, 5, 20000, 0, 300], 128, 256),
+    # a split segment with 1538 rows on average (the 32-deep ring)
+    ([9000, 5, 3000, 0, 300, 0, 0, 0], 128, 256),
+    # 4398 rows on average, ragged ends and a partial column tile (64-deep ring)
+    ([4096, 4100, 4999], 128, 192),
 ]
 
 
