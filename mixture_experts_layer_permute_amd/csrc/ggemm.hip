@@ -24,7 +24,8 @@
 // bf16 path: block tile 256x256, 8 waves of 64 (4x2, 64x128 each), gfx950
 // MFMA v_mfma_f32_32x32x16_bf16 with fp32 accumulators.  Operands go from
 // HBM straight into an LDS ring (two 64-deep stages for RAGGED_M, four
-// 32-deep ones for RAGGED_K); K-contiguous operands are read as
+// 32-deep ones for RAGGED_K, or two 64-deep ones over long segments);
+// K-contiguous operands are read as
 // 16-byte fragments, M/N-contiguous ones with the transposing LDS read.
 // Products that are a few rounds of workgroups run as a full-tile launch
 // and a partial-tile launch; independent launches may run on a side stream.
