@@ -1024,8 +1024,9 @@ __global__ __launch_bounds__(64 * WM * WN, 2) void ggemm_bf16_dma_kernel(GemmArg
     if constexpr (KGATHER) opA.rows_of(0, kmap, 0, krow);
     // Prologue: the first NP stages.  With both operands K-contiguous the
     // slot of stage NSTG-1 is filled here too (one stage more in flight
-    // from the start: dA, dX 2-3% faster); with a transposed operand the
-    // extra loads compete with the transposing LDS reads and cost as much.
+    // from the start: dA, dX 2-3% faster); with a transposed operand that
+    // was slower (long-context down and dW 2-2.5%, the MoE-S-like products
+    // 2-6%), although reads and loads do not slow each other in LDS itself.
     constexpr int NP = ALAY == KMAJ && BLAY == KMAJ ? NSTG : NSTG - 1;
 #pragma unroll
     for (int q = 0; q < NP; ++q)
