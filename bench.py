@@ -35,7 +35,7 @@ PEAK_HBM_GBS = 8000.0
 # and factors).  Valid only for the kernel sources whose code (comments and
 # blank lines aside, see source_hash) has the SHA-256 prefix TRAFFIC_SRC;
 # null once it changes.
-TRAFFIC_SRC = "2c038bc255a954d0"
+TRAFFIC_SRC = "0a2b78b8595eaa05"
 TRAFFIC_SOURCES = ("ggemm.hip", "common.h", "permute.hip", "combine.hip")
 TRAFFIC = {
     # profiles/hbm_traffic_long_ctx_swiglu.md

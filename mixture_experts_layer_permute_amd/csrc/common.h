@@ -173,6 +173,26 @@ __device__ __forceinline__ int block_excl_scan(int v, int* sh, int* total) {
     return base + inc - v;
 }
 
+// ------------------------------------------------------- debug bounds
+
+// Debug build (-DMOE_DEBUG_BOUNDS): device-side checks of indexes that come
+// from data -- caller-supplied segment offsets, routing, the tile plan --
+// before the accesses they guard.  A failed check ends the kernel with a
+// trap, so that a fault is reported where the bad index arises instead of
+// as a stray access later.  Empty in the normal build (the library's code
+// is the same with or without the checks' source lines).  For finding the
+// cause of a fault; never for timing.
+#ifdef MOE_DEBUG_BOUNDS
+#define MOE_DASSERT(cond)                  \
+    do {                                   \
+        if (!(cond)) __builtin_trap();     \
+    } while (0)
+#else
+#define MOE_DASSERT(cond) \
+    do {                  \
+    } while (0)
+#endif
+
 // ------------------------------------------------------------ host side
 
 // Checks (once per device) that the current device is gfx950 and returns

@@ -443,6 +443,7 @@ __device__ __forceinline__ TileInfo decode_tile(const GemmArgs<T>& p) {
             const int seg0 = p.offsets[lo], seg1 = p.offsets[lo + 1];
             ti.r0 = (long)seg0 + (long)(mt - pre[lo]) * BM;
             ti.rows = (int)min((long)BM, (long)seg1 - ti.r0);
+            MOE_DASSERT(seg0 >= 0 && seg0 <= seg1 && ti.rows > 0);
         }
         ti.n0 = nt * BN;
         ti.m0 = 0;
@@ -470,6 +471,7 @@ __device__ __forceinline__ TileInfo decode_tile(const GemmArgs<T>& p) {
             ti.live = es < *p.item_count;
             if (!ti.live) return ti;
             const int4 it = p.items[es];
+            MOE_DASSERT(it.x >= 0 && it.x < p.E && it.y >= 0 && it.z >= 0);
             ti.e = it.x;
             ti.kbeg = it.y;
             ti.klen = it.z;
@@ -1251,6 +1253,7 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(const int32_t* __restric
     __shared__ int sh[16];
     const int e = threadIdx.x;
     const int c_e = e < E ? offsets[e + 1] - offsets[e] : 0;
+    MOE_DASSERT(c_e >= 0 && (e > 0 || offsets[0] >= 0));   // nondecreasing, from row >= 0
     if (e < E) cnt[e] = c_e;
     // per-expert prefixes of the row tiles, of the full row tiles and of the
     // experts with a partial last tile (block scans; experts in index order)

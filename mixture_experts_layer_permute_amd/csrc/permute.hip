@@ -172,6 +172,7 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(
         if (valid) {
             const int pos = offs[e] + (FUSED ? base_l[e] : block_base[(long)e * nblk + b]) +
                             wcnt[w * E + e] + popc64(peers & lt);
+            MOE_DASSERT((unsigned)pos < (unsigned)(Tn * k));
             dest[i] = pos;
             src[pos] = (int)(i / k);
         } else if (i < end) {
